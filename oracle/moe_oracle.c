@@ -1,0 +1,218 @@
+/*
+ * moe_oracle.c -- plain fp64 CPU oracle of the sparse Mixture-of-Experts FFN
+ * forward pass.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header or constant with the HIP library; it is written from the definition
+ * of the layer, one step per function, with no blocking, fusion or reordering
+ * of any sum beyond what the definition states.  Loops over independent
+ * tokens (or independent rows) are spread over OpenMP threads; every single
+ * sum runs in ascending index order in one thread.
+ *
+ * Sources (page titles as printed on the pages):
+ *  - linear router logits: "AMD MI300X平台上的MoE模型训练实践", section 3.2
+ *    (a conventional MoE uses a simple linear router); zero-initialised gate
+ *    bias: TorchTitan 1K-GPU MoE article, section 4.2.
+ *  - softmax with a router temperature: "AMD GPU深度学习优化与ZAYA1大模型实践",
+ *    section 7 (router_temp), and the TorchTitan article, section 2.1
+ *    (gate temperature 0.3).
+ *  - top-1 routing: ZAYA1 page, section 2; top-2 with a capacity factor of
+ *    1.25: TorchTitan article, section 2.1.
+ *  - GeGLU expert FFN: ZAYA1 page, section 3.2 (GeGLU fused with the matmul);
+ *    GELU in its erf form (the router listing on the MI300X page, section 3.2,
+ *    uses nn.GELU, whose default is the erf form).
+ *
+ * Readings taken where the pages are silent (each one stated again at the
+ * function that applies it):
+ *  - top-k ranks the logits themselves, ties go to the lower expert index;
+ *  - p = softmax(l / tau) over all E experts; with renormalisation the k chosen
+ *    gates are p divided by the sum of the chosen p, otherwise the raw p;
+ *  - capacity C = ceil(cap_num * k * T / (cap_den * E)) in exact integers,
+ *    C = T when there is no limit;
+ *  - overflow is dropped in token order: for each expert the first C tokens
+ *    (ascending t, whatever the rank j at which they chose it) are kept;
+ *  - dropped assignments contribute nothing and the kept gates are not
+ *    renormalised again; a token with every assignment dropped gets y = 0.
+ *
+ * dtype codes: 0 = fp32, 1 = bf16 (raw 16-bit patterns, the upper half of an
+ * IEEE fp32).  Every input value is widened exactly to fp64 before use.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Exact fp64 value of element i of an fp32 or bf16 array. */
+static double load(const void* p, int64_t i, int dtype) {
+    float f;
+    if (dtype == 0) {
+        f = ((const float*)p)[i];
+    } else {
+        uint32_t u = ((uint32_t)((const uint16_t*)p)[i]) << 16;
+        memcpy(&f, &u, sizeof f);
+    }
+    return (double)f;
+}
+
+/* GELU, erf form: v * Phi(v) = 0.5 * v * (1 + erf(v / sqrt(2))). */
+static double gelu(double v) { return 0.5 * v * (1.0 + erf(v / sqrt(2.0))); }
+
+/* Step 1 -- router logits l[t][e] = sum_i x[t][i] * Wr[i][e] + b[e].
+ * x is [T][d], Wr is [d][E] (row-major); bias may be NULL (zero). */
+void orc_logits(int64_t T, int64_t d, int64_t E, int dtype, const void* x,
+                const void* wr, const float* bias, double* logits) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int64_t i = 0; i < d; ++i)
+                s += load(x, t * d + i, dtype) * load(wr, i * E + e, dtype);
+            if (bias) s += (double)bias[e];
+            logits[t * E + e] = s;
+        }
+    }
+}
+
+/* Step 2 -- top-k expert choice and gate weights, per token.
+ * Experts are ranked by their logit (largest first); equal logits rank the
+ * lower expert index first.  The ranking uses the logits themselves, never
+ * l / tau or p: tau > 0 keeps the order, and ranking rounded quotients could
+ * merge distinct logits.
+ * p[e] = exp((l[e] - max l) / tau) / sum_e' exp((l[e'] - max l) / tau).
+ * renorm != 0: gate[j] = p[idx[j]] / sum_j' p[idx[j']]; else gate[j] = p[idx[j]]. */
+void orc_route(int64_t T, int64_t E, int64_t k, double tau, int renorm,
+               const double* logits, int32_t* idx, double* gate) {
+    #pragma omp parallel
+    {
+        char* taken = (char*)calloc((size_t)E, 1);
+        double* p = (double*)malloc(sizeof(double) * (size_t)E);
+        #pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const double* l = logits + t * E;
+            memset(taken, 0, (size_t)E);
+            for (int64_t j = 0; j < k; ++j) {
+                int64_t best = -1;
+                for (int64_t e = 0; e < E; ++e) {
+                    if (taken[e]) continue;
+                    if (best < 0 || l[e] > l[best]) best = e;   /* strict: ties keep the lower e */
+                }
+                taken[best] = 1;
+                idx[t * k + j] = (int32_t)best;
+            }
+            double m = l[0];
+            for (int64_t e = 1; e < E; ++e) if (l[e] > m) m = l[e];
+            double z = 0.0;
+            for (int64_t e = 0; e < E; ++e) { p[e] = exp((l[e] - m) / tau); z += p[e]; }
+            for (int64_t e = 0; e < E; ++e) p[e] /= z;
+            double s = 0.0;
+            for (int64_t j = 0; j < k; ++j) s += p[idx[t * k + j]];
+            for (int64_t j = 0; j < k; ++j)
+                gate[t * k + j] = renorm ? p[idx[t * k + j]] / s : p[idx[t * k + j]];
+        }
+        free(taken);
+        free(p);
+    }
+}
+
+/* Step 3 -- expert capacity C = ceil(cap_num * k * T / (cap_den * E)),
+ * exact integer arithmetic; cap_den == 0 means no limit, C = T (a token picks
+ * an expert at most once, so no expert can receive more than T). */
+int64_t orc_capacity(int64_t T, int64_t E, int64_t k, int64_t cap_num, int64_t cap_den) {
+    if (cap_den == 0) return T;
+    int64_t num = cap_num * k * T, den = cap_den * E;
+    return (num + den - 1) / den;
+}
+
+/* Step 4 -- token-order positions, capacity drops and the permutation.
+ * pos[t][j] = number of earlier assignments (t' < t) to the same expert;
+ * kept when pos < C.  count = assignments per expert before drops,
+ * kept_e = min(count_e, C), offset = exclusive prefix sum of kept (E + 1
+ * entries, offset[E] = rows kept in total).  Rows are grouped by expert,
+ * ascending token inside an expert: row = offset[e] + pos, or -1 if dropped;
+ * token_of_row[row] = t. */
+void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C, const int32_t* idx,
+                  int32_t* count, int32_t* kept, int32_t* offset, int32_t* pos,
+                  int32_t* row_of, int32_t* token_of_row) {
+    for (int64_t e = 0; e < E; ++e) count[e] = 0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < k; ++j) {
+            int32_t e = idx[t * k + j];
+            pos[t * k + j] = count[e];
+            count[e] += 1;
+        }
+    offset[0] = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        kept[e] = count[e] < C ? count[e] : (int32_t)C;
+        offset[e + 1] = offset[e] + kept[e];
+    }
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t a = t * k + j;
+            if (pos[a] < C) {
+                int32_t row = offset[idx[a]] + pos[a];
+                row_of[a] = row;
+                token_of_row[row] = (int32_t)t;
+            } else {
+                row_of[a] = -1;
+            }
+        }
+}
+
+/* Step 5 -- the GeGLU expert FFN for a list of (token, expert) rows.
+ * For row r (token t = tok[r], expert e = ex[r]):
+ *   g[n] = sum_i x[t][i] * Wg[e][i][n],  u[n] = sum_i x[t][i] * Wu[e][i][n],
+ *   h[n] = GELU(g[n]) * u[n],            o[c] = sum_n h[n] * Wd[e][n][c].
+ * Wg, Wu are [E][d][d_ff], Wd is [E][d_ff][d].  Each sum runs over its index
+ * in ascending order (the loops visit i, then n, outermost so that the weight
+ * rows are read in order; that does not change any sum).  h may be NULL. */
+void orc_ffn_rows(int64_t n_rows, const int64_t* tok, const int32_t* ex, int64_t d,
+                  int64_t d_ff, int dtype, const void* x, const void* wg,
+                  const void* wu, const void* wd, double* h_out, double* o_out) {
+    #pragma omp parallel
+    {
+        double* g = (double*)malloc(sizeof(double) * (size_t)d_ff);
+        double* u = (double*)malloc(sizeof(double) * (size_t)d_ff);
+        double* o = (double*)malloc(sizeof(double) * (size_t)d);
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t t = tok[r], e = ex[r];
+            for (int64_t n = 0; n < d_ff; ++n) { g[n] = 0.0; u[n] = 0.0; }
+            for (int64_t i = 0; i < d; ++i) {
+                double xi = load(x, t * d + i, dtype);
+                int64_t wrow = (e * d + i) * d_ff;
+                for (int64_t n = 0; n < d_ff; ++n) {
+                    g[n] += xi * load(wg, wrow + n, dtype);
+                    u[n] += xi * load(wu, wrow + n, dtype);
+                }
+            }
+            for (int64_t n = 0; n < d_ff; ++n) g[n] = gelu(g[n]) * u[n];  /* g now holds h */
+            for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+            for (int64_t n = 0; n < d_ff; ++n) {
+                int64_t wrow = (e * d_ff + n) * d;
+                for (int64_t c = 0; c < d; ++c) o[c] += g[n] * load(wd, wrow + c, dtype);
+            }
+            if (h_out) memcpy(h_out + r * d_ff, g, sizeof(double) * (size_t)d_ff);
+            memcpy(o_out + r * d, o, sizeof(double) * (size_t)d);
+        }
+        free(g); free(u); free(o);
+    }
+}
+
+/* Step 6 -- gate-weighted combine for a list of tokens.
+ * y[t] = sum over j = 0..k-1 with row_of[t][j] >= 0 of gate[t][j] * o[slot][.],
+ * where o holds one row per (t, j) of the listed tokens: o[(s * k + j) * d + c]
+ * for the s-th listed token.  A token with nothing kept gets y = 0. */
+void orc_combine(int64_t n_tok, const int64_t* toks, int64_t k, int64_t d,
+                 const int32_t* row_of, const double* gate, const double* o, double* y) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < n_tok; ++s) {
+        int64_t t = toks[s];
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                if (row_of[t * k + j] >= 0) acc += gate[t * k + j] * o[(s * k + j) * d + c];
+            y[s * d + c] = acc;
+        }
+    }
+}

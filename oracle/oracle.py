@@ -1,0 +1,221 @@
+"""Python front end of the fp64 CPU oracle (moe_oracle.c).
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  It never imports the
+HIP library or its binding, and the HIP library never imports it.
+
+Arrays are passed as numpy arrays or CPU torch tensors: fp32 values, or bf16
+values (torch.bfloat16, or their raw 16-bit patterns as uint16/int16).  All
+arithmetic happens in fp64 in the C library; this file only moves arrays and
+strings the C steps together in the order the layer defines them:
+logits -> top-k and gates -> capacity -> token-order dispatch -> GeGLU expert
+FFN per kept row -> gate-weighted combine.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# A different build of moe_oracle.c (the mutation tests plant mistakes in a
+# copy of the source and check that the pins catch them).
+_LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def build() -> str:
+    """Compile moe_oracle.c with gcc (OpenMP, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-std=c11", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None and _LIB_OVERRIDE:
+            _lib = _declare(ctypes.CDLL(_LIB_OVERRIDE))
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            _lib = _declare(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _declare(lib):
+    lib.orc_logits.argtypes = [_I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P]
+    lib.orc_logits.restype = None
+    lib.orc_route.argtypes = [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int, _P, _P, _P]
+    lib.orc_route.restype = None
+    lib.orc_capacity.argtypes = [_I64, _I64, _I64, _I64, _I64]
+    lib.orc_capacity.restype = _I64
+    lib.orc_dispatch.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]
+    lib.orc_dispatch.restype = None
+    lib.orc_ffn_rows.argtypes = [_I64, _P, _P, _I64, _I64, ctypes.c_int,
+                                 _P, _P, _P, _P, _P, _P]
+    lib.orc_ffn_rows.restype = None
+    lib.orc_combine.argtypes = [_I64, _P, _I64, _I64, _P, _P, _P, _P]
+    lib.orc_combine.restype = None
+    return lib
+
+
+def _raw(a):
+    """numpy view of an input array, plus its dtype code (0 fp32, 1 bf16)."""
+    if a is None:
+        return None, None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().contiguous()
+            if a.dtype == torch.bfloat16:
+                a = a.view(torch.int16).numpy().view(np.uint16)
+            else:
+                a = a.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, 0
+    if a.dtype in (np.uint16, np.int16):
+        return a.view(np.uint16), 1
+    raise TypeError(f"oracle inputs must be fp32 or bf16, got {a.dtype}")
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def logits(x, w_router, bias=None) -> np.ndarray:
+    """l[t][e] = sum_i x[t][i] Wr[i][e] + b[e], in fp64."""
+    xr, dt = _raw(x)
+    wr, dt2 = _raw(w_router)
+    assert dt == dt2
+    T, d = xr.shape
+    E = wr.shape[1]
+    b = None if bias is None else np.ascontiguousarray(_raw(bias)[0], dtype=np.float32)
+    out = np.empty((T, E), dtype=np.float64)
+    _load().orc_logits(T, d, E, dt, _ptr(xr), _ptr(wr), _ptr(b), _ptr(out))
+    return out
+
+
+def route(logits_, k: int, tau: float, renormalize: bool):
+    """Top-k experts (logit descending, lower index on ties) and fp64 gates."""
+    lg = np.ascontiguousarray(logits_, dtype=np.float64)
+    T, E = lg.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    gate = np.empty((T, k), dtype=np.float64)
+    _load().orc_route(T, E, k, float(tau), int(bool(renormalize)), _ptr(lg), _ptr(idx), _ptr(gate))
+    return idx, gate
+
+
+def capacity(T: int, E: int, k: int, cap_num: int, cap_den: int) -> int:
+    return int(_load().orc_capacity(T, E, k, cap_num, cap_den))
+
+
+def dispatch(idx: np.ndarray, E: int, C: int) -> Dict[str, np.ndarray]:
+    """Token-order positions, drops, counts, offsets and the permutation maps."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    count = np.empty(E, dtype=np.int32)
+    kept = np.empty(E, dtype=np.int32)
+    offset = np.empty(E + 1, dtype=np.int32)
+    pos = np.empty((T, k), dtype=np.int32)
+    row_of = np.empty((T, k), dtype=np.int32)
+    token_of_row = np.full(T * k, -1, dtype=np.int32)
+    _load().orc_dispatch(T, E, k, C, _ptr(idx), _ptr(count), _ptr(kept), _ptr(offset),
+                         _ptr(pos), _ptr(row_of), _ptr(token_of_row))
+    n_kept = int(offset[E])
+    return dict(count=count, kept=kept, offset=offset, pos=pos, row_of=row_of,
+                token_of_row=token_of_row[:n_kept].copy(), n_kept=n_kept)
+
+
+def ffn_rows(tokens: Sequence[int], experts: Sequence[int], x, w_gate, w_up, w_down,
+             want_h: bool = False):
+    """GeGLU expert FFN, fp64, for each listed (token, expert) row."""
+    xr, dt = _raw(x)
+    wg, d1 = _raw(w_gate)
+    wu, d2 = _raw(w_up)
+    wd, d3 = _raw(w_down)
+    assert dt == d1 == d2 == d3
+    d = xr.shape[1]
+    d_ff = wg.shape[2]
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    ex = np.ascontiguousarray(experts, dtype=np.int32)
+    n = tok.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    h = np.empty((n, d_ff), dtype=np.float64) if want_h else None
+    if n:
+        _load().orc_ffn_rows(n, _ptr(tok), _ptr(ex), d, d_ff, dt, _ptr(xr), _ptr(wg),
+                             _ptr(wu), _ptr(wd), _ptr(h), _ptr(o))
+    return (h, o) if want_h else o
+
+
+def combine(tokens: Sequence[int], row_of: np.ndarray, gate: np.ndarray,
+            o_slots: np.ndarray) -> np.ndarray:
+    """y[t] = sum of gate * o over the kept assignments of each listed token.
+
+    ``o_slots`` holds one row per (listed token, j): shape [n_tok * k, d]."""
+    row_of = np.ascontiguousarray(row_of, dtype=np.int32)
+    gate = np.ascontiguousarray(gate, dtype=np.float64)
+    o_slots = np.ascontiguousarray(o_slots, dtype=np.float64)
+    toks = np.ascontiguousarray(tokens, dtype=np.int64)
+    k = row_of.shape[1]
+    d = o_slots.shape[1]
+    y = np.empty((toks.shape[0], d), dtype=np.float64)
+    if toks.shape[0]:
+        _load().orc_combine(toks.shape[0], _ptr(toks), k, d, _ptr(row_of), _ptr(gate),
+                            _ptr(o_slots), _ptr(y))
+    return y
+
+
+def forward(x, w_router, bias, w_gate, w_up, w_down, *, k: int, tau: float,
+            renormalize: bool, cap_num: int, cap_den: int,
+            logits_in: Optional[np.ndarray] = None,
+            tokens: Optional[Sequence[int]] = None, want_h: bool = False) -> Dict:
+    """The whole layer in fp64.
+
+    ``logits_in`` replaces step 1 (routing then runs on exactly those values,
+    e.g. fp32 logits exported by another implementation).  ``tokens`` limits
+    the expert FFN and the combine to the listed tokens (routing, capacity and
+    dispatch always cover the whole batch, since drops depend on every earlier
+    token).  Returns every intermediate."""
+    xr, _ = _raw(x)
+    T = xr.shape[0]
+    E = _raw(w_router)[0].shape[1]
+    lg = logits(x, w_router, bias) if logits_in is None else np.asarray(logits_in, np.float64)
+    idx, gate = route(lg, k, tau, renormalize)
+    C = capacity(T, E, k, cap_num, cap_den)
+    dsp = dispatch(idx, E, C)
+    toks = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
+    slot_tok = np.repeat(toks, k)
+    slot_ex = idx[toks].reshape(-1)
+    kept_mask = dsp["row_of"][toks].reshape(-1) >= 0
+    d = xr.shape[1]
+    d_ff = _raw(w_gate)[0].shape[2]
+    o_slots = np.zeros((toks.shape[0] * k, d), dtype=np.float64)
+    h_slots = np.zeros((toks.shape[0] * k, d_ff), dtype=np.float64) if want_h else None
+    sel = np.nonzero(kept_mask)[0]
+    res = ffn_rows(slot_tok[sel], slot_ex[sel], x, w_gate, w_up, w_down, want_h=want_h)
+    if want_h:
+        h_slots[sel], o_slots[sel] = res
+    else:
+        o_slots[sel] = res
+    y = combine(toks, dsp["row_of"], gate, o_slots)
+    out = dict(logits=lg, idx=idx, gate=gate, C=C, tokens=toks, o_slots=o_slots, y=y)
+    out.update(dsp)
+    if want_h:
+        out["h_slots"] = h_slots
+    return out

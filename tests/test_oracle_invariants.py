@@ -1,0 +1,99 @@
+"""Invariants of the oracle's routing and dispatch at the real token counts,
+expert counts, k, capacity and temperature of every configuration (model
+width shrunk so the CPU finishes quickly), plus the whole tiny layer."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_15_amd import configs, synthetic
+from oracle import oracle as orc
+
+
+def _check_routing(lg, idx, gate, k, renorm):
+    T, E = lg.shape
+    # k distinct experts per token
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1]) if k > 1 else True
+    chosen = np.take_along_axis(lg, idx, axis=1)
+    mask = np.ones_like(lg, dtype=bool)
+    np.put_along_axis(mask, idx, False, axis=1)
+    if k < E:
+        assert np.all(chosen.min(1) >= np.where(mask, lg, -np.inf).max(1))
+    assert np.all(np.diff(chosen, axis=1) <= 0)
+    if renorm:
+        np.testing.assert_allclose(gate.sum(1), 1.0, rtol=1e-13)
+    else:
+        assert np.all(gate > 0) and np.all(gate <= 1.0)
+        if k == 1:
+            assert np.all(gate[:, 0] >= 1.0 / E - 1e-15)
+    if k > 1:
+        assert np.all(np.diff(gate, axis=1) <= 1e-15)
+
+
+def _check_dispatch(idx, dsp, E, C):
+    T, k = idx.shape
+    count, kept, off, row_of, tor = (dsp[n] for n in ("count", "kept", "offset", "row_of", "token_of_row"))
+    assert count.sum() == T * k
+    np.testing.assert_array_equal(kept, np.minimum(count, C))
+    assert off[0] == 0 and np.all(np.diff(off) == kept)
+    drops = int((row_of < 0).sum())
+    assert dsp["n_kept"] == T * k - drops == off[-1]
+    if C >= T:
+        assert drops == 0
+    # every kept (t, e) appears exactly once, in its expert's segment
+    tt, jj = np.nonzero(row_of >= 0)
+    rows = row_of[tt, jj]
+    assert np.unique(rows).size == rows.size == dsp["n_kept"]
+    np.testing.assert_array_equal(tor[rows], tt)
+    ex = idx[tt, jj]
+    assert np.all((rows >= off[ex]) & (rows < off[ex + 1]))
+    # segments ascending in token
+    for e in range(E):
+        seg = tor[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+@pytest.mark.parametrize("ci", range(len(configs.CONFIGS)))
+def test_routing_and_dispatch_invariants_at_real_token_counts(ci):
+    cfg = configs.CONFIGS[ci]
+    small = cfg.scaled(d=64, d_ff=64)
+    inp = synthetic.make_inputs(small, seed=0, experts=1)
+    lg = orc.logits(inp["x"], inp["w_router"], inp["bias"])
+    idx, gate = orc.route(lg, cfg.k, float(np.float32(cfg.temperature)), cfg.renormalize)
+    _check_routing(lg, idx, gate, cfg.k, cfg.renormalize)
+    C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    dsp = orc.dispatch(idx, cfg.E, C)
+    _check_dispatch(idx, dsp, cfg.E, C)
+
+
+def test_zipf_bias_values_and_skew():
+    b = synthetic.zipf_bias(64, 1.2).double().numpy()
+    H = sum(i ** -1.2 for i in range(1, 65))
+    assert abs(H - 3.418596) < 1e-6
+    np.testing.assert_allclose(np.exp(b).sum(), 1.0, rtol=1e-6)
+    assert abs(b[0] - (-1.22923)) < 1e-5 and np.all(np.diff(b) < 0)
+
+
+def test_whole_tiny_layer_invariants():
+    cfg = configs.get("tiny")
+    inp = synthetic.make_inputs(cfg, seed=0)
+    out = orc.forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                      inp["w_down"], k=cfg.k, tau=cfg.temperature, renormalize=cfg.renormalize,
+                      cap_num=cfg.cap_num, cap_den=cfg.cap_den)
+    assert out["C"] == cfg.T and out["n_kept"] == cfg.T * cfg.k
+    _check_routing(out["logits"], out["idx"], out["gate"], cfg.k, cfg.renormalize)
+    _check_dispatch(out["idx"], out, cfg.E, out["C"])
+    assert np.all(np.isfinite(out["y"])) and np.abs(out["y"]).max() > 0
+
+
+def test_synthetic_inputs_are_seeded_and_scaled():
+    cfg = configs.get("tiny").scaled(T=512, d=256, d_ff=256, dtype="bf16")
+    a = synthetic.make_inputs(cfg, seed=0)
+    b = synthetic.make_inputs(cfg, seed=0)
+    c = synthetic.make_inputs(cfg, seed=1)
+    for n in ("x", "w_router", "w_gate", "w_up", "w_down"):
+        assert a[n].dtype == synthetic.torch_dtype(cfg)
+        assert torch.equal(a[n], b[n])
+        assert not (a[n] == c[n]).all()
+    assert abs(a["x"].float().std().item() - 1.0) < 0.02
+    assert abs(a["w_gate"].float().std().item() * 16 - 1.0) < 0.02
+    assert abs(a["w_down"].float().std().item() * 16 - 1.0) < 0.02

@@ -1,0 +1,70 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of moe_oracle.c (on the CPU, in a
+temporary directory), builds it, and runs the pin tests against that build:
+the run must fail.  An unmodified copy built the same way must pass."""
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+
+MUTANTS = {
+    "bias dropped": ("if (bias) s += (double)bias[e];", "if (0) s += (double)bias[e];"),
+    "router weight transposed": ("load(wr, i * E + e, dtype)", "load(wr, e * d + i, dtype)"),
+    "ties to the higher index": ("l[e] > l[best]) best = e;", "l[e] >= l[best]) best = e;"),
+    "temperature multiplies": ("exp((l[e] - m) / tau)", "exp((l[e] - m) * tau)"),
+    "no renormalisation": ("renorm ? p[idx[t * k + j]] / s : p[idx[t * k + j]]",
+                           "p[idx[t * k + j]]"),
+    "always renormalised": ("renorm ? p[idx[t * k + j]] / s : p[idx[t * k + j]]",
+                            "p[idx[t * k + j]] / s"),
+    "capacity floor": ("return (num + den - 1) / den;", "return num / den;"),
+    "keep one too many": ("if (pos[a] < C) {", "if (pos[a] <= C) {"),
+    "choice-major drops": (
+        "for (int64_t t = 0; t < T; ++t)\n        for (int64_t j = 0; j < k; ++j) {\n"
+        "            int32_t e = idx[t * k + j];",
+        "for (int64_t j = 0; j < k; ++j)\n        for (int64_t t = 0; t < T; ++t) {\n"
+        "            int32_t e = idx[t * k + j];"),
+    "tanh GELU": ("0.5 * v * (1.0 + erf(v / sqrt(2.0)))",
+                  "0.5 * v * (1.0 + tanh(0.7978845608028654 * (v + 0.044715 * v * v * v)))"),
+    "GELU on the up branch": ("g[n] = gelu(g[n]) * u[n];", "g[n] = g[n] * gelu(u[n]);"),
+    "down weight transposed": ("o[c] += g[n] * load(wd, wrow + c, dtype);",
+                               "o[c] += g[n] * load(wd, (e * d + c) * d_ff + n, dtype);"),
+    "expert index ignored": ("int64_t t = tok[r], e = ex[r];", "int64_t t = tok[r], e = 0;"),
+    "second expert dropped in combine": ("for (int64_t j = 0; j < k; ++j)\n                if (row_of",
+                                         "for (int64_t j = 0; j < 1; ++j)\n                if (row_of"),
+}
+
+
+def _run(name, src_text, tmp):
+    path = os.path.join(tmp, name.replace(" ", "_"))
+    os.makedirs(path, exist_ok=True)
+    c = os.path.join(path, "m.c")
+    lib = os.path.join(path, "libm.so")
+    open(c, "w").write(src_text)
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-std=c11", c, "-o", lib, "-lm"], check=True)
+    env = dict(os.environ, MOE_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", PINS],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode
+
+
+def test_every_planted_mistake_is_caught():
+    base = open(SRC).read()
+    for name, (old, new) in MUTANTS.items():
+        assert base.count(old) == 1, f"mutation site for {name!r} not unique in the source"
+    with tempfile.TemporaryDirectory() as tmp:
+        jobs = {"(unmodified)": base}
+        jobs.update({n: base.replace(o, w) for n, (o, w) in MUTANTS.items()})
+        with ThreadPoolExecutor(max_workers=4) as ex:
+            rc = dict(zip(jobs, ex.map(lambda kv: _run(kv[0], kv[1], tmp), jobs.items())))
+    assert rc.pop("(unmodified)") == 0
+    survivors = [n for n, code in rc.items() if code == 0]
+    assert not survivors, f"pins missed planted mistakes: {survivors}"
