@@ -1,0 +1,253 @@
+"""Benchmark of the MoE FFN forward on one MI355X.
+
+A step is one pass of the whole layer -- route, dispatch, gate/up GEMM, down
+GEMM, combine -- over one batch of synthetic tokens, through the C ABI.
+Inputs sit in HBM before the timed region; the token batch rotates over
+several copies so that no step finds its activations in the 256 MB
+last-level cache (the weights, 1.6 GB here, never fit).  HIP events recorded
+on the launch stream between the stages give each stage's time inside the
+same timed region.
+
+Prints ONE JSON line.  Default workload: the ZAYA1-like layer (T = 4096,
+d = 2048, E = 16, top-1, GeGLU d_ff = 8192, bf16).  ``--config`` selects
+another of the five layers for manual runs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MoE fwd tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak) on 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="zaya1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, counts, n_kept):
+    """Bytes and flops each stage must move / do (padding and dropped rows excluded)."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    ne = sum(1 for c in counts if c > 0)
+    return {
+        "route_bytes": T * d * b + d * E * b + T * E * 4 + T * k * 8,
+        "dispatch_bytes": None,   # filled by caller (needs active-token count)
+        "gate_up_flops": 4.0 * d * F * n_kept,
+        "gate_up_bytes": 2 * ne * d * F * b + n_kept * d * b + n_kept * F * b,
+        "down_flops": 2.0 * d * F * n_kept,
+        "down_bytes": ne * F * d * b + n_kept * F * b + n_kept * d * b,
+        "combine_bytes": n_kept * d * b + T * d * b + T * k * 8,
+    }
+
+
+def cpu_baseline(cfg, host, logits_gpu, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same batch:
+    routing + capacity + dispatch of every token, then the GeGLU FFN and
+    combine of a token sample sized to about target_s seconds; scaled to the
+    whole batch."""
+    import numpy as np
+    from oracle import oracle as orc
+    kw = dict(k=cfg.k, tau=float(np.float32(cfg.temperature)), renormalize=cfg.renormalize,
+              cap_num=cfg.cap_num, cap_den=cfg.cap_den)
+    t0 = time.perf_counter()
+    lg = orc.logits(host["x"], host["w_router"], host["bias"])
+    idx, gate = orc.route(lg, cfg.k, kw["tau"], cfg.renormalize)
+    C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    orc.dispatch(idx, cfg.E, C)
+    t_route = time.perf_counter() - t0
+    # probe the per-token FFN cost, then size the sample
+    probe = 16
+    t0 = time.perf_counter()
+    orc.forward(host["x"], host["w_router"], host["bias"], host["w_gate"], host["w_up"],
+                host["w_down"], logits_in=lg, tokens=list(range(probe)), **kw)
+    t_probe = time.perf_counter() - t0
+    per_tok = max(t_probe / probe, 1e-6)
+    n = int(min(cfg.T, max(probe, target_s / per_tok)))
+    rng = np.random.default_rng(1)
+    toks = np.sort(rng.choice(cfg.T, size=n, replace=False))
+    t0 = time.perf_counter()
+    orc.forward(host["x"], host["w_router"], host["bias"], host["w_gate"], host["w_up"],
+                host["w_down"], logits_in=lg, tokens=toks, **kw)
+    t_ffn = time.perf_counter() - t0
+    total = t_route + t_ffn * cfg.T / n
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": cfg.T / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fp64 oracle: logits, top-k, capacity and dispatch of all {cfg.T} tokens "
+                       f"({t_route:.2f} s) + GeGLU FFN and combine of {n} random tokens "
+                       f"({t_ffn:.2f} s), scaled to {cfg.T} tokens"),
+            "seconds_measured": round(t_route + t_ffn, 2)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this layer's forward is measured on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_15_amd as moe
+    from mixture_experts_layer_15_amd import configs, synthetic
+
+    cfg = configs.get(args.config)
+    torch.cuda.set_device(0)
+    dev = synthetic.make_inputs(cfg, seed=0, device="cuda")
+    x0 = dev["x"]
+    xb = x0.numel() * x0.element_size()
+    n_rot = max(1, min(64, -(-512 * 2 ** 20 // xb)))   # >= 512 MB of distinct token batches
+    xs = [x0] + [x0.roll(i, dims=0).contiguous() for i in range(1, n_rot)]
+    wr, bias, wg, wu, wd = dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"]
+
+    R = moe.max_rows(cfg)
+    dt = x0.dtype
+    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    x_perm = torch.empty((R, cfg.d), dtype=dt, device="cuda")
+    count = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    offset = torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda")
+    row_of = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    tor = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device="cuda")
+    h = torch.empty((R, cfg.d_ff), dtype=dt, device="cuda")
+    y_perm = torch.empty((R, cfg.d), dtype=dt, device="cuda")
+    y = torch.empty((cfg.T, cfg.d), dtype=dt, device="cuda")
+    dws = moe.workspace_bytes(cfg, dispatch_only=True)
+    dsp_ws = torch.empty(max(dws, 16), dtype=torch.uint8, device="cuda")
+
+    L = moe.lib()
+    c = moe.cconfig(cfg)
+    P = moe._ptr
+    import ctypes
+    cref = ctypes.byref(c)
+
+    def step(x, ev=None):
+        s = moe._stream()
+        if ev: ev[0].record()
+        moe._check(L.moe_route(cref, P(x), P(wr), P(bias), P(logits), P(idx), P(gate), s), "route")
+        if ev: ev[1].record()
+        moe._check(L.moe_dispatch(cref, P(idx), P(x), P(x_perm), P(count), P(offset), P(row_of),
+                                  P(tor), P(dsp_ws), dws, s), "dispatch")
+        if ev: ev[2].record()
+        moe._check(L.moe_expert_gate_up(cref, P(x_perm), P(offset), P(wg), P(wu), P(h), s), "gate_up")
+        if ev: ev[3].record()
+        moe._check(L.moe_expert_down(cref, P(h), P(offset), P(wd), P(y_perm), s), "down")
+        if ev: ev[4].record()
+        moe._check(L.moe_combine(cref, P(y_perm), P(row_of), P(gate), P(y), s), "combine")
+        if ev: ev[5].record()
+
+    for i in range(args.warmup):
+        step(xs[i % n_rot])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(xs[i % n_rot], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["route", "dispatch", "gate_up", "down", "combine"]
+    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+                for j, n in enumerate(names)}
+    gpu_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][5]) for i in range(K)]))
+    ms_step = wall * 1e3 / K
+
+    # the fused entry point, same work, for reference
+    fwd = moe.Forward(cfg)
+    for i in range(3):
+        fwd(xs[i % n_rot], wr, bias, wg, wu, wd, y)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(K):
+        fwd(xs[i % n_rot], wr, bias, wg, wu, wd, y)
+    torch.cuda.synchronize()
+    fused_ms = (time.perf_counter() - t1) * 1e3 / K
+
+    # algorithmic work of the last step's routing (same for every rotated batch
+    # up to token order; recompute from the first batch for exactness)
+    step(xs[0])
+    torch.cuda.synchronize()
+    cnt = count.cpu().numpy()
+    off = offset.cpu().numpy()
+    n_kept = int(off[-1])
+    rows = row_of.cpu().numpy()
+    active = int((rows >= 0).any(1).sum())
+    a = algorithmic(cfg, cnt, n_kept)
+    b = 2 if cfg.dtype == "bf16" else 4
+    a["dispatch_bytes"] = (active + n_kept) * cfg.d * b + cfg.T * cfg.k * 4 * 3 + \
+        2 * 256 * cfg.E * 4
+    gemm_ms = stage_ms["gate_up"] + stage_ms["down"]
+    gemm_tflops = (a["gate_up_flops"] + a["down_flops"]) / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    gu_tflops = a["gate_up_flops"] / (stage_ms["gate_up"] * 1e-3) / 1e12
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init weights)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} top-{cfg.k} "
+                               f"GeGLU d_ff={cfg.d_ff} {cfg.dtype}",
+                   "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "d_ff": cfg.d_ff,
+                   "temperature": cfg.temperature,
+                   "capacity_factor": None if cfg.cap_den == 0 else cfg.cap_num / cfg.cap_den,
+                   "rows_kept": n_kept, "parallelism": "single GPU"},
+        "grouped_gemm_tflops": round(gemm_tflops, 1),
+        "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),
+        "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
+        "stage_gbs": {"route": round(gbs(a["route_bytes"], stage_ms["route"]), 1),
+                      "dispatch": round(gbs(a["dispatch_bytes"], stage_ms["dispatch"]), 1),
+                      "combine": round(gbs(a["combine_bytes"], stage_ms["combine"]), 1)},
+        "stage_hbm_frac": {"dispatch": round(gbs(a["dispatch_bytes"], stage_ms["dispatch"]) / PEAK_HBM_GBS, 4),
+                           "combine": round(gbs(a["combine_bytes"], stage_ms["combine"]) / PEAK_HBM_GBS, 4)},
+        "gpu_ms_per_step_events": round(gpu_ms, 4),
+        "fused_forward_ms_per_step": round(fused_ms, 4),
+        "roofline": {"kernel": "grouped_gemm_bf16_kernel<gate/up>" if cfg.dtype == "bf16"
+                     else "grouped_gemm_f32_kernel<gate/up>",
+                     "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": round(gu_tflops, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gu_tflops / peak, 4), "traffic": None,
+                     "flops_per_launch": a["gate_up_flops"],
+                     "avg_launch_ms": round(stage_ms["gate_up"], 4)},
+    }
+    if not args.no_cpu_baseline:
+        host = {k2: (None if v is None else v.cpu()) for k2, v in dev.items()}
+        out["cpu_baseline"] = cpu_baseline(cfg, host, logits, args.cpu_seconds)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

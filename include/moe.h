@@ -1,0 +1,190 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN forward.
+ *
+ * The layer (sources are page titles as printed on the pages):
+ *   1. router logits  l = x . W_r + b            (linear router: "AMD MI300X平台上的MoE
+ *      模型训练实践", section 3.2; zero-initialised gate bias: TorchTitan 1K-GPU MoE
+ *      article, section 4.2)
+ *   2. p = softmax(l / tau) over all experts      (router temperature: "AMD GPU深度学习优化
+ *      与ZAYA1大模型实践", section 7; gate temperature 0.3: TorchTitan article, section 2.1)
+ *   3. top-k experts per token, gates = p of the chosen experts, optionally
+ *      renormalised over them                    (top-1: ZAYA1 page, section 2; top-2:
+ *      TorchTitan article, section 2.1)
+ *   4. capacity C per expert from a capacity factor, overflow dropped in token
+ *      order                                     (capacity factor 1.25: TorchTitan article,
+ *      section 2.1)
+ *   5. token permutation grouped by expert
+ *   6. per-expert GeGLU FFN h = GELU(x W_gate) * (x W_up), o = h W_down
+ *                                                 (expert-FFN kernel: MI300X page, section 4.2;
+ *      GeGLU fused with the matmul: ZAYA1 page, section 3.2)
+ *   7. gate-weighted un-permute and combine      y_t = sum_j g_tj o_(t,j)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers (memory of the current HIP device) unless
+ *     the comment says "host".  Arrays are row-major and contiguous.  Device
+ *     arrays must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; nothing synchronises with the
+ *     host.  Results are visible after the caller synchronises the stream.
+ *   - The caller owns every buffer.  The library allocates no memory, frees
+ *     nothing and keeps no pointer after a call returns.
+ *   - Errors are reported by the returned moe_status; nothing is thrown across
+ *     the ABI.  Arguments are validated on the host before anything is
+ *     enqueued, so an invalid call enqueues nothing.  On any error the output
+ *     contents are unspecified.  moe_last_error() gives a message for the
+ *     calling thread's most recent failure.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified results.
+ *   - Floating-point results are deterministic: the same inputs on the same
+ *     device give bit-identical outputs (no float atomics anywhere).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* a size, pointer, alignment or config field is out of range */
+    MOE_ERR_UNSUPPORTED = 2,  /* a valid layer this build does not run (dtype) */
+    MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than moe_workspace_size() */
+    MOE_ERR_HIP = 4           /* the HIP runtime reported an error when enqueuing */
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,   /* activations and weights fp32 */
+    MOE_BF16 = 1   /* activations and weights bf16; accumulation is always fp32 */
+} moe_dtype;
+
+/* Layer shape and routing parameters.  Limits (checked by every call):
+ *   0 <= T, T * k < 2^31           tokens (T = 0 is a valid empty batch)
+ *   d % 64 == 0, 64 <= d <= 16384  model width (64-multiple rule of the ZAYA1
+ *                                  page's parameter table, section 2)
+ *   d_ff % 64 == 0, 64 <= d_ff <= 65536
+ *   1 <= E <= 256, 1 <= k <= min(E, 8)
+ *   temperature > 0 and finite
+ *   cap_den == 0: no capacity limit (C = T); else cap_num >= 0, cap_den > 0
+ *   renormalize: 0 or 1;  dtype: a moe_dtype */
+typedef struct {
+    int64_t T;
+    int32_t d;
+    int32_t E;
+    int32_t k;
+    int32_t d_ff;
+    float temperature;
+    int32_t cap_num;
+    int32_t cap_den;
+    int32_t renormalize;
+    int32_t dtype;
+} moe_config;
+
+/* Host.  Expert capacity C = ceil(cap_num * k * T / (cap_den * E)) in exact
+ * integer arithmetic, or T when cap_den == 0.  Returns -1 for an invalid
+ * config.  (The pages give only the factor, 1.25; tokens-per-expert times the
+ * factor, rounded up, is the reading used.) */
+int64_t moe_capacity(const moe_config* cfg);
+
+/* Host.  Upper bound on rows kept after drops: min(T * k, C * E).  -1 if the
+ * config is invalid.  x_perm, h and y_perm need this many rows. */
+int64_t moe_max_rows(const moe_config* cfg);
+
+/* Host.  Bytes of workspace moe_dispatch (dispatch_only = 1) or moe_forward
+ * (dispatch_only = 0) needs for this config, written to *bytes. */
+moe_status moe_workspace_size(const moe_config* cfg, int dispatch_only, size_t* bytes);
+
+/* Host.  Static, human-readable name of a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Host.  Message describing the calling thread's most recent failed call
+ * ("" if none).  The string is owned by the library and valid until the
+ * thread's next call into it. */
+const char* moe_last_error(void);
+
+/* Steps 1-3: router logits, softmax with temperature, top-k and gates.
+ *   x        [T, d]   dtype       input activations
+ *   w_router [d, E]   dtype       router weight
+ *   bias     [E]      fp32        router bias, or NULL for none
+ *   logits   [T, E]   fp32  out   l = x W_r + b, fp32 accumulation
+ *   topk_idx [T, k]   int32 out   chosen experts, largest logit first; equal
+ *                                 logits order the lower expert index first.
+ *                                 Ranking uses the fp32 logits themselves.
+ *   topk_gate[T, k]   fp32  out   p of each chosen expert, divided by the sum
+ *                                 of the chosen p when cfg->renormalize. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* bias, float* logits, int32_t* topk_idx,
+                     float* topk_gate, void* stream);
+
+/* Steps 2-3 only, from given fp32 logits [T, E] (same top-k and gate code as
+ * moe_route; lets callers and tests route exactly-known logits, e.g. ties). */
+moe_status moe_route_from_logits(const moe_config* cfg, const float* logits,
+                                 int32_t* topk_idx, float* topk_gate, void* stream);
+
+/* Steps 4-5: capacity, token-order drops and the expert-grouped permutation.
+ *   topk_idx      [T, k]         int32  in
+ *   x             [T, d]         dtype  in
+ *   x_perm        [max_rows, d]  dtype  out  row r = x[token_of_row[r]]; rows of
+ *                                            expert e are offset[e]..offset[e+1)-1,
+ *                                            ascending token order inside
+ *   expert_count  [E]            int32  out  assignments per expert before drops
+ *   expert_offset [E + 1]        int32  out  exclusive prefix of kept counts
+ *                                            min(count, C); [E] = rows kept
+ *   row_of        [T, k]         int32  out  row of assignment (t, j), -1 if dropped
+ *   token_of_row  [T * k]        int32  out  token of each kept row; entries at and
+ *                                            past offset[E] are set to -1
+ *   workspace     ws_bytes >= moe_workspace_size(cfg, 1, .)
+ * An assignment (t, j) to expert e is kept iff fewer than C earlier tokens
+ * (t' < t, at any rank) chose e ("drop overflow in token order"). */
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                        void* x_perm, int32_t* expert_count, int32_t* expert_offset,
+                        int32_t* row_of, int32_t* token_of_row, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/* Step 6: grouped GeGLU expert FFN over the permuted rows.
+ *   x_perm        [max_rows, d]    dtype in   (rows past expert_offset[E] ignored)
+ *   expert_offset [E + 1]          int32 in   as written by moe_dispatch
+ *   w_gate, w_up  [E, d, d_ff]     dtype in
+ *   w_down        [E, d_ff, d]     dtype in
+ *   h             [max_rows, d_ff] dtype out  GELU_erf(x W_gate) * (x W_up), fp32
+ *                                             epilogue rounded once to dtype
+ *   y_perm        [max_rows, d]    dtype out  h W_down, fp32 accumulation
+ * Rows at and past expert_offset[E] of h and y_perm are not written. */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm,
+                          const int32_t* expert_offset, const void* w_gate,
+                          const void* w_up, const void* w_down, void* h, void* y_perm,
+                          void* stream);
+
+/* Step 6, first half only: h = GELU_erf(x_perm W_gate) * (x_perm W_up)
+ * (same arguments and results as in moe_expert_ffn; one kernel launch). */
+moe_status moe_expert_gate_up(const moe_config* cfg, const void* x_perm,
+                              const int32_t* expert_offset, const void* w_gate,
+                              const void* w_up, void* h, void* stream);
+
+/* Step 6, second half only: y_perm = h W_down (one kernel launch). */
+moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offset,
+                           const void* w_down, void* y_perm, void* stream);
+
+/* Step 7: y[t] = sum over kept j (ascending) of topk_gate[t][j] * y_perm[row_of[t][j]],
+ * accumulated in fp32 and rounded once to dtype; a token with nothing kept
+ * gets y = 0.
+ *   y_perm [max_rows, d] dtype in;  row_of [T, k] int32 in;
+ *   topk_gate [T, k] fp32 in;       y [T, d] dtype out */
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of,
+                       const float* topk_gate, void* y, void* stream);
+
+/* Steps 1-7 on one stream, intermediates in the workspace
+ * (ws_bytes >= moe_workspace_size(cfg, 0, .)).  Same arguments and results as
+ * the four calls above in sequence. */
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* bias, const void* w_gate, const void* w_up,
+                       const void* w_down, void* y, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,284 @@
+"""MI355X (gfx950) sparse Mixture-of-Experts FFN forward.
+
+A thin ctypes binding over libmoe_mi355x.so (C ABI: include/moe.h).  This
+module only marshals arguments: it checks tensor dtypes, devices and shapes,
+allocates outputs with torch (device memory is torch's), and passes raw
+pointers and the current HIP stream.  Every step of the layer runs in the
+library's HIP kernels; there is no fallback path, and a missing or unloadable
+library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+from .configs import CONFIGS, MoEConfig, get  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_status_string",
+           "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
+           "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
+           "moe_forward")
+
+
+class CConfig(ctypes.Structure):
+    """Mirror of moe_config (include/moe.h)."""
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("temperature", ctypes.c_float), ("cap_num", ctypes.c_int32),
+                ("cap_den", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: status {status} ({message})")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} not found: build it first (python -m mixture_experts_layer_15_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        cp = ctypes.POINTER(CConfig)
+        L.moe_capacity.argtypes = [cp]
+        L.moe_capacity.restype = ctypes.c_int64
+        L.moe_max_rows.argtypes = [cp]
+        L.moe_max_rows.restype = ctypes.c_int64
+        L.moe_workspace_size.argtypes = [cp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_workspace_size.restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_route.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_route_from_logits.argtypes = [cp, _P, _P, _P, _P]
+        L.moe_dispatch.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_expert_ffn.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_expert_gate_up.argtypes = [cp, _P, _P, _P, _P, _P, _P]
+        L.moe_expert_down.argtypes = [cp, _P, _P, _P, _P, _P]
+        L.moe_combine.argtypes = [cp, _P, _P, _P, _P, _P]
+        L.moe_forward.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        for n in ("moe_route", "moe_route_from_logits", "moe_dispatch", "moe_expert_ffn",
+                  "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward"):
+            getattr(L, n).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def cconfig(cfg: MoEConfig, T: Optional[int] = None) -> CConfig:
+    return CConfig(T=cfg.T if T is None else T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff,
+                   temperature=cfg.temperature, cap_num=cfg.cap_num, cap_den=cfg.cap_den,
+                   renormalize=int(cfg.renormalize),
+                   dtype=MOE_BF16 if cfg.dtype == "bf16" else MOE_F32)
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        msg = lib().moe_last_error().decode()
+        raise MoEError(status, where, msg or lib().moe_status_string(status).decode())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape, device):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _dt(cfg: MoEConfig):
+    import torch
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def capacity(cfg: MoEConfig) -> int:
+    return int(lib().moe_capacity(ctypes.byref(cconfig(cfg))))
+
+
+def max_rows(cfg: MoEConfig) -> int:
+    return int(lib().moe_max_rows(ctypes.byref(cconfig(cfg))))
+
+
+def workspace_bytes(cfg: MoEConfig, dispatch_only: bool = False) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(ctypes.byref(cconfig(cfg)), int(dispatch_only),
+                                    ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def route(cfg: MoEConfig, x, w_router, bias=None):
+    """moe_route -> (logits [T,E] fp32, topk_idx [T,k] int32, topk_gate [T,k] fp32)."""
+    import torch
+    dev = x.device
+    _need(x, "x", _dt(cfg), (cfg.T, cfg.d), dev)
+    _need(w_router, "w_router", _dt(cfg), (cfg.d, cfg.E), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (cfg.E,), dev)
+    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    _check(lib().moe_route(ctypes.byref(cconfig(cfg)), _ptr(x), _ptr(w_router), _ptr(bias),
+                           _ptr(logits), _ptr(idx), _ptr(gate), _stream()), "moe_route")
+    return logits, idx, gate
+
+
+def route_from_logits(cfg: MoEConfig, logits):
+    """moe_route_from_logits -> (topk_idx, topk_gate) from given fp32 logits."""
+    import torch
+    dev = logits.device
+    _need(logits, "logits", torch.float32, (cfg.T, cfg.E), dev)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    _check(lib().moe_route_from_logits(ctypes.byref(cconfig(cfg)), _ptr(logits), _ptr(idx),
+                                       _ptr(gate), _stream()), "moe_route_from_logits")
+    return idx, gate
+
+
+def dispatch(cfg: MoEConfig, topk_idx, x) -> Dict:
+    """moe_dispatch -> dict(x_perm, expert_count, expert_offset, row_of, token_of_row)."""
+    import torch
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int32, (cfg.T, cfg.k), dev)
+    _need(x, "x", _dt(cfg), (cfg.T, cfg.d), dev)
+    R = max_rows(cfg)
+    out = dict(
+        x_perm=torch.empty((R, cfg.d), dtype=_dt(cfg), device=dev),
+        expert_count=torch.empty(cfg.E, dtype=torch.int32, device=dev),
+        expert_offset=torch.empty(cfg.E + 1, dtype=torch.int32, device=dev),
+        row_of=torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
+        token_of_row=torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
+    wsb = workspace_bytes(cfg, dispatch_only=True)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check(lib().moe_dispatch(ctypes.byref(cconfig(cfg)), _ptr(topk_idx), _ptr(x),
+                              _ptr(out["x_perm"]), _ptr(out["expert_count"]),
+                              _ptr(out["expert_offset"]), _ptr(out["row_of"]),
+                              _ptr(out["token_of_row"]), _ptr(ws), wsb, _stream()),
+           "moe_dispatch")
+    out["_workspace"] = ws   # keep alive until the stream has run
+    return out
+
+
+def expert_ffn(cfg: MoEConfig, x_perm, expert_offset, w_gate, w_up, w_down) -> Tuple:
+    """moe_expert_ffn -> (h [R, d_ff], y_perm [R, d])."""
+    import torch
+    dev = x_perm.device
+    R = max_rows(cfg)
+    _need(x_perm, "x_perm", _dt(cfg), (R, cfg.d), dev)
+    _need(expert_offset, "expert_offset", torch.int32, (cfg.E + 1,), dev)
+    _need(w_gate, "w_gate", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
+    _need(w_up, "w_up", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
+    _need(w_down, "w_down", _dt(cfg), (cfg.E, cfg.d_ff, cfg.d), dev)
+    h = torch.empty((R, cfg.d_ff), dtype=_dt(cfg), device=dev)
+    y_perm = torch.empty((R, cfg.d), dtype=_dt(cfg), device=dev)
+    _check(lib().moe_expert_ffn(ctypes.byref(cconfig(cfg)), _ptr(x_perm), _ptr(expert_offset),
+                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(y_perm),
+                                _stream()), "moe_expert_ffn")
+    return h, y_perm
+
+
+def expert_gate_up(cfg: MoEConfig, x_perm, expert_offset, w_gate, w_up, h=None):
+    """moe_expert_gate_up -> h [R, d_ff]."""
+    import torch
+    dev = x_perm.device
+    R = max_rows(cfg)
+    _need(x_perm, "x_perm", _dt(cfg), (R, cfg.d), dev)
+    _need(expert_offset, "expert_offset", torch.int32, (cfg.E + 1,), dev)
+    _need(w_gate, "w_gate", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
+    _need(w_up, "w_up", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
+    if h is None:
+        h = torch.empty((R, cfg.d_ff), dtype=_dt(cfg), device=dev)
+    _need(h, "h", _dt(cfg), (R, cfg.d_ff), dev)
+    _check(lib().moe_expert_gate_up(ctypes.byref(cconfig(cfg)), _ptr(x_perm), _ptr(expert_offset),
+                                    _ptr(w_gate), _ptr(w_up), _ptr(h), _stream()),
+           "moe_expert_gate_up")
+    return h
+
+
+def expert_down(cfg: MoEConfig, h, expert_offset, w_down, y_perm=None):
+    """moe_expert_down -> y_perm [R, d]."""
+    import torch
+    dev = h.device
+    R = max_rows(cfg)
+    _need(h, "h", _dt(cfg), (R, cfg.d_ff), dev)
+    _need(expert_offset, "expert_offset", torch.int32, (cfg.E + 1,), dev)
+    _need(w_down, "w_down", _dt(cfg), (cfg.E, cfg.d_ff, cfg.d), dev)
+    if y_perm is None:
+        y_perm = torch.empty((R, cfg.d), dtype=_dt(cfg), device=dev)
+    _need(y_perm, "y_perm", _dt(cfg), (R, cfg.d), dev)
+    _check(lib().moe_expert_down(ctypes.byref(cconfig(cfg)), _ptr(h), _ptr(expert_offset),
+                                 _ptr(w_down), _ptr(y_perm), _stream()), "moe_expert_down")
+    return y_perm
+
+
+def combine(cfg: MoEConfig, y_perm, row_of, topk_gate):
+    """moe_combine -> y [T, d]."""
+    import torch
+    dev = y_perm.device
+    _need(y_perm, "y_perm", _dt(cfg), (max_rows(cfg), cfg.d), dev)
+    _need(row_of, "row_of", torch.int32, (cfg.T, cfg.k), dev)
+    _need(topk_gate, "topk_gate", torch.float32, (cfg.T, cfg.k), dev)
+    y = torch.empty((cfg.T, cfg.d), dtype=_dt(cfg), device=dev)
+    _check(lib().moe_combine(ctypes.byref(cconfig(cfg)), _ptr(y_perm), _ptr(row_of),
+                             _ptr(topk_gate), _ptr(y), _stream()), "moe_combine")
+    return y
+
+
+class Forward:
+    """moe_forward with a workspace allocated once and reused across calls."""
+
+    def __init__(self, cfg: MoEConfig, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.c = cconfig(cfg)
+        self.ws_bytes = workspace_bytes(cfg)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+
+    def __call__(self, x, w_router, bias, w_gate, w_up, w_down, y=None):
+        import torch
+        cfg = self.cfg
+        dev = x.device
+        _need(x, "x", _dt(cfg), (cfg.T, cfg.d), dev)
+        _need(w_router, "w_router", _dt(cfg), (cfg.d, cfg.E), dev)
+        if bias is not None:
+            _need(bias, "bias", torch.float32, (cfg.E,), dev)
+        _need(w_gate, "w_gate", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
+        _need(w_up, "w_up", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
+        _need(w_down, "w_down", _dt(cfg), (cfg.E, cfg.d_ff, cfg.d), dev)
+        if y is None:
+            y = torch.empty((cfg.T, cfg.d), dtype=_dt(cfg), device=dev)
+        _check(lib().moe_forward(ctypes.byref(self.c), _ptr(x), _ptr(w_router), _ptr(bias),
+                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(self.ws),
+                                 self.ws_bytes, _stream()), "moe_forward")
+        return y
+
+
+def forward(cfg: MoEConfig, x, w_router, bias, w_gate, w_up, w_down):
+    """moe_forward -> y [T, d] (allocates a fresh workspace)."""
+    return Forward(cfg, device=x.device)(x, w_router, bias, w_gate, w_up, w_down)

@@ -1,0 +1,85 @@
+// combine.hip -- gate-weighted un-permute and combine on gfx950.
+//
+// y[t] = sum over j = 0..k-1 (ascending) with row_of[t][j] >= 0 of
+//        gate[t][j] * y_perm[row_of[t][j]], accumulated in fp32 and rounded
+//        once to the output type; y[t] = 0 when nothing was kept.
+// A gather (each output row is written exactly once, no atomics), so the
+// result is deterministic.  One wave per token, 16-byte vector loads and
+// stores; bound by HBM bandwidth.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ gate,
+                                                      u32x4* __restrict__ y, long long ntok,
+                                                      int nvec, int k) {
+    constexpr int PV = Elem<T>::kPerVec;
+    const int lane = threadIdx.x & 63;
+    const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+    int rows[8];
+    float g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        rows[j] = (j < k) ? row_of[t * k + j] : -1;
+        g[j] = (rows[j] >= 0) ? gate[t * k + j] : 0.f;
+    }
+    u32x4* dst = y + t * nvec;
+    for (int v0 = lane; v0 < nvec; v0 += 2 * 64) {
+        float acc[2][PV];
+        u32x4 in[2][8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int i = 0; i < PV; ++i) acc[u][i] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (rows[j] >= 0 && v0 + u * 64 < nvec)
+                    in[u][j] = y_perm[(long long)rows[j] * nvec + v0 + u * 64];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (v0 + u * 64 >= nvec) continue;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (rows[j] < 0) continue;
+#pragma unroll
+                for (int i = 0; i < PV; ++i)
+                    acc[u][i] = fmaf(g[j], Elem<T>::to_f32(in[u][j], i), acc[u][i]);
+            }
+            u32x4 out;
+            if constexpr (PV == 8) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) out[p] = pack_bf16x2(acc[u][2 * p], acc[u][2 * p + 1]);
+            } else {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) out[p] = __float_as_uint(acc[u][p]);
+            }
+            dst[v0 + u * 64] = out;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
+                          const float* gate, void* y, long long T, int d, int k,
+                          hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid((unsigned)((T + 3) / 4));
+    if (dtype == 1) {
+        hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, (const u32x4*)y_perm,
+                           row_of, gate, (u32x4*)y, T, d / 8, k);
+    } else {
+        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, (const u32x4*)y_perm,
+                           row_of, gate, (u32x4*)y, T, d / 4, k);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,58 @@
+// common.h -- device types and helpers shared by the gfx950 kernels of the
+// MoE FFN forward.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// 16-byte vector used for every coalesced global/LDS copy.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// MFMA operand and accumulator fragments.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// bf16 <-> fp32.  bf16 is the upper half of an IEEE binary32, so widening is
+// exact; narrowing rounds to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+// Two fp32 -> packed pair of bf16 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// GELU in its erf form, v * Phi(v), in fp32 with the device library's erff.
+__device__ __forceinline__ float gelu_erf(float v) {
+    return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
+}
+
+// Element type traits: raw storage type and 16-byte vector width.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kPerVec = 4;
+    __device__ __forceinline__ static float to_f32(const u32x4& v, int i) {
+        return __uint_as_float(v[i]);
+    }
+};
+template <> struct Elem<uint16_t> {
+    static constexpr int kPerVec = 8;
+    __device__ __forceinline__ static float to_f32(const u32x4& v, int i) {
+        uint32_t w = v[i >> 1];
+        return bf16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace moe

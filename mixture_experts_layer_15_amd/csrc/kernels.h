@@ -1,0 +1,55 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public interface is include/moe.h).  Every launcher only
+// enqueues on the given stream and returns the HIP error of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace moe {
+
+// Router: logits = x W_r + b (fp32 accumulation), softmax(l / tau), top-k, gates.
+hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* bias,
+                        float* logits, int32_t* idx, float* gate, long long T, int d, int E,
+                        int k, float tau, int renorm, hipStream_t s);
+// Top-k and gates from given fp32 logits.
+hipError_t launch_route_from_logits(const float* logits, int32_t* idx, float* gate,
+                                    long long T, int E, int k, float tau, int renorm,
+                                    hipStream_t s);
+
+// Dispatch.  Tokens are cut into nblk blocks of blk_tokens (a multiple of 256)
+// with nblk <= 256; workspace holds two [nblk][E] int32 tables.
+struct DispatchPlan {
+    long long T;
+    int E, k;
+    long long C;
+    int blk_tokens, nblk;
+};
+DispatchPlan plan_dispatch(long long T, int E, int k, long long C);
+size_t dispatch_workspace_bytes(const DispatchPlan& p);
+hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx, const void* x,
+                           void* x_perm, int32_t* count, int32_t* offset, int32_t* row_of,
+                           int32_t* token_of_row, void* workspace, int d, hipStream_t s);
+
+// Grouped GeGLU expert FFN (gate/up GEMM with fused epilogue, then down GEMM).
+hipError_t launch_expert_ffn(int dtype, const void* x_perm, const int32_t* off,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             void* h, void* y_perm, int E, int d, int d_ff,
+                             long long max_rows, int grid_cap, hipStream_t s);
+
+// The two halves of the expert FFN, one launch each.
+hipError_t launch_gate_up(int dtype, const void* x_perm, const int32_t* off, const void* w_gate,
+                          const void* w_up, void* h, int E, int d, int d_ff, long long max_rows,
+                          int grid_cap, hipStream_t s);
+hipError_t launch_down(int dtype, const void* h, const int32_t* off, const void* w_down,
+                       void* y_perm, int E, int d, int d_ff, long long max_rows, int grid_cap,
+                       hipStream_t s);
+
+// Gate-weighted combine.
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
+                          const float* gate, void* y, long long T, int d, int k,
+                          hipStream_t s);
+
+}  // namespace moe

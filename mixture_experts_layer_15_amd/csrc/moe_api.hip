@@ -1,0 +1,349 @@
+// moe_api.hip -- the C ABI (include/moe.h): argument validation, workspace
+// carving and launch sequencing.  Host code only; every entry point checks
+// its arguments before enqueuing anything and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+    return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Exact ceil(cap_num * k * T / (cap_den * E)), saturating; T when cap_den == 0.
+int64_t capacity_raw(const moe_config* c) {
+    if (c->cap_den == 0) return c->T;
+    const __int128 num = (__int128)c->cap_num * c->k * c->T;
+    const __int128 den = (__int128)c->cap_den * c->E;
+    const __int128 q = (num + den - 1) / den;
+    return q > (__int128)INT64_MAX ? INT64_MAX : (int64_t)q;
+}
+
+// Capacity as the kernels use it: a limit of T or more never drops anything.
+int64_t capacity_eff(const moe_config* c) {
+    const int64_t C = capacity_raw(c);
+    return C < c->T ? C : c->T;
+}
+
+int64_t max_rows(const moe_config* c) {
+    const int64_t tk = c->T * c->k;
+    const int64_t ce = capacity_eff(c) * c->E;
+    return tk < ce ? tk : ce;
+}
+
+size_t esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status check_cfg(const moe_config* c) {
+    if (c == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+    if (c->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld < 0", (long long)c->T);
+    if (c->E < 1 || c->E > 256) return fail(MOE_ERR_INVALID_ARG, "E = %d outside [1, 256]", c->E);
+    if (c->k < 1 || c->k > c->E || c->k > 8)
+        return fail(MOE_ERR_INVALID_ARG, "k = %d outside [1, min(E, 8)]", c->k);
+    if (c->d < 64 || c->d > 16384 || c->d % 64 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "d = %d: need a multiple of 64 in [64, 16384]", c->d);
+    if (c->d_ff < 64 || c->d_ff > 65536 || c->d_ff % 64 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "d_ff = %d: need a multiple of 64 in [64, 65536]", c->d_ff);
+    if (c->T > 0 && c->T * (int64_t)c->k >= (int64_t)1 << 31)
+        return fail(MOE_ERR_INVALID_ARG, "T * k = %lld must be < 2^31", (long long)(c->T * c->k));
+    if (!(c->temperature > 0.f) || !std::isfinite(c->temperature))
+        return fail(MOE_ERR_INVALID_ARG, "temperature must be finite and > 0");
+    if (c->cap_den < 0 || (c->cap_den > 0 && c->cap_num < 0))
+        return fail(MOE_ERR_INVALID_ARG, "capacity factor %d/%d invalid", c->cap_num, c->cap_den);
+    if (c->renormalize != 0 && c->renormalize != 1)
+        return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1");
+    if (c->dtype != MOE_F32 && c->dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
+    return MOE_OK;
+}
+
+// A NULL pointer is accepted only for an optional argument or an empty buffer.
+moe_status check_ptr(const void* p, const char* name, size_t bytes, bool optional = false) {
+    if (p == nullptr) {
+        if (optional || bytes == 0) return MOE_OK;
+        return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+    }
+    if (((uintptr_t)p & 15u) != 0)
+        return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return MOE_OK;
+}
+
+// Element counts of a config, as size_t, for pointer checks.
+#define SIZES(c)                                                              \
+    const size_t T = (size_t)(c)->T, d = (size_t)(c)->d, E = (size_t)(c)->E;  \
+    const size_t k = (size_t)(c)->k, F = (size_t)(c)->d_ff, es = esize(c);    \
+    const size_t R = (size_t)max_rows(c);                                     \
+    (void)T; (void)d; (void)E; (void)k; (void)F; (void)es; (void)R
+
+#define CHECK(expr)                          \
+    do {                                     \
+        moe_status _s = (expr);              \
+        if (_s != MOE_OK) return _s;         \
+    } while (0)
+
+// Persistent-grid size of the grouped GEMM: two workgroups per CU.
+int gemm_grid_cap() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    v = 2 * cus;
+    v = (v + 7) / 8 * 8;
+    cached[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+struct FwdLayout {
+    size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, h, y_perm, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+FwdLayout fwd_layout(const moe_config* c) {
+    const size_t T = (size_t)c->T, E = (size_t)c->E, k = (size_t)c->k;
+    const size_t R = (size_t)max_rows(c);
+    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c));
+    FwdLayout L;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+    L.logits = take(T * E * 4);
+    L.idx = take(T * k * 4);
+    L.gate = take(T * k * 4);
+    L.count = take(E * 4);
+    L.offset = take((E + 1) * 4);
+    L.row_of = take(T * k * 4);
+    L.token_of_row = take(T * k * 4);
+    L.dsp = take(moe::dispatch_workspace_bytes(p));
+    L.x_perm = take(R * (size_t)c->d * esize(c));
+    L.h = take(R * (size_t)c->d_ff * esize(c));
+    L.y_perm = take(R * (size_t)c->d * esize(c));
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity(const moe_config* cfg) {
+    if (check_cfg(cfg) != MOE_OK) return -1;
+    return capacity_raw(cfg);
+}
+
+int64_t moe_max_rows(const moe_config* cfg) {
+    if (check_cfg(cfg) != MOE_OK) return -1;
+    return max_rows(cfg);
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, int dispatch_only, size_t* bytes) {
+    CHECK(check_cfg(cfg));
+    if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    if (dispatch_only) {
+        *bytes = moe::dispatch_workspace_bytes(
+            moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg)));
+    } else {
+        *bytes = fwd_layout(cfg).total;
+    }
+    return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* bias, float* logits, int32_t* topk_idx, float* topk_gate,
+                     void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    CHECK(check_ptr(x, "x", T * d * es));
+    CHECK(check_ptr(w_router, "w_router", d * E * es));
+    CHECK(check_ptr(bias, "bias", E * 4, true));
+    CHECK(check_ptr(logits, "logits", T * E * 4));
+    CHECK(check_ptr(topk_idx, "topk_idx", T * k * 4));
+    CHECK(check_ptr(topk_gate, "topk_gate", T * k * 4));
+    hipError_t e = moe::launch_route(cfg->dtype, x, w_router, bias, logits, topk_idx, topk_gate,
+                                     cfg->T, cfg->d, cfg->E, cfg->k, cfg->temperature,
+                                     cfg->renormalize, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
+}
+
+moe_status moe_route_from_logits(const moe_config* cfg, const float* logits, int32_t* topk_idx,
+                                 float* topk_gate, void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    CHECK(check_ptr(logits, "logits", T * E * 4));
+    CHECK(check_ptr(topk_idx, "topk_idx", T * k * 4));
+    CHECK(check_ptr(topk_gate, "topk_gate", T * k * 4));
+    hipError_t e = moe::launch_route_from_logits(logits, topk_idx, topk_gate, cfg->T, cfg->E,
+                                                 cfg->k, cfg->temperature, cfg->renormalize,
+                                                 (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_from_logits");
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                        void* x_perm, int32_t* expert_count, int32_t* expert_offset,
+                        int32_t* row_of, int32_t* token_of_row, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    CHECK(check_ptr(topk_idx, "topk_idx", T * k * 4));
+    CHECK(check_ptr(x, "x", T * d * es));
+    CHECK(check_ptr(x_perm, "x_perm", R * d * es));
+    if (expert_count == nullptr || expert_offset == nullptr)
+        return fail(MOE_ERR_INVALID_ARG, "expert_count / expert_offset is NULL");
+    CHECK(check_ptr(expert_count, "expert_count", E * 4));
+    CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
+    CHECK(check_ptr(row_of, "row_of", T * k * 4));
+    CHECK(check_ptr(token_of_row, "token_of_row", T * k * 4));
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg));
+    const size_t need = moe::dispatch_workspace_bytes(p);
+    if (workspace == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "dispatch workspace: need %zu bytes, got %zu", need, ws_bytes);
+    CHECK(check_ptr(workspace, "workspace", 1));
+    hipError_t e = moe::launch_dispatch(p, cfg->dtype, topk_idx, x, x_perm, expert_count,
+                                        expert_offset, row_of, token_of_row, workspace, cfg->d,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_dispatch");
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offset,
+                          const void* w_gate, const void* w_up, const void* w_down, void* h,
+                          void* y_perm, void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    if (expert_offset == nullptr) return fail(MOE_ERR_INVALID_ARG, "expert_offset is NULL");
+    CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
+    CHECK(check_ptr(x_perm, "x_perm", R * d * es));
+    CHECK(check_ptr(w_gate, "w_gate", E * d * F * es));
+    CHECK(check_ptr(w_up, "w_up", E * d * F * es));
+    CHECK(check_ptr(w_down, "w_down", E * d * F * es));
+    CHECK(check_ptr(h, "h", R * F * es));
+    CHECK(check_ptr(y_perm, "y_perm", R * d * es));
+    hipError_t e = moe::launch_expert_ffn(cfg->dtype, x_perm, expert_offset, w_gate, w_up, w_down,
+                                          h, y_perm, cfg->E, cfg->d, cfg->d_ff, max_rows(cfg),
+                                          gemm_grid_cap(), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn");
+}
+
+moe_status moe_expert_gate_up(const moe_config* cfg, const void* x_perm,
+                              const int32_t* expert_offset, const void* w_gate, const void* w_up,
+                              void* h, void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    if (expert_offset == nullptr) return fail(MOE_ERR_INVALID_ARG, "expert_offset is NULL");
+    CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
+    CHECK(check_ptr(x_perm, "x_perm", R * d * es));
+    CHECK(check_ptr(w_gate, "w_gate", E * d * F * es));
+    CHECK(check_ptr(w_up, "w_up", E * d * F * es));
+    CHECK(check_ptr(h, "h", R * F * es));
+    hipError_t e = moe::launch_gate_up(cfg->dtype, x_perm, expert_offset, w_gate, w_up, h, cfg->E,
+                                       cfg->d, cfg->d_ff, max_rows(cfg), gemm_grid_cap(),
+                                       (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_gate_up");
+}
+
+moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offset,
+                           const void* w_down, void* y_perm, void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    if (expert_offset == nullptr) return fail(MOE_ERR_INVALID_ARG, "expert_offset is NULL");
+    CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
+    CHECK(check_ptr(h, "h", R * F * es));
+    CHECK(check_ptr(w_down, "w_down", E * d * F * es));
+    CHECK(check_ptr(y_perm, "y_perm", R * d * es));
+    hipError_t e = moe::launch_down(cfg->dtype, h, expert_offset, w_down, y_perm, cfg->E, cfg->d,
+                                    cfg->d_ff, max_rows(cfg), gemm_grid_cap(), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_down");
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of,
+                       const float* topk_gate, void* y, void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    CHECK(check_ptr(y_perm, "y_perm", R * d * es));
+    CHECK(check_ptr(row_of, "row_of", T * k * 4));
+    CHECK(check_ptr(topk_gate, "topk_gate", T * k * 4));
+    CHECK(check_ptr(y, "y", T * d * es));
+    hipError_t e = moe::launch_combine(cfg->dtype, y_perm, row_of, topk_gate, y, cfg->T, cfg->d,
+                                       cfg->k, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine");
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* bias, const void* w_gate, const void* w_up,
+                       const void* w_down, void* y, void* workspace, size_t ws_bytes,
+                       void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    CHECK(check_ptr(x, "x", T * d * es));
+    CHECK(check_ptr(w_router, "w_router", d * E * es));
+    CHECK(check_ptr(bias, "bias", E * 4, true));
+    CHECK(check_ptr(w_gate, "w_gate", E * d * F * es));
+    CHECK(check_ptr(w_up, "w_up", E * d * F * es));
+    CHECK(check_ptr(w_down, "w_down", E * d * F * es));
+    CHECK(check_ptr(y, "y", T * d * es));
+    const FwdLayout L = fwd_layout(cfg);
+    if (workspace == nullptr || ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE, "forward workspace: need %zu bytes, got %zu", L.total, ws_bytes);
+    CHECK(check_ptr(workspace, "workspace", 1));
+    char* w = (char*)workspace;
+    float* logits = (float*)(w + L.logits);
+    int32_t* idx = (int32_t*)(w + L.idx);
+    float* gate = (float*)(w + L.gate);
+    int32_t* count = (int32_t*)(w + L.count);
+    int32_t* offset = (int32_t*)(w + L.offset);
+    int32_t* row_of = (int32_t*)(w + L.row_of);
+    int32_t* tor = (int32_t*)(w + L.token_of_row);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T,
+                                     cfg->d, cfg->E, cfg->k, cfg->temperature, cfg->renormalize, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg));
+    e = moe::launch_dispatch(p, cfg->dtype, idx, x, w + L.x_perm, count, offset, row_of, tor,
+                             w + L.dsp, cfg->d, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/dispatch");
+    e = moe::launch_expert_ffn(cfg->dtype, w + L.x_perm, offset, w_gate, w_up, w_down, w + L.h,
+                               w + L.y_perm, cfg->E, cfg->d, cfg->d_ff, max_rows(cfg),
+                               gemm_grid_cap(), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/expert_ffn");
+    e = moe::launch_combine(cfg->dtype, w + L.y_perm, row_of, gate, y, cfg->T, cfg->d, cfg->k, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""Shared helpers of the GPU parity tests: input placement, tolerance
+formulas and the oracle comparisons.  The expected values always come from
+the fp64 oracle; nothing here computes a step of the layer itself."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import mixture_experts_layer_15_amd as moe
+from mixture_experts_layer_15_amd import synthetic
+from oracle import oracle as orc
+
+U32 = 2.0 ** -24          # unit roundoff of fp32
+TOL_Y = {"bf16": 2e-2, "f32": 1e-5}   # max |y - y*| / max |y*| over the output
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gpu_inputs(cfg, seed=0):
+    """Inputs on the GPU plus host copies for the oracle.  Small layers are
+    drawn on the CPU (identical everywhere); large ones on the GPU."""
+    small = cfg.E * cfg.d * cfg.d_ff <= (1 << 24) and cfg.T * cfg.d <= (1 << 24)
+    if small:
+        host = synthetic.make_inputs(cfg, seed=seed, device="cpu")
+        dev = {k: (None if v is None else v.cuda()) for k, v in host.items()}
+    else:
+        dev = synthetic.make_inputs(cfg, seed=seed, device="cuda")
+        torch.cuda.synchronize()
+        host = {k: (None if v is None else v.cpu()) for k, v in dev.items()}
+    return dev, host
+
+
+def rel_err(got, want) -> float:
+    """max |got - want| / max |want| (0 when both are exactly zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    scale = np.abs(want).max() if want.size else 0.0
+    diff = np.abs(got - want).max() if want.size else 0.0
+    if scale == 0.0:
+        return 0.0 if diff == 0.0 else math.inf
+    return diff / scale
+
+
+def check_logits(logits_gpu, x_host, wr_host, bias_host, tokens):
+    """GPU fp32 logits against the oracle's fp64 logits within the fp32
+    summation bound |l - l*| <= 2 g_K sum_i |x_i w_i| + 2u |l*| (+ bias term),
+    g_K = K u / (1 - K u) (the factor 2 covers the MFMA's internal order)."""
+    xs = x_host[tokens]
+    want = orc.logits(xs, wr_host, bias_host)
+    K = x_host.shape[1]
+    gk = K * U32 / (1 - K * U32)
+    ax = np.abs(xs.double().numpy())
+    aw = np.abs(wr_host.double().numpy())
+    bound = 2 * gk * (ax @ aw) + 2 * U32 * np.abs(want) + 1e-30
+    got = logits_gpu[tokens].double().numpy()
+    over = np.abs(got - want) > bound
+    assert not over.any(), f"logits outside the fp32 bound at {np.argwhere(over)[:5]}"
+    return float((np.abs(got - want) / np.maximum(np.abs(want), 1e-30)).max())
+
+
+def check_route(cfg, logits_gpu, idx_gpu, gate_gpu):
+    """Same-fp32-logits protocol: the oracle routes the GPU's logits; indices
+    must match exactly, gates within an fp32 error bound of the softmax."""
+    lg = logits_gpu.double().numpy()
+    tau = float(np.float32(cfg.temperature))
+    oidx, ogate = orc.route(lg, cfg.k, tau, cfg.renormalize)
+    gidx = idx_gpu.numpy()
+    bad = np.argwhere(gidx != oidx)
+    assert bad.size == 0, f"top-k differs at {bad[:5]}: gpu {gidx[bad[0][0]]} oracle {oidx[bad[0][0]]}"
+    # fp32 gate error: exp argument (l_j - max)/tau rounded twice and amplified by
+    # exp, plus the sum of E terms and the division
+    a = (np.take_along_axis(lg, oidx, 1) - lg.max(1, keepdims=True)) / tau
+    # below fp32's normal range (2^-126) there is no relative precision left (and
+    # the hardware may flush to zero): an absolute slack of 2^-126 covers that
+    tol = (4 * np.abs(a) + 2 * cfg.E + 24) * U32 * ogate + 2.0 ** -126
+    g = gate_gpu.double().numpy()
+    err = np.abs(g - ogate)
+    bad = err > tol
+    assert not bad.any(), f"gate error {err[bad].max():.3g} above bound at {np.argwhere(bad)[:5]}"
+    rel = err / ogate
+    return oidx, ogate, float(rel.max())
+
+
+def check_dispatch(cfg, oidx, dsp):
+    """Integer outputs of dispatch bit-exact against the oracle."""
+    C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    od = orc.dispatch(oidx, cfg.E, C)
+    n = od["n_kept"]
+    np.testing.assert_array_equal(dsp["expert_count"].cpu().numpy(), od["count"])
+    np.testing.assert_array_equal(dsp["expert_offset"].cpu().numpy(), od["offset"])
+    np.testing.assert_array_equal(dsp["row_of"].cpu().numpy(), od["row_of"])
+    tor = dsp["token_of_row"].cpu().numpy()
+    np.testing.assert_array_equal(tor[:n], od["token_of_row"])
+    assert (tor[n:] == -1).all()
+    return od
+
+
+def check_x_perm(x_dev, x_perm, token_of_row, n):
+    """x_perm[r] is byte-for-byte x[token_of_row[r]] for every kept row."""
+    if n == 0:
+        return
+    tor = torch.from_numpy(np.ascontiguousarray(token_of_row[:n])).long().cuda()
+    a = x_perm[:n]
+    b = x_dev.index_select(0, tor)
+    iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(a.view(iv), b.view(iv)), "x_perm rows differ from x"
+
+
+def expert_of_rows(offset, rows):
+    return np.searchsorted(offset, rows, side="right") - 1
+
+
+def sample_rows(offset, n, full, rng, extra=96):
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
+    if full:
+        return np.arange(n)
+    pick = set()
+    E = len(offset) - 1
+    for e in range(E):
+        if offset[e + 1] > offset[e]:
+            pick.update({int(offset[e]), int(offset[e + 1] - 1)})
+    pick.update(rng.integers(0, n, size=extra).tolist())
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def to_np(t):
+    return t.float().cpu().double().numpy() if t.dtype == torch.bfloat16 else t.cpu().double().numpy()

@@ -1,0 +1,145 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects invalid arguments on the host before touching a
+GPU.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_15_amd as moe
+from mixture_experts_layer_15_amd import configs
+from oracle import oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from mixture_experts_layer_15_amd import build
+        build.build()
+    return moe.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    decl = _declared()
+    assert set(decl) == set(moe.EXPORTS), decl
+    for name in decl:
+        assert hasattr(L, name), name
+    # the exported names are plain C symbols (no C++ mangling)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = set(re.findall(r" T (moe_\w+)", out))
+    assert set(decl) <= syms
+
+
+def test_status_strings(L):
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+    assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("ci", range(len(configs.CONFIGS)))
+def test_capacity_matches_oracle(L, ci):
+    cfg = configs.CONFIGS[ci]
+    want = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    assert moe.capacity(cfg) == want
+    assert moe.max_rows(cfg) == min(cfg.T * cfg.k, min(want, cfg.T) * cfg.E)
+
+
+def test_capacity_edge_values(L):
+    base = configs.get("tiny")
+    for (T, E, k, n, dd, want) in [(10, 3, 1, 5, 4, 5), (12, 3, 1, 1, 1, 4), (7, 2, 2, 0, 1, 0),
+                                   (0, 4, 1, 5, 4, 0), (1 << 20, 256, 8, 1 << 30, 1, None)]:
+        c = base.scaled(T=T, E=E, k=k, cap_num=n, cap_den=dd)
+        got = moe.capacity(c)
+        if want is None:   # huge factor: exact ceil, no overflow
+            assert got == -(-(n * k * T) // (dd * E))
+        else:
+            assert got == want == orc.capacity(T, E, k, n, dd)
+
+
+BAD = [
+    (dict(k=5), "k"), (dict(k=9, E=16), "k"), (dict(E=0, k=1), "E"), (dict(E=257), "E"),
+    (dict(d=96), "d"), (dict(d=0), "d"), (dict(d_ff=100), "d_ff"), (dict(T=-1), "T"),
+    (dict(T=1 << 30, k=2, E=4), "T * k"), (dict(temperature=0.0), "temperature"),
+    (dict(temperature=-1.0), "temperature"), (dict(temperature=float("inf")), "temperature"),
+    (dict(temperature=float("nan")), "temperature"), (dict(cap_num=-1, cap_den=4), "capacity"),
+    (dict(cap_den=-1), "capacity"),
+]
+
+
+@pytest.mark.parametrize("kw,word", BAD)
+def test_invalid_config_rejected_on_host(L, kw, word):
+    cfg = configs.get("tiny").scaled(**kw)
+    c = moe.cconfig(cfg)
+    assert L.moe_capacity(ctypes.byref(c)) == -1
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(c), 0, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    st = L.moe_route(ctypes.byref(c), fake, fake, None, fake, fake, fake, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    assert word in L.moe_last_error().decode()
+
+
+def test_bad_flags_and_dtype(L):
+    c = moe.cconfig(configs.get("tiny"))
+    c.renormalize = 2
+    assert L.moe_capacity(ctypes.byref(c)) == -1
+    c = moe.cconfig(configs.get("tiny"))
+    c.dtype = 7
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(c), 1, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_size(None, 1, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_null_and_misaligned_pointers_rejected(L):
+    c = moe.cconfig(configs.get("zaya1"))
+    ok = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    assert L.moe_route(ctypes.byref(c), None, ok, None, ok, ok, ok, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in L.moe_last_error()
+    assert L.moe_route(ctypes.byref(c), ok, odd, None, ok, ok, ok, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"aligned" in L.moe_last_error()
+    assert L.moe_combine(ctypes.byref(c), ok, ok, ok, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn(ctypes.byref(c), ok, None, ok, ok, ok, ok, ok, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route_from_logits(ctypes.byref(c), ok, ok, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_rejected(L):
+    cfg = configs.get("wide")
+    c = moe.cconfig(cfg)
+    ok = ctypes.c_void_p(1 << 20)
+    need = moe.workspace_bytes(cfg, dispatch_only=True)
+    st = L.moe_dispatch(ctypes.byref(c), ok, ok, ok, ok, ok, ok, ok, ok, need - 1, None)
+    assert st == moe.MOE_ERR_WORKSPACE and b"need" in L.moe_last_error()
+    st = L.moe_dispatch(ctypes.byref(c), ok, ok, ok, ok, ok, ok, ok, None, need, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    fneed = moe.workspace_bytes(cfg)
+    st = L.moe_forward(ctypes.byref(c), ok, ok, None, ok, ok, ok, ok, ok, fneed - 1, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+
+
+def test_workspace_sizes_cover_intermediates(L):
+    for cfg in configs.CONFIGS:
+        R = moe.max_rows(cfg)
+        es = 2 if cfg.dtype == "bf16" else 4
+        inter = R * (2 * cfg.d + cfg.d_ff) * es + cfg.T * (cfg.E + 4 * cfg.k) * 4
+        assert moe.workspace_bytes(cfg) >= inter
+        assert 0 < moe.workspace_bytes(cfg, dispatch_only=True) <= 2 * 256 * cfg.E * 4
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoe_mi355x.so")
+    with pytest.raises(RuntimeError, match="not found"):
+        moe.lib()

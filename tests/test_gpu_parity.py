@@ -1,0 +1,194 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Protocol: the oracle routes the GPU's exported fp32 logits (the layer makes
+integer decisions -- top-k, drops, positions -- from fp32 logits, so both
+sides decide from the same values); those decisions must match bit-exactly.
+The logits themselves must sit within the fp32 summation bound of the
+oracle's fp64 logits; floating outputs must satisfy
+max |y - y*| / max |y*| <= 2e-2 (bf16 layers) or 1e-5 (fp32 layers).
+
+Small shapes are compared element by element over every output; the five
+full-size layers on sampled rows and tokens (each expert's first and last row
+plus random ones) that the oracle computes one by one, in the same launch
+configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_15_amd as moe
+from mixture_experts_layer_15_amd import configs
+from oracle import oracle as orc
+
+from parity_util import (TOL_Y, check_dispatch, check_logits, check_route, check_x_perm,
+                         expert_of_rows, gpu_inputs, rel_err, sample_rows, say, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()   # raises if the HIP library is missing
+
+
+def run_layer(cfg, dev, host, full, seed=0, label=""):
+    """Every stage through the C ABI, each checked against the oracle."""
+    rng = np.random.default_rng(seed)
+    x, wr, b = dev["x"], dev["w_router"], dev["bias"]
+    say(f"[{label}] moe_route T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k}")
+    logits, idx, gate = moe.route(cfg, x, wr, b)
+    torch.cuda.synchronize()
+    lg_h, idx_h, gate_h = logits.cpu(), idx.cpu(), gate.cpu()
+    toks = np.arange(cfg.T) if full else np.unique(rng.integers(0, cfg.T, size=256))
+    if cfg.T:
+        check_logits(lg_h, host["x"], host["w_router"], host["bias"], toks)
+    oidx, ogate, _ = check_route(cfg, lg_h, idx_h, gate_h)
+
+    say(f"[{label}] moe_dispatch")
+    dsp = moe.dispatch(cfg, idx, x)
+    torch.cuda.synchronize()
+    od = check_dispatch(cfg, oidx, dsp)
+    n = od["n_kept"]
+    check_x_perm(x, dsp["x_perm"], od["token_of_row"], n)
+
+    say(f"[{label}] moe_expert_ffn rows={n}")
+    h, y_perm = moe.expert_ffn(cfg, dsp["x_perm"], dsp["expert_offset"], dev["w_gate"],
+                               dev["w_up"], dev["w_down"])
+    torch.cuda.synchronize()
+    rows = sample_rows(od["offset"], n, full, rng)
+    if rows.size:
+        ex = expert_of_rows(od["offset"], rows)
+        oh, oo = orc.ffn_rows(od["token_of_row"][rows], ex, host["x"], host["w_gate"],
+                              host["w_up"], host["w_down"], want_h=True)
+        eh = rel_err(to_np(h[torch.from_numpy(rows).cuda()]), oh)
+        eo = rel_err(to_np(y_perm[torch.from_numpy(rows).cuda()]), oo)
+        say(f"[{label}] h err {eh:.3g}  y_perm err {eo:.3g} over {rows.size} rows")
+        assert eh <= TOL_Y[cfg.dtype] and eo <= TOL_Y[cfg.dtype]
+
+    say(f"[{label}] moe_combine")
+    y = moe.combine(cfg, y_perm, dsp["row_of"], gate)
+    torch.cuda.synchronize()
+    if cfg.T:
+        row_of = od["row_of"]
+        if full:
+            stoks = np.arange(cfg.T)
+        else:
+            dropped = np.nonzero((row_of < 0).any(1))[0]
+            stoks = np.unique(np.concatenate([rng.integers(0, cfg.T, size=48), dropped[:16],
+                                              [0, cfg.T - 1]]))
+        ofw = orc.forward(host["x"], host["w_router"], host["bias"], host["w_gate"],
+                          host["w_up"], host["w_down"], k=cfg.k,
+                          tau=float(np.float32(cfg.temperature)), renormalize=cfg.renormalize,
+                          cap_num=cfg.cap_num, cap_den=cfg.cap_den,
+                          logits_in=lg_h.double().numpy(), tokens=stoks)
+        ey = rel_err(to_np(y[torch.from_numpy(stoks).cuda()]), ofw["y"])
+        say(f"[{label}] y err {ey:.3g} over {stoks.size} tokens")
+        assert ey <= TOL_Y[cfg.dtype]
+        fully = (row_of < 0).all(1)
+        if fully.any():   # tokens with every assignment dropped are exactly zero
+            zt = torch.from_numpy(np.nonzero(fully)[0]).cuda()
+            assert (y.index_select(0, zt).float() == 0).all()
+
+    say(f"[{label}] moe_forward")
+    yf = moe.forward(cfg, x, wr, b, dev["w_gate"], dev["w_up"], dev["w_down"])
+    torch.cuda.synchronize()
+    iv = torch.int16 if y.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(yf.view(iv), y.view(iv)), "fused forward differs from the staged calls"
+    return dict(logits=logits, idx=idx, gate=gate, dsp=dsp, h=h, y_perm=y_perm, y=y, n=n)
+
+
+SMALL = [
+    # ragged tails everywhere: T % 64, d % 128 == 64, E % 8 != 0, k = 3, heavy drops, bias
+    ("ragged", configs.get("tiny").scaled(T=1000, d=192, E=5, k=3, d_ff=320, temperature=0.5,
+                                          cap_num=1, cap_den=1, renormalize=True, dtype="bf16",
+                                          zipf_bias=1.2)),
+    ("single", configs.get("tiny").scaled(T=1, d=64, E=1, k=1, d_ff=64, dtype="bf16")),
+    ("maxEk", configs.get("tiny").scaled(T=300, d=256, E=256, k=8, d_ff=128, cap_num=5,
+                                         cap_den=4, renormalize=True, dtype="bf16")),
+    ("zero_capacity", configs.get("tiny").scaled(T=4096, d=128, E=8, k=2, d_ff=192, cap_num=0,
+                                                 cap_den=1, renormalize=True, dtype="bf16")),
+    ("f32_ragged", configs.get("tiny").scaled(T=777, d=128, E=6, k=2, d_ff=192, temperature=0.7,
+                                              cap_num=3, cap_den=2, renormalize=True)),
+    ("many_chunks", configs.get("tiny").scaled(T=70000, d=64, E=16, k=2, d_ff=64, cap_num=5,
+                                               cap_den=4, renormalize=True, dtype="bf16")),
+    ("tiles_2x", configs.get("tiny").scaled(T=2500, d=384, E=3, k=1, d_ff=448, dtype="bf16")),
+]
+
+
+@pytest.mark.parametrize("name,cfg", SMALL, ids=[s[0] for s in SMALL])
+def test_small_layers_every_element(name, cfg):
+    dev, host = gpu_inputs(cfg, seed=3)
+    run_layer(cfg, dev, host, full=True, seed=3, label=name)
+
+
+def test_hot_expert_overflow():
+    """Every token's first choice is expert 0 (large bias): capacity drops in
+    token order decide almost everything."""
+    cfg = configs.get("tiny").scaled(T=3000, d=128, E=6, k=2, d_ff=128, cap_num=5, cap_den=4,
+                                     renormalize=True, dtype="bf16", temperature=0.3)
+    dev, host = gpu_inputs(cfg, seed=4)
+    bias = torch.tensor([30.0, 0, 0, 0, 0, 0], dtype=torch.float32)
+    dev["bias"], host["bias"] = bias.cuda(), bias
+    out = run_layer(cfg, dev, host, full=True, seed=4, label="hot")
+    C = orc.capacity(cfg.T, cfg.E, cfg.k, 5, 4)
+    assert int(out["dsp"]["expert_count"][0]) == cfg.T
+    assert int(out["dsp"]["expert_offset"][1]) == C
+
+
+def test_empty_batch():
+    cfg = configs.get("tiny").scaled(T=0, dtype="bf16", d=128, d_ff=128)
+    dev, host = gpu_inputs(cfg.scaled(T=1))
+    x = dev["x"][:0]
+    logits, idx, gate = moe.route(cfg, x, dev["w_router"], None)
+    dsp = moe.dispatch(cfg, idx, x)
+    h, yp = moe.expert_ffn(cfg, dsp["x_perm"], dsp["expert_offset"], dev["w_gate"], dev["w_up"],
+                           dev["w_down"])
+    y = moe.combine(cfg, yp, dsp["row_of"], gate)
+    yf = moe.forward(cfg, x, dev["w_router"], None, dev["w_gate"], dev["w_up"], dev["w_down"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, cfg.d) and yf.shape == (0, cfg.d)
+    assert (dsp["expert_offset"].cpu() == 0).all() and (dsp["expert_count"].cpu() == 0).all()
+
+
+def test_route_from_logits_ties_and_signed_zero():
+    T, E = 64, 20
+    lg = torch.zeros((T, E), dtype=torch.float32)
+    lg[1] = torch.arange(E, dtype=torch.float32) % 3          # repeated values
+    lg[2, :] = -0.0
+    lg[2, 7] = 0.0
+    lg[3] = 1e30
+    lg[3, 5] = -1e30
+    lg[4] = torch.tensor([1.0, 1.0 + 2 ** -23] * 10)          # one-ulp differences
+    lg[5:] = torch.randint(-2, 3, (T - 5, E)).float()         # many exact ties
+    for k, tau, renorm in [(1, 1.0, False), (3, 0.3, True), (8, 2.0, True), (20, 1.0, True)]:
+        cfg = configs.get("tiny").scaled(T=T, E=E, k=min(k, 8), temperature=tau,
+                                         renormalize=renorm)
+        if k > 8:
+            continue
+        idx, gate = moe.route_from_logits(cfg, lg.cuda())
+        torch.cuda.synchronize()
+        # row 3 has |l| = 1e30: exp underflows to exactly 0 for the far experts
+        check_route(cfg, lg, idx.cpu(), gate.cpu())
+
+
+def test_deterministic_reruns():
+    cfg = configs.get("tiny").scaled(T=5000, d=256, E=12, k=2, d_ff=384, cap_num=5, cap_den=4,
+                                     renormalize=True, dtype="bf16", temperature=0.3)
+    dev, _ = gpu_inputs(cfg, seed=5)
+    f = moe.Forward(cfg)
+    a = f(dev["x"], dev["w_router"], None, dev["w_gate"], dev["w_up"], dev["w_down"]).clone()
+    b = f(dev["x"], dev["w_router"], None, dev["w_gate"], dev["w_up"], dev["w_down"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", [c.name for c in configs.CONFIGS])
+def test_full_size_layer(name):
+    cfg = configs.get(name)
+    dev, host = gpu_inputs(cfg, seed=0)
+    out = run_layer(cfg, dev, host, full=(name == "tiny"), seed=0, label=name)
+    if name == "skewed":
+        cnt = out["dsp"]["expert_count"].cpu().numpy()
+        say(f"[skewed] top expert share of assignments {cnt[0] / cnt.sum():.3f}, "
+            f"rows kept {out['n']} of {cfg.T * cfg.k}")
