@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (5 times) and exit: the "
+                         "known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -56,6 +59,22 @@ def algorithmic(cfg, counts, n_kept):
         "down_bytes": ne * F * d * b + n_kept * F * b + n_kept * d * b,
         "combine_bytes": n_kept * d * b + T * d * b + T * k * 8,
     }
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch of the gate/up GEMM from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs (scaled by a plain copy of known size), or None when
+    they were taken on another workload or the GEMM source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_gate_up_{cfg.name}.json")
+    if not os.path.exists(path):
+        return None, None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "mixture_experts_layer_15_amd", "csrc", "gemm_mfma.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("gemm_source_sha256_16") != sha:
+        return None, None
+    return rec["traffic_bytes_per_launch"], rec["kernel"]
 
 
 def cpu_baseline(cfg, host, logits_gpu, target_s):
@@ -109,6 +128,16 @@ def main():
 
     import mixture_experts_layer_15_amd as moe
     from mixture_experts_layer_15_amd import configs, synthetic
+
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
 
     cfg = configs.get(args.config)
     torch.cuda.set_device(0)
@@ -206,6 +235,8 @@ def main():
     def gbs(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
 
+    traffic, traffic_kernel = measured_traffic(cfg)
+
     out = {
         "metric": METRIC,
         "value": round(cfg.T / (ms_step * 1e-3), 1),
@@ -235,10 +266,13 @@ def main():
                            "combine": round(gbs(a["combine_bytes"], stage_ms["combine"]) / PEAK_HBM_GBS, 4)},
         "gpu_ms_per_step_events": round(gpu_ms, 4),
         "fused_forward_ms_per_step": round(fused_ms, 4),
-        "roofline": {"kernel": "grouped_gemm_bf16_kernel<gate/up>" if cfg.dtype == "bf16"
-                     else "grouped_gemm_f32_kernel<gate/up>",
+        "roofline": {"kernel": traffic_kernel or ("gemm_mfma_kernel<true, ...> (gate/up + GeGLU)"
+                                                  if cfg.dtype == "bf16" else
+                                                  "grouped_gemm_f32_kernel<true> (gate/up + GeGLU)"),
                      "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": round(gu_tflops, 1), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(gu_tflops / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(gu_tflops / peak, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes_per_launch": a["gate_up_bytes"],
                      "flops_per_launch": a["gate_up_flops"],
                      "avg_launch_ms": round(stage_ms["gate_up"], 4)},
     }

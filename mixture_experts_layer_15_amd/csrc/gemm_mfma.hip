@@ -1,0 +1,377 @@
+// gemm_mfma.hip -- bf16 grouped expert GEMMs on gfx950 MFMA.
+//
+//   gate/up:  h = GELU_erf(X_e W_gate[e]) * (X_e W_up[e])   (GeGLU applied to
+//             the accumulators in registers; only h is written -- the fusion of
+//             GeGLU into the matmul that "AMD GPU深度学习优化与ZAYA1大模型实践"
+//             section 3.2 describes for its expert MLP)
+//   down:     O = h_e W_down[e]
+//
+// Workgroup: 4 waves as 2 (M) x 2 (N).  A wave owns MI x NJ tiles of 16 x 16
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulators in registers), so the
+// workgroup tile is (32 MI) rows x (32 NJ) B-columns.  For gate/up the
+// B-columns are half W_gate and half the same W_up columns, and a wave's gate
+// tile j and up tile j + NJ/2 cover the same h columns: GeGLU is elementwise
+// on matching registers.
+//
+// Data path per K-step of 64: global_load_lds (16 bytes per lane, straight
+// into LDS, no VGPR round trip) fills one of two LDS stages while the other is
+// consumed; each wave issues whole 1 KB rows-blocks, choosing per lane the
+// global 16-byte chunk that belongs at LDS position base + 16 * lane, which
+// applies an XOR swizzle that spreads the fragment reads over the LDS banks.
+// A fragments: ds_read_b128 (row-major rows, K contiguous).  B fragments:
+// ds_read_b64_tr_b16 on the weight tile kept in its [K][N] layout (each
+// 16-lane group reads a 4 x 16 block; lane n receives column n).
+// Rows past the expert's last row are clamped on load and their MFMAs are
+// skipped per 16-row subtile.  The epilogue stages the tile through LDS and
+// writes whole 16-byte row pieces.
+#include "common.h"
+#include "kernels.h"
+#include "tiles.h"
+
+#include <type_traits>
+
+namespace moe {
+namespace {
+
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr int GM = 4;   // M-tiles per group in the tile order (tiles.h)
+
+// LDS swizzles.  An A row holds BK bf16 = BK/8 chunks of 16 bytes; chunk c of
+// row r sits in slot c ^ fa(r), fa spreading the 16 rows a fragment read
+// touches over distinct banks.  B rows hold 16-byte chunks too; chunk c of
+// row r sits in slot c ^ 2 h(r), h(r) = (r & 3) | ((r >> 3) & 1) << 2: the
+// even mask keeps each aligned pair of chunks (the 32 bytes one transposing
+// read takes from a row) together.  XOR is an involution, so the same map
+// gives slot -> chunk when filling and chunk -> slot when reading.
+template <int BKT>
+__device__ __forceinline__ int fa(int r) {
+    return BKT == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+// Pair swizzle h(r) of a B row holding CPR chunks (CPR/2 pairs).
+template <int CPR>
+__device__ __forceinline__ int hb(int r) {
+    return ((r & 3) | (((r >> 3) & 1) << 2)) & (CPR / 2 - 1);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
+// lane (global_load_lds_dwordx4; M0 holds the wave-uniform LDS address, and
+// one wait state must separate the M0 write from the load).  Issued through
+// inline asm so that the compiler's wait-count tracking does not treat later
+// LDS reads of other stage buffers as dependent on it: the K-loop's explicit
+// vmcnt waits order every fill before the reads of its stage.
+__device__ __forceinline__ void load_to_lds(const void* gptr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_base), "v"(gptr) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_void_t*)p;
+}
+
+template <bool GATEUP, int MI, int NJ, int BKT, int NST>
+struct Shape {
+    static constexpr int BM = 32 * MI;              // rows per tile
+    static constexpr int BN = 32 * NJ;              // B-columns per tile
+    static constexpr int KS = BKT / 32;             // 32-deep MFMA steps per stage
+    static constexpr int A_ROWB = BKT * 2;          // bytes per A row
+    static constexpr int ACH = BKT / 8;             // 16-byte chunks per A row
+    static constexpr int A_RPK = 1024 / A_ROWB;     // A rows per 1 KB wave-load
+    static constexpr int NB = GATEUP ? 2 : 1;       // B sub-tiles (W_gate, W_up)
+    static constexpr int BNS = BN / NB;             // columns per sub-tile
+    static constexpr int RB = BNS * 2;              // bytes per sub-tile row
+    static constexpr int SUB = BKT * RB;            // bytes per sub-tile
+    static constexpr int A_BYTES = BM * A_ROWB;
+    static constexpr int B_BYTES = NB * SUB;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 4096;  // 1 KB wave-loads per wave
+    static constexpr int B_LOADS = B_BYTES / 4096;
+    static constexpr int LOADS = A_LOADS + B_LOADS; // per wave per stage
+    static constexpr int SUB_LOADS = SUB / 1024;    // wave-loads per sub-tile
+    static constexpr int CPR = RB / 16;             // 16-byte chunks per sub-tile row
+    static constexpr int RPK = 1024 / RB;           // sub-tile rows per 1 KB
+    static constexpr int OUTC = GATEUP ? BN / 2 : BN;       // output columns per tile
+    static constexpr int OUTW = OUTC / 2;                   // output columns per wave
+    static constexpr int LDC = OUTC + 8;                    // epilogue LDS row stride (elements)
+    // epilogue passes per wave-row: the fewest (a power of two) whose rows fit
+    // one stage buffer
+    static constexpr int PPW = ((MI * 16 / 2) * LDC * 2 <= STAGE) ? 2
+                             : ((MI * 16 / 4) * LDC * 2 <= STAGE) ? 4 : 8;
+    static constexpr int HR = MI * 16 / PPW;                 // rows per epilogue pass
+    static_assert(BKT == 32 || BKT == 64, "K-step");
+    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole wave-loads");
+    static_assert(SUB_LOADS % B_LOADS == 0 || B_LOADS % SUB_LOADS == 0, "uniform sources");
+    static_assert(HR * LDC * 2 <= STAGE && MI % PPW == 0, "epilogue staging fits in one stage");
+    static_assert(CPR <= 32 && CPR >= 8, "swizzle stays inside a row");
+    static_assert(NST >= 2 && NST <= 4, "stages");
+};
+
+// Per-lane constants of the fragment reads.
+struct FragLane {
+    int a_rd, a_sw, g4, b_rd;
+};
+
+// One stage: KS steps of 32 in K.  B fragments through transposing reads, A
+// fragments prefetched one subtile ahead, MFMAs of the wave's valid 16-row
+// subtiles (FULL: all MI, no branches).
+template <int MI, int NJ, int KS, int A_ROWB, int RB, bool FULL>
+__device__ __forceinline__ void mfma_stage(const char* __restrict__ sb, f32x4 (&acc)[MI][NJ],
+                                           int nvm, const FragLane& fl,
+                                           const int (&b_sub)[NJ], const int (&b_pair)[NJ]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 bfr[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const char* p = sb + b_sub[j] + ks * 32 * RB + fl.b_rd + b_pair[j];
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * RB));
+            bfr[j] = __builtin_bit_cast(
+                bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        const int a_ch = ((ks * 4 + fl.g4) ^ fl.a_sw) << 4;
+        bf16x8 a_cur = *(const bf16x8*)(sb + fl.a_rd + a_ch);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int in = (i + 1 < MI) ? i + 1 : i;
+            const bf16x8 a_nxt = *(const bf16x8*)(sb + fl.a_rd + in * 16 * A_ROWB + a_ch);
+            if (FULL || i < nvm) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_cur, bfr[j], acc[i][j],
+                                                                        0, 0, 0);
+            }
+            a_cur = a_nxt;
+        }
+    }
+}
+
+// Wait until at most `later` of this wave's stages issued after the one to be
+// read are still in flight, and for this wave's LDS reads, then barrier: every
+// wave's part of the stage has landed, and every wave is done reading the
+// buffer about to be refilled.  A bare s_barrier: __syncthreads() adds a
+// workgroup release fence, which waits for every outstanding vector memory
+// operation -- including the later stages' prefetches.
+template <int LOADS>
+__device__ __forceinline__ void stage_sync(int later) {
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LOADS) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool GATEUP, int MI, int NJ, int BKT, int NST>
+__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
+    const int32_t* __restrict__ off, int E, int K, int N) {
+    using S = Shape<GATEUP, MI, NJ, BKT, NST>;
+    // distinct stage buffers, so that the compiler can tell the reads of one
+    // stage from the asynchronous fills of the others
+    __shared__ __attribute__((aligned(1024))) char st0[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) char st1[S::STAGE];
+    __shared__ __attribute__((aligned(1024))) char st2[NST > 2 ? S::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char st3[NST > 3 ? S::STAGE : 16];
+    __shared__ TileTable tt;
+    __shared__ long long s_wave[4];
+
+    const int ntn = (N + S::OUTC - 1) / S::OUTC;
+    build_tile_table<S::BM>(off, E, ntn, tt, s_wave);
+    const long long total = tt.start[E];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int c16 = lane & 15, g4 = lane >> 4;
+    const int G = gridDim.x;
+    const int nk = K / BKT;
+
+    // Per-lane LDS read offsets: the rows a lane reads differ only in
+    // multiples of 16 (A) or 4 (B), so the swizzles are lane constants.
+    FragLane fl;
+    fl.a_rd = (wm * MI * 16 + c16) * S::A_ROWB;
+    fl.a_sw = fa<BKT>(c16);
+    fl.g4 = g4;
+    const int hl = ((c16 >> 2) | ((g4 & 1) << 2)) & (S::CPR / 2 - 1);
+    fl.b_rd = (g4 * 8 + (c16 >> 2)) * S::RB + ((c16 >> 1) & 1) * 16 + (c16 & 1) * 8;
+    int b_sub[NJ], b_pair[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        int sub, colS;
+        if (GATEUP) {
+            sub = (j < NJ / 2) ? 0 : 1;
+            colS = wn * (S::BNS / 2) + (j % (NJ / 2)) * 16;
+        } else {
+            sub = 0;
+            colS = wn * (S::BN / 2) + j * 16;
+        }
+        b_sub[j] = S::A_BYTES + sub * S::SUB;
+        b_pair[j] = ((colS >> 4) ^ hl) * 32;
+    }
+
+    for (long long base = 0; base < total; base += G) {
+        const long long t = base + xcd_slot(blockIdx.x, G);
+        if (t >= total) continue;   // uniform across the workgroup
+        int e, mtile, ntile;
+        decode_tile<GM>(tt, E, ntn, t, e, mtile, ntile);
+        const int row0 = off[e] + mtile * S::BM;
+        const int rows = min(S::BM, off[e + 1] - row0);
+        const int n0 = ntile * S::OUTC;
+        const int nvm = __builtin_amdgcn_readfirstlane(
+            max(0, min(MI, (rows - wm * MI * 16 + 15) >> 4)));
+
+        // uniform tile bases, per-lane 32-bit element offsets of each wave-load
+        const uint16_t* a_base = A + (long long)row0 * K;
+        const long long wofs = (long long)e * K * N + n0;
+        int a_off[S::A_LOADS];
+#pragma unroll
+        for (int q = 0; q < S::A_LOADS; ++q) {
+            const int r = (w * S::A_LOADS + q) * S::A_RPK + lane / S::ACH;
+            const int c = (lane % S::ACH) ^ fa<BKT>(r);
+            a_off[q] = min(r, rows - 1) * K + c * 8;
+        }
+        int b_off[S::B_LOADS];
+#pragma unroll
+        for (int q = 0; q < S::B_LOADS; ++q) {
+            const int ql = (w * S::B_LOADS + q) % S::SUB_LOADS;   // wave-load within its sub-tile
+            const int r = ql * S::RPK + lane / S::CPR;
+            const int c = (lane % S::CPR) ^ (hb<S::CPR>(r) << 1);
+            const int col = min(n0 + c * 8, N - 8) - n0;
+            b_off[q] = r * N + col;
+        }
+
+        auto issue = [&](int kt, char* sb) {
+            const int ka = kt * BKT;
+            const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(sb));
+#pragma unroll
+            for (int q = 0; q < S::A_LOADS; ++q)
+                load_to_lds(a_base + (a_off[q] + ka), lb + (w * S::A_LOADS + q) * 1024);
+            const int kb = ka * N;
+#pragma unroll
+            for (int q = 0; q < S::B_LOADS; ++q) {
+                const int gl = w * S::B_LOADS + q;                 // wave-load index in the stage
+                const uint16_t* src = (GATEUP && gl >= S::SUB_LOADS) ? B1 : B0;
+                load_to_lds(src + wofs + (b_off[q] + kb), lb + S::A_BYTES + gl * 1024);
+            }
+        };
+
+        f32x4 acc[MI][NJ];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        __syncthreads();   // the previous tile's epilogue is done with the stages
+        // prologue: stages 0 .. NST-2
+        issue(0, st0);
+        if (NST > 2 && 1 < nk) issue(1, st1);
+        if (NST > 3 && 2 < nk) issue(2, st2);
+
+        // one step: wait for stage kt (buffer `cur`), refill the buffer read
+        // one step ago with stage kt + NST - 1, run the MFMAs on `cur`
+        auto k_loop = [&](auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            char* bufs[4] = {st0, st1, st2, st3};
+            for (int kt = 0; kt < nk; kt += NST) {
+#pragma unroll
+                for (int s = 0; s < NST; ++s) {
+                    const int k = kt + s;
+                    if (k >= nk) break;
+                    stage_sync<S::LOADS>(min(nk - 1 - k, NST - 2));
+                    if (k + NST - 1 < nk) issue(k + NST - 1, bufs[(s + NST - 1) % NST]);
+                    mfma_stage<MI, NJ, S::KS, S::A_ROWB, S::RB, FULL>(bufs[s], acc, nvm, fl,
+                                                                      b_sub, b_pair);
+                }
+            }
+        };
+        if (nvm == MI) k_loop(std::true_type{});
+        else k_loop(std::false_type{});
+        __syncthreads();   // every wave is done reading the stages
+
+        // epilogue: 2 * PPW passes of HR rows each through LDS
+        uint16_t* cs = (uint16_t*)st0;
+        constexpr int VPR = S::OUTC / 8;          // 16-byte pieces per output row
+        constexpr int HR = S::HR;
+        constexpr int SPP = MI / S::PPW;          // 16-row subtiles per pass
+#pragma unroll
+        for (int p = 0; p < 2 * S::PPW; ++p) {
+            if (wm == p / S::PPW) {
+#pragma unroll
+                for (int ii = 0; ii < SPP; ++ii) {
+                    const int i = (p % S::PPW) * SPP + ii;
+#pragma unroll
+                    for (int jj = 0; jj < S::OUTW / 16; ++jj) {
+                        const int col = wn * S::OUTW + jj * 16 + c16;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int rt = ii * 16 + g4 * 4 + r;
+                            float v;
+                            if (GATEUP) v = gelu_erf(acc[i][jj][r]) * acc[i][jj + NJ / 2][r];
+                            else v = acc[i][jj][r];
+                            cs[rt * S::LDC + col] = (uint16_t)f32_to_bf16_bits(v);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            for (int ch = tid; ch < HR * VPR; ch += 256) {
+                const int rt = ch / VPR, c8 = ch % VPR;
+                const int grow = p * HR + rt;
+                const int gcol = n0 + c8 * 8;
+                if (grow < rows && gcol < N)
+                    *(u32x4*)(C + (long long)(row0 + grow) * N + gcol) =
+                        *(const u32x4*)(cs + rt * S::LDC + c8 * 8);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <bool GATEUP, int MI, int NJ, int BKT, int NST>
+hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
+                        const int32_t* off, int E, int K, int N, long long max_rows, int cus,
+                        hipStream_t s) {
+    using S = Shape<GATEUP, MI, NJ, BKT, NST>;
+    const long long mt = (max_rows + S::BM - 1) / S::BM + E;   // >= sum_e ceil(rows_e / BM)
+    const long long tiles = mt * ((N + S::OUTC - 1) / S::OUTC);
+    long long g = std::min<long long>(cus, (tiles + 7) / 8 * 8);
+    g = std::max<long long>(8, g / 8 * 8);
+    hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NST>), dim3((unsigned)g), dim3(256),
+                       0, s, A, B0, B1, C, off, E, K, N);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile shape policy.  Rows per expert are only known on the device; the host
+// knows their mean (max_rows / E, exact when nothing is dropped).  Layers
+// whose experts hold up to ~320 rows (weight-streaming bound: every weight
+// byte is used by that few rows) take 320-row tiles so that one M-tile covers
+// an expert and each weight tile is streamed once; larger experts take
+// 256 x 256 tiles (the most flops per byte moved into a CU).
+static bool small_experts(long long max_rows, int E) { return max_rows <= 320LL * E; }
+
+hipError_t launch_mfma_gate_up(const uint16_t* x_perm, const int32_t* off, const uint16_t* w_gate,
+                               const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
+                               long long max_rows, int cus, hipStream_t s) {
+    if (small_experts(max_rows, E))
+        return launch_shape<true, 10, 4, 64, 2>(x_perm, w_gate, w_up, h, off, E, d, d_ff,
+                                                max_rows, cus, s);
+    return launch_shape<true, 8, 8, 32, 4>(x_perm, w_gate, w_up, h, off, E, d, d_ff, max_rows,
+                                           cus, s);
+}
+
+hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_t* w_down,
+                            uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
+                            int cus, hipStream_t s) {
+    if (small_experts(max_rows, E))
+        return launch_shape<false, 10, 4, 64, 2>(h, w_down, nullptr, y_perm, off, E, d_ff, d,
+                                                 max_rows, cus, s);
+    return launch_shape<false, 8, 8, 64, 2>(h, w_down, nullptr, y_perm, off, E, d_ff, d,
+                                            max_rows, cus, s);
+}
+
+}  // namespace moe

@@ -47,6 +47,14 @@ hipError_t launch_down(int dtype, const void* h, const int32_t* off, const void*
                        void* y_perm, int E, int d, int d_ff, long long max_rows, int grid_cap,
                        hipStream_t s);
 
+// bf16 MFMA kernels (gemm_mfma.hip); cus = workgroups of the persistent grid.
+hipError_t launch_mfma_gate_up(const uint16_t* x_perm, const int32_t* off, const uint16_t* w_gate,
+                               const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
+                               long long max_rows, int cus, hipStream_t s);
+hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_t* w_down,
+                            uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
+                            int cus, hipStream_t s);
+
 // Gate-weighted combine.
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
                           const float* gate, void* y, long long T, int d, int k,

@@ -1,0 +1,80 @@
+// tiles.h -- the grouped GEMMs' tile list, built on the device from
+// expert_offset (the number of kept rows per expert never leaves the GPU).
+//
+// Tiles are numbered expert-major, then N-tile, then M-tile (M fastest), so
+// the M-tiles that share one weight tile are adjacent, and consecutive
+// N-tiles of one expert reuse that expert's rows.  A persistent grid walks
+// the list in sweeps of gridDim.x tiles; within a sweep workgroup b takes
+// slot xcd_slot(b), which hands each XCD (workgroups b, b+8, ... run on XCD
+// b % 8) a contiguous run of tile ids, so tiles that share data meet in the
+// same L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct TileTable {
+    long long start[257];   // tiles before expert e; start[E] = total
+    int mtiles[256];        // M-tiles of expert e
+};
+
+// All 256 threads of the block call this.  ntn = N-tiles per expert.
+template <int TBM>
+__device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ off, int E, int ntn,
+                                                 TileTable& tt, long long* s_wave) {
+    const int e = threadIdx.x;
+    long long cnt = 0;
+    int mt = 0;
+    if (e < E) {
+        const int kept = off[e + 1] - off[e];
+        mt = (kept + TBM - 1) / TBM;
+        cnt = (long long)mt * ntn;
+    }
+    tt.mtiles[e] = mt;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    long long v = cnt;
+    for (int o = 1; o < 64; o <<= 1) {
+        const long long u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) s_wave[w] = v;
+    __syncthreads();
+    long long add = 0;
+    for (int i = 0; i < w; ++i) add += s_wave[i];
+    tt.start[e + 1] = v + add;
+    if (e == 0) tt.start[0] = 0;
+    __syncthreads();
+}
+
+// Tile id -> (expert, m-tile, n-tile): the largest e with start[e] <= t (an
+// expert with no tiles has start[e] == start[e+1] and is never chosen).
+// Inside an expert the M-tiles go in groups of GM: for each group, every
+// N-tile, M fastest.  Experts with at most GM M-tiles get the plain order
+// (N-tile, then M); larger ones get GM x N blocks, so a run of consecutive
+// tiles on one XCD shares both its activation rows and its weight columns.
+template <int GM>
+__device__ __forceinline__ void decode_tile(const TileTable& tt, int E, int ntn, long long t,
+                                            int& e, int& m, int& n) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tt.start[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    const long long local = t - tt.start[e];
+    const int mt = tt.mtiles[e];
+    const int g = (int)(local / ((long long)GM * ntn));
+    const int gs = min(GM, mt - g * GM);
+    const int r = (int)(local - (long long)g * GM * ntn);
+    n = r / gs;
+    m = g * GM + r % gs;
+}
+
+// Slot of workgroup b in a sweep of G (G a multiple of 8).
+__device__ __forceinline__ long long xcd_slot(int b, int G) {
+    return (long long)(b & 7) * (G >> 3) + (b >> 3);
+}
+
+}  // namespace moe
