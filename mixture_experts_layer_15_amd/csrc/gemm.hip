@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     __shared__ float Bg[FBK][FBN + 4];
     __shared__ float Bu[FBK][FBN + 4];
     __shared__ TileTable tt;
-    __shared__ long long s_wave[4];
+    __shared__ long long s_wave[8];
     const int ntn = (N + FBN - 1) / FBN;
     build_tile_table<FBM>(off, E, ntn, tt, s_wave);
     const long long total = tt.start[E];

@@ -6,9 +6,11 @@
 //             section 3.2 describes for its expert MLP)
 //   down:     O = h_e W_down[e]
 //
-// Workgroup: 4 waves as 2 (M) x 2 (N).  A wave owns MI x NJ tiles of 16 x 16
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulators in registers), so the
-// workgroup tile is (32 MI) rows x (32 NJ) B-columns.  For gate/up the
+// Workgroup: 8 waves as 2 (M) x 4 (N), two per SIMD, so that one wave's LDS
+// reads, barrier waits and MFMA issue gaps are covered by the other's MFMAs.
+// A wave owns MI x NJ tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16, fp32
+// accumulators in registers), so the workgroup tile is (32 MI) rows x (64 NJ)
+// B-columns.  For gate/up the
 // B-columns are half W_gate and half the same W_up columns, and a wave's gate
 // tile j and up tile j + NJ/2 cover the same h columns: GeGLU is elementwise
 // on matching registers.
@@ -42,18 +44,27 @@ constexpr int GM = 4;   // M-tiles per group in the tile order (tiles.h)
 // LDS swizzles.  An A row holds BK bf16 = BK/8 chunks of 16 bytes; chunk c of
 // row r sits in slot c ^ fa(r), fa spreading the 16 rows a fragment read
 // touches over distinct banks.  B rows hold 16-byte chunks too; chunk c of
-// row r sits in slot c ^ 2 h(r), h(r) = (r & 3) | ((r >> 3) & 1) << 2: the
-// even mask keeps each aligned pair of chunks (the 32 bytes one transposing
-// read takes from a row) together.  XOR is an involution, so the same map
-// gives slot -> chunk when filling and chunk -> slot when reading.
+// row r sits in slot c ^ 2 h(r) (below): the even mask keeps each aligned
+// pair of chunks (the 32 bytes one transposing read takes from a row)
+// together.  XOR is an involution, so the same map gives slot -> chunk when
+// filling and chunk -> slot when reading.
 template <int BKT>
 __device__ __forceinline__ int fa(int r) {
     return BKT == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
-// Pair swizzle h(r) of a B row holding CPR chunks (CPR/2 pairs).
+// Pair swizzle h(r) of a B row holding CPR chunks (CPR/2 pairs of 32 bytes).
+// One transposing read covers 16 rows, {0..3, 8..11, 16..19, 24..27} + base
+// (four 16-lane groups), 32 bytes each; the LDS serves 256 bytes (eight
+// 32-byte units) per pass, two groups at a time.  Rows of 256 or 512 bytes
+// all start on the same bank, so the 8 rows of a pass need 8 distinct pair
+// slots: h = (r & 3) | (r >> 3 & 1) << 2.  Rows of 128 bytes alternate
+// between the two halves of the banks, so the 4 rows on each half need 4
+// distinct slots: h = (r >> 1 & 1) | (r >> 3 & 1) << 1.  The fragment rows of
+// one lane differ only in bits 2 and 5+ of r, so h is a lane constant.
 template <int CPR>
 __device__ __forceinline__ int hb(int r) {
-    return ((r & 3) | (((r >> 3) & 1) << 2)) & (CPR / 2 - 1);
+    if (CPR == 8) return ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
+    return (r & 3) | (((r >> 3) & 1) << 2);
 }
 
 // 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
@@ -71,41 +82,50 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(lds_void_t*)p;
 }
 
-template <bool GATEUP, int MI, int NJ, int BKT, int NST>
+template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB>
 struct Shape {
+    static constexpr int WAVES = 8;                 // 2 (M) x 4 (N)
+    static constexpr int THREADS = 64 * WAVES;
     static constexpr int BM = 32 * MI;              // rows per tile
-    static constexpr int BN = 32 * NJ;              // B-columns per tile
+    static constexpr int BN = 64 * NJ;              // B-columns per tile
     static constexpr int KS = BKT / 32;             // 32-deep MFMA steps per stage
     static constexpr int A_ROWB = BKT * 2;          // bytes per A row
     static constexpr int ACH = BKT / 8;             // 16-byte chunks per A row
     static constexpr int A_RPK = 1024 / A_ROWB;     // A rows per 1 KB wave-load
-    static constexpr int NB = GATEUP ? 2 : 1;       // B sub-tiles (W_gate, W_up)
-    static constexpr int BNS = BN / NB;             // columns per sub-tile
+    static constexpr int NSUB = GATEUP ? 2 : 1;     // B sub-tiles (W_gate, W_up)
+    static constexpr int BNS = BN / NSUB;           // columns per sub-tile
     static constexpr int RB = BNS * 2;              // bytes per sub-tile row
     static constexpr int SUB = BKT * RB;            // bytes per sub-tile
-    static constexpr int A_BYTES = BM * A_ROWB;
-    static constexpr int B_BYTES = NB * SUB;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 4096;  // 1 KB wave-loads per wave
-    static constexpr int B_LOADS = B_BYTES / 4096;
-    static constexpr int LOADS = A_LOADS + B_LOADS; // per wave per stage
+    static constexpr int A_BYTES = BM * A_ROWB;     // one A stage
+    static constexpr int B_BYTES = NSUB * SUB;      // one B stage
+    // waves 0-3 fill the A stages, waves 4-7 the B stages (1 KB wave-loads)
+    static constexpr int A_LOADS = A_BYTES / 4096;  // per A-loading wave per stage
+    static constexpr int B_LOADS = B_BYTES / 4096;  // per B-loading wave per stage
     static constexpr int SUB_LOADS = SUB / 1024;    // wave-loads per sub-tile
     static constexpr int CPR = RB / 16;             // 16-byte chunks per sub-tile row
     static constexpr int RPK = 1024 / RB;           // sub-tile rows per 1 KB
     static constexpr int OUTC = GATEUP ? BN / 2 : BN;       // output columns per tile
-    static constexpr int OUTW = OUTC / 2;                   // output columns per wave
+    static constexpr int OUTW = OUTC / 4;                   // output columns per wave
     static constexpr int LDC = OUTC + 8;                    // epilogue LDS row stride (elements)
-    // epilogue passes per wave-row: the fewest (a power of two) whose rows fit
-    // one stage buffer
-    static constexpr int PPW = ((MI * 16 / 2) * LDC * 2 <= STAGE) ? 2
-                             : ((MI * 16 / 4) * LDC * 2 <= STAGE) ? 4 : 8;
+    // epilogue passes per wave-row: the fewest (a divisor of MI) whose rows fit
+    // one A stage buffer
+    static constexpr int ppw() {
+        for (int p = 1; p <= MI; ++p)
+            if (MI % p == 0 && (MI * 16 / p) * LDC * 2 <= A_BYTES) return p;
+        return MI;
+    }
+    static constexpr int PPW = ppw();
     static constexpr int HR = MI * 16 / PPW;                 // rows per epilogue pass
+    static constexpr int U = NA > NB ? NA : NB;              // K-loop unroll (static buffers)
     static_assert(BKT == 32 || BKT == 64, "K-step");
-    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole wave-loads");
+    static_assert(!GATEUP || NJ % 2 == 0, "gate and up halves");
+    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole wave-loads per loader");
     static_assert(SUB_LOADS % B_LOADS == 0 || B_LOADS % SUB_LOADS == 0, "uniform sources");
-    static_assert(HR * LDC * 2 <= STAGE && MI % PPW == 0, "epilogue staging fits in one stage");
+    static_assert(HR * LDC * 2 <= A_BYTES && MI % PPW == 0, "epilogue staging fits an A stage");
     static_assert(CPR <= 32 && CPR >= 8, "swizzle stays inside a row");
-    static_assert(NST >= 2 && NST <= 4, "stages");
+    static_assert(NA >= 2 && NA <= 4 && NB >= 2 && NB <= 4 && U % NA == 0 && U % NB == 0,
+                  "stage counts");
+    static_assert(NA * A_BYTES + NB * B_BYTES + 4096 <= 160 * 1024, "LDS budget");
 };
 
 // Per-lane constants of the fragment reads.
@@ -117,26 +137,27 @@ struct FragLane {
 // fragments prefetched one subtile ahead, MFMAs of the wave's valid 16-row
 // subtiles (FULL: all MI, no branches).
 template <int MI, int NJ, int KS, int A_ROWB, int RB, bool FULL>
-__device__ __forceinline__ void mfma_stage(const char* __restrict__ sb, f32x4 (&acc)[MI][NJ],
-                                           int nvm, const FragLane& fl,
+__device__ __forceinline__ void mfma_stage(const char* __restrict__ sa,
+                                           const char* __restrict__ sbb,
+                                           f32x4 (&acc)[MI][NJ], int nvm, const FragLane& fl,
                                            const int (&b_sub)[NJ], const int (&b_pair)[NJ]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         bf16x8 bfr[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const char* p = sb + b_sub[j] + ks * 32 * RB + fl.b_rd + b_pair[j];
+            const char* p = sbb + b_sub[j] + ks * 32 * RB + fl.b_rd + b_pair[j];
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * RB));
             bfr[j] = __builtin_bit_cast(
                 bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
         const int a_ch = ((ks * 4 + fl.g4) ^ fl.a_sw) << 4;
-        bf16x8 a_cur = *(const bf16x8*)(sb + fl.a_rd + a_ch);
+        bf16x8 a_cur = *(const bf16x8*)(sa + fl.a_rd + a_ch);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int in = (i + 1 < MI) ? i + 1 : i;
-            const bf16x8 a_nxt = *(const bf16x8*)(sb + fl.a_rd + in * 16 * A_ROWB + a_ch);
+            const bf16x8 a_nxt = *(const bf16x8*)(sa + fl.a_rd + in * 16 * A_ROWB + a_ch);
             if (FULL || i < nvm) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
@@ -149,11 +170,12 @@ __device__ __forceinline__ void mfma_stage(const char* __restrict__ sb, f32x4 (&
 }
 
 // Wait until at most `later` of this wave's stages issued after the one to be
-// read are still in flight, and for this wave's LDS reads, then barrier: every
-// wave's part of the stage has landed, and every wave is done reading the
-// buffer about to be refilled.  A bare s_barrier: __syncthreads() adds a
-// workgroup release fence, which waits for every outstanding vector memory
-// operation -- including the later stages' prefetches.
+// read are still in flight (each stage is LOADS of this wave's wave-loads),
+// and for this wave's LDS reads, then barrier: every wave's part of the stage
+// has landed, and every wave is done reading the buffers about to be
+// refilled.  A bare s_barrier: __syncthreads() adds a workgroup release
+// fence, which waits for every outstanding vector memory operation --
+// including the later stages' prefetches.
 template <int LOADS>
 __device__ __forceinline__ void stage_sync(int later) {
     if (later >= 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LOADS) : "memory");
@@ -163,20 +185,24 @@ __device__ __forceinline__ void stage_sync(int later) {
     asm volatile("" ::: "memory");
 }
 
-template <bool GATEUP, int MI, int NJ, int BKT, int NST>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
+template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB>
+__global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
     const int32_t* __restrict__ off, int E, int K, int N) {
-    using S = Shape<GATEUP, MI, NJ, BKT, NST>;
-    // distinct stage buffers, so that the compiler can tell the reads of one
-    // stage from the asynchronous fills of the others
-    __shared__ __attribute__((aligned(1024))) char st0[S::STAGE];
-    __shared__ __attribute__((aligned(1024))) char st1[S::STAGE];
-    __shared__ __attribute__((aligned(1024))) char st2[NST > 2 ? S::STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) char st3[NST > 3 ? S::STAGE : 16];
+    using S = Shape<GATEUP, MI, NJ, BKT, NA, NB>;
+    // one distinct __shared__ array per stage buffer, so that the compiler can
+    // tell the reads of one stage from the fills of the others
+    __shared__ __attribute__((aligned(1024))) char sa0[S::A_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sa1[S::A_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sa2[NA > 2 ? S::A_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sa3[NA > 3 ? S::A_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sb0[S::B_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sb1[S::B_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sb2[NB > 2 ? S::B_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sb3[NB > 3 ? S::B_BYTES : 16];
     __shared__ TileTable tt;
-    __shared__ long long s_wave[4];
+    __shared__ long long s_wave[S::WAVES];
 
     const int ntn = (N + S::OUTC - 1) / S::OUTC;
     build_tile_table<S::BM>(off, E, ntn, tt, s_wave);
@@ -184,7 +210,9 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w >> 2, wn = w & 3;
+    const bool a_loader = w < 4;            // waves 0-3 fill A stages, 4-7 fill B stages
+    const int lw = w & 3;                   // index among the loaders of its operand
     const int c16 = lane & 15, g4 = lane >> 4;
     const int G = gridDim.x;
     const int nk = K / BKT;
@@ -195,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
     fl.a_rd = (wm * MI * 16 + c16) * S::A_ROWB;
     fl.a_sw = fa<BKT>(c16);
     fl.g4 = g4;
-    const int hl = ((c16 >> 2) | ((g4 & 1) << 2)) & (S::CPR / 2 - 1);
+    const int hl = hb<S::CPR>(g4 * 8 + (c16 >> 2));   // = h of every B row this lane reads
     fl.b_rd = (g4 * 8 + (c16 >> 2)) * S::RB + ((c16 >> 1) & 1) * 16 + (c16 & 1) * 8;
     int b_sub[NJ], b_pair[NJ];
 #pragma unroll
@@ -203,12 +231,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
         int sub, colS;
         if (GATEUP) {
             sub = (j < NJ / 2) ? 0 : 1;
-            colS = wn * (S::BNS / 2) + (j % (NJ / 2)) * 16;
+            colS = wn * (S::BNS / 4) + (j % (NJ / 2)) * 16;
         } else {
             sub = 0;
-            colS = wn * (S::BN / 2) + j * 16;
+            colS = wn * (S::BN / 4) + j * 16;
         }
-        b_sub[j] = S::A_BYTES + sub * S::SUB;
+        b_sub[j] = sub * S::SUB;
         b_pair[j] = ((colS >> 4) ^ hl) * 32;
     }
 
@@ -223,38 +251,42 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
         const int nvm = __builtin_amdgcn_readfirstlane(
             max(0, min(MI, (rows - wm * MI * 16 + 15) >> 4)));
 
-        // uniform tile bases, per-lane 32-bit element offsets of each wave-load
+        // uniform tile bases and this lane's 32-bit element offsets for each of
+        // its wave-loads (A loaders: A rows; B loaders: weight rows)
         const uint16_t* a_base = A + (long long)row0 * K;
         const long long wofs = (long long)e * K * N + n0;
-        int a_off[S::A_LOADS];
+        constexpr int NL = S::A_LOADS > S::B_LOADS ? S::A_LOADS : S::B_LOADS;
+        int l_off[NL];
 #pragma unroll
-        for (int q = 0; q < S::A_LOADS; ++q) {
-            const int r = (w * S::A_LOADS + q) * S::A_RPK + lane / S::ACH;
-            const int c = (lane % S::ACH) ^ fa<BKT>(r);
-            a_off[q] = min(r, rows - 1) * K + c * 8;
-        }
-        int b_off[S::B_LOADS];
-#pragma unroll
-        for (int q = 0; q < S::B_LOADS; ++q) {
-            const int ql = (w * S::B_LOADS + q) % S::SUB_LOADS;   // wave-load within its sub-tile
-            const int r = ql * S::RPK + lane / S::CPR;
-            const int c = (lane % S::CPR) ^ (hb<S::CPR>(r) << 1);
-            const int col = min(n0 + c * 8, N - 8) - n0;
-            b_off[q] = r * N + col;
+        for (int q = 0; q < NL; ++q) {
+            if (a_loader) {
+                const int r = (lw * S::A_LOADS + q) * S::A_RPK + lane / S::ACH;
+                const int c = (lane % S::ACH) ^ fa<BKT>(r);
+                l_off[q] = (q < S::A_LOADS) ? min(r, rows - 1) * K + c * 8 : 0;
+            } else {
+                const int gl = lw * S::B_LOADS + q;                 // wave-load index in the stage
+                const int r = (gl % S::SUB_LOADS) * S::RPK + lane / S::CPR;
+                const int c = (lane % S::CPR) ^ (hb<S::CPR>(r) << 1);
+                const int col = min(n0 + c * 8, N - 8) - n0;
+                l_off[q] = (q < S::B_LOADS) ? r * N + col : 0;
+            }
         }
 
-        auto issue = [&](int kt, char* sb) {
+        auto issue_a = [&](int kt, char* sa) {
             const int ka = kt * BKT;
-            const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(sb));
+            const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(sa));
 #pragma unroll
             for (int q = 0; q < S::A_LOADS; ++q)
-                load_to_lds(a_base + (a_off[q] + ka), lb + (w * S::A_LOADS + q) * 1024);
-            const int kb = ka * N;
+                load_to_lds(a_base + (l_off[q] + ka), lb + (lw * S::A_LOADS + q) * 1024);
+        };
+        auto issue_b = [&](int kt, char* sb) {
+            const int kb = kt * BKT * N;
+            const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(sb));
 #pragma unroll
             for (int q = 0; q < S::B_LOADS; ++q) {
-                const int gl = w * S::B_LOADS + q;                 // wave-load index in the stage
+                const int gl = lw * S::B_LOADS + q;
                 const uint16_t* src = (GATEUP && gl >= S::SUB_LOADS) ? B1 : B0;
-                load_to_lds(src + wofs + (b_off[q] + kb), lb + S::A_BYTES + gl * 1024);
+                load_to_lds(src + wofs + (l_off[q] + kb), lb + gl * 1024);
             }
         };
 
@@ -264,26 +296,38 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        __syncthreads();   // the previous tile's epilogue is done with the stages
-        // prologue: stages 0 .. NST-2
-        issue(0, st0);
-        if (NST > 2 && 1 < nk) issue(1, st1);
-        if (NST > 3 && 2 < nk) issue(2, st2);
+        char* abuf[4] = {sa0, sa1, sa2, sa3};
+        char* bbuf[4] = {sb0, sb1, sb2, sb3};
+        __syncthreads();   // the previous tile's epilogue is done with the buffers
+        // prologue: A stages 0 .. NA-2, B stages 0 .. NB-2
+        if (a_loader) {
+#pragma unroll
+            for (int q = 0; q + 1 < NA; ++q)
+                if (q < nk) issue_a(q, abuf[q]);
+        } else {
+#pragma unroll
+            for (int q = 0; q + 1 < NB; ++q)
+                if (q < nk) issue_b(q, bbuf[q]);
+        }
 
-        // one step: wait for stage kt (buffer `cur`), refill the buffer read
-        // one step ago with stage kt + NST - 1, run the MFMAs on `cur`
+        // step k: wait for A and B stage k, refill the buffers read at step k-1
+        // with A stage k+NA-1 / B stage k+NB-1, run the MFMAs on stage k
         auto k_loop = [&](auto full_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
-            char* bufs[4] = {st0, st1, st2, st3};
-            for (int kt = 0; kt < nk; kt += NST) {
+            for (int kt = 0; kt < nk; kt += S::U) {
 #pragma unroll
-                for (int s = 0; s < NST; ++s) {
+                for (int s = 0; s < S::U; ++s) {
                     const int k = kt + s;
                     if (k >= nk) break;
-                    stage_sync<S::LOADS>(min(nk - 1 - k, NST - 2));
-                    if (k + NST - 1 < nk) issue(k + NST - 1, bufs[(s + NST - 1) % NST]);
-                    mfma_stage<MI, NJ, S::KS, S::A_ROWB, S::RB, FULL>(bufs[s], acc, nvm, fl,
-                                                                      b_sub, b_pair);
+                    if (a_loader) {
+                        stage_sync<S::A_LOADS>(min(nk - 1 - k, NA - 2));
+                        if (k + NA - 1 < nk) issue_a(k + NA - 1, abuf[(s + NA - 1) % NA]);
+                    } else {
+                        stage_sync<S::B_LOADS>(min(nk - 1 - k, NB - 2));
+                        if (k + NB - 1 < nk) issue_b(k + NB - 1, bbuf[(s + NB - 1) % NB]);
+                    }
+                    mfma_stage<MI, NJ, S::KS, S::A_ROWB, S::RB, FULL>(
+                        abuf[s % NA], bbuf[s % NB], acc, nvm, fl, b_sub, b_pair);
                 }
             }
         };
@@ -292,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
         __syncthreads();   // every wave is done reading the stages
 
         // epilogue: 2 * PPW passes of HR rows each through LDS
-        uint16_t* cs = (uint16_t*)st0;
+        uint16_t* cs = (uint16_t*)sa0;
         constexpr int VPR = S::OUTC / 8;          // 16-byte pieces per output row
         constexpr int HR = S::HR;
         constexpr int SPP = MI / S::PPW;          // 16-row subtiles per pass
@@ -317,7 +361,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
                 }
             }
             __syncthreads();
-            for (int ch = tid; ch < HR * VPR; ch += 256) {
+            for (int ch = tid; ch < HR * VPR; ch += S::THREADS) {
                 const int rt = ch / VPR, c8 = ch % VPR;
                 const int grow = p * HR + rt;
                 const int gcol = n0 + c8 * 8;
@@ -330,17 +374,17 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
     }
 }
 
-template <bool GATEUP, int MI, int NJ, int BKT, int NST>
+template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB>
 hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                         const int32_t* off, int E, int K, int N, long long max_rows, int cus,
                         hipStream_t s) {
-    using S = Shape<GATEUP, MI, NJ, BKT, NST>;
+    using S = Shape<GATEUP, MI, NJ, BKT, NA, NB>;
     const long long mt = (max_rows + S::BM - 1) / S::BM + E;   // >= sum_e ceil(rows_e / BM)
     const long long tiles = mt * ((N + S::OUTC - 1) / S::OUTC);
     long long g = std::min<long long>(cus, (tiles + 7) / 8 * 8);
     g = std::max<long long>(8, g / 8 * 8);
-    hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NST>), dim3((unsigned)g), dim3(256),
-                       0, s, A, B0, B1, C, off, E, K, N);
+    hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NA, NB>), dim3((unsigned)g),
+                       dim3(S::THREADS), 0, s, A, B0, B1, C, off, E, K, N);
     return hipGetLastError();
 }
 
@@ -358,9 +402,9 @@ hipError_t launch_mfma_gate_up(const uint16_t* x_perm, const int32_t* off, const
                                const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
                                long long max_rows, int cus, hipStream_t s) {
     if (small_experts(max_rows, E))
-        return launch_shape<true, 10, 4, 64, 2>(x_perm, w_gate, w_up, h, off, E, d, d_ff,
+        return launch_shape<true, 10, 4, 64, 2, 2>(x_perm, w_gate, w_up, h, off, E, d, d_ff,
                                                 max_rows, cus, s);
-    return launch_shape<true, 8, 8, 32, 4>(x_perm, w_gate, w_up, h, off, E, d, d_ff, max_rows,
+    return launch_shape<true, 8, 4, 64, 2, 2>(x_perm, w_gate, w_up, h, off, E, d, d_ff, max_rows,
                                            cus, s);
 }
 
@@ -368,9 +412,9 @@ hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
                             int cus, hipStream_t s) {
     if (small_experts(max_rows, E))
-        return launch_shape<false, 10, 4, 64, 2>(h, w_down, nullptr, y_perm, off, E, d_ff, d,
+        return launch_shape<false, 10, 2, 64, 2, 4>(h, w_down, nullptr, y_perm, off, E, d_ff, d,
                                                  max_rows, cus, s);
-    return launch_shape<false, 8, 8, 64, 2>(h, w_down, nullptr, y_perm, off, E, d_ff, d,
+    return launch_shape<false, 8, 4, 64, 2, 2>(h, w_down, nullptr, y_perm, off, E, d_ff, d,
                                             max_rows, cus, s);
 }
 

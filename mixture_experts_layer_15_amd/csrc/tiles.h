@@ -20,7 +20,9 @@ struct TileTable {
     int mtiles[256];        // M-tiles of expert e
 };
 
-// All 256 threads of the block call this.  ntn = N-tiles per expert.
+// Every thread of the block (a multiple of 64, at least 256) calls this; the
+// first 256 own one expert each.  ntn = N-tiles per expert.  s_wave holds one
+// entry per wave.
 template <int TBM>
 __device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ off, int E, int ntn,
                                                  TileTable& tt, long long* s_wave) {
@@ -32,7 +34,7 @@ __device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ off
         mt = (kept + TBM - 1) / TBM;
         cnt = (long long)mt * ntn;
     }
-    tt.mtiles[e] = mt;
+    if (e < 256) tt.mtiles[e] = mt;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     long long v = cnt;
     for (int o = 1; o < 64; o <<= 1) {
@@ -43,7 +45,7 @@ __device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ off
     __syncthreads();
     long long add = 0;
     for (int i = 0; i < w; ++i) add += s_wave[i];
-    tt.start[e + 1] = v + add;
+    if (e < 256) tt.start[e + 1] = v + add;
     if (e == 0) tt.start[0] = 0;
     __syncthreads();
 }
