@@ -36,6 +36,8 @@ namespace moe {
 namespace {
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
@@ -106,25 +108,14 @@ struct Shape {
     static constexpr int RPK = 1024 / RB;           // sub-tile rows per 1 KB
     static constexpr int OUTC = GATEUP ? BN / 2 : BN;       // output columns per tile
     static constexpr int OUTW = OUTC / 4;                   // output columns per wave
-    static constexpr int LDC = OUTC + 8;                    // epilogue LDS row stride (elements)
-    // epilogue passes per wave-row: the fewest (a divisor of MI) whose rows fit
-    // one A stage buffer
-    static constexpr int ppw() {
-        for (int p = 1; p <= MI; ++p)
-            if (MI % p == 0 && (MI * 16 / p) * LDC * 2 <= A_BYTES) return p;
-        return MI;
-    }
-    static constexpr int PPW = ppw();
-    static constexpr int HR = MI * 16 / PPW;                 // rows per epilogue pass
     static constexpr int U = NA > NB ? NA : NB;              // K-loop unroll (static buffers)
+    static_assert(U % NA == 0 && U % NB == 0, "the larger stage count is a multiple of the smaller");
     static_assert(BKT == 32 || BKT == 64, "K-step");
     static_assert(!GATEUP || NJ % 2 == 0, "gate and up halves");
     static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole wave-loads per loader");
     static_assert(SUB_LOADS % B_LOADS == 0 || B_LOADS % SUB_LOADS == 0, "uniform sources");
-    static_assert(HR * LDC * 2 <= A_BYTES && MI % PPW == 0, "epilogue staging fits an A stage");
     static_assert(CPR <= 32 && CPR >= 8, "swizzle stays inside a row");
-    static_assert(NA >= 2 && NA <= 4 && NB >= 2 && NB <= 4 && U % NA == 0 && U % NB == 0,
-                  "stage counts");
+    static_assert(NA >= 2 && NA <= 4 && NB >= 2 && NB <= 8, "stage counts");
     static_assert(NA * A_BYTES + NB * B_BYTES + 4096 <= 160 * 1024, "LDS budget");
 };
 
@@ -161,7 +152,7 @@ __device__ __forceinline__ void mfma_stage(const char* __restrict__ sa,
             if (FULL || i < nvm) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_cur, bfr[j], acc[i][j],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], a_cur, acc[i][j],
                                                                         0, 0, 0);
             }
             a_cur = a_nxt;
@@ -178,9 +169,15 @@ __device__ __forceinline__ void mfma_stage(const char* __restrict__ sa,
 // including the later stages' prefetches.
 template <int LOADS>
 __device__ __forceinline__ void stage_sync(int later) {
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LOADS) : "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    switch (later) {
+        case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LOADS) : "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LOADS) : "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(3 * LOADS) : "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(4 * LOADS) : "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(5 * LOADS) : "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(6 * LOADS) : "memory"); break;
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -201,6 +198,10 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     __shared__ __attribute__((aligned(1024))) char sb1[S::B_BYTES];
     __shared__ __attribute__((aligned(1024))) char sb2[NB > 2 ? S::B_BYTES : 16];
     __shared__ __attribute__((aligned(1024))) char sb3[NB > 3 ? S::B_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sb4[NB > 4 ? S::B_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sb5[NB > 5 ? S::B_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sb6[NB > 6 ? S::B_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char sb7[NB > 7 ? S::B_BYTES : 16];
     __shared__ TileTable tt;
     __shared__ long long s_wave[S::WAVES];
 
@@ -297,8 +298,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
             for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         char* abuf[4] = {sa0, sa1, sa2, sa3};
-        char* bbuf[4] = {sb0, sb1, sb2, sb3};
-        __syncthreads();   // the previous tile's epilogue is done with the buffers
+        char* bbuf[8] = {sb0, sb1, sb2, sb3, sb4, sb5, sb6, sb7};
         // prologue: A stages 0 .. NA-2, B stages 0 .. NB-2
         if (a_loader) {
 #pragma unroll
@@ -333,44 +333,33 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         };
         if (nvm == MI) k_loop(std::true_type{});
         else k_loop(std::false_type{});
-        __syncthreads();   // every wave is done reading the stages
 
-        // epilogue: 2 * PPW passes of HR rows each through LDS
-        uint16_t* cs = (uint16_t*)sa0;
-        constexpr int VPR = S::OUTC / 8;          // 16-byte pieces per output row
-        constexpr int HR = S::HR;
-        constexpr int SPP = MI / S::PPW;          // 16-row subtiles per pass
+        // epilogue straight from the accumulators: lane (g4, c16) of block
+        // (i, j) holds output columns 4 g4 .. 4 g4 + 3 of row c16, one 8-byte
+        // store per block
 #pragma unroll
-        for (int p = 0; p < 2 * S::PPW; ++p) {
-            if (wm == p / S::PPW) {
+        for (int i = 0; i < MI; ++i) {
+            const int r = wm * MI * 16 + i * 16 + c16;
+            if (i < nvm && r < rows) {
+                uint16_t* crow = C + (long long)(row0 + r) * N + n0;
 #pragma unroll
-                for (int ii = 0; ii < SPP; ++ii) {
-                    const int i = (p % S::PPW) * SPP + ii;
+                for (int jj = 0; jj < S::OUTW / 16; ++jj) {
+                    const int col = wn * S::OUTW + jj * 16 + g4 * 4;
+                    bf16x4 v;
 #pragma unroll
-                    for (int jj = 0; jj < S::OUTW / 16; ++jj) {
-                        const int col = wn * S::OUTW + jj * 16 + c16;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int rt = ii * 16 + g4 * 4 + r;
-                            float v;
-                            if (GATEUP) v = gelu_erf(acc[i][jj][r]) * acc[i][jj + NJ / 2][r];
-                            else v = acc[i][jj][r];
-                            cs[rt * S::LDC + col] = (uint16_t)f32_to_bf16_bits(v);
-                        }
+                    for (int q = 0; q < 4; ++q) {
+                        const float a = acc[i][jj][q];
+                        v[q] = (__bf16)(GATEUP ? gelu_erf_bf16(a) * acc[i][jj + NJ / 2][q] : a);
                     }
+                    if (n0 + col < N) *(u32x2*)(crow + col) = __builtin_bit_cast(u32x2, v);
                 }
             }
-            __syncthreads();
-            for (int ch = tid; ch < HR * VPR; ch += S::THREADS) {
-                const int rt = ch / VPR, c8 = ch % VPR;
-                const int grow = p * HR + rt;
-                const int gcol = n0 + c8 * 8;
-                if (grow < rows && gcol < N)
-                    *(u32x4*)(C + (long long)(row0 + grow) * N + gcol) =
-                        *(const u32x4*)(cs + rt * S::LDC + c8 * 8);
-            }
-            __syncthreads();
         }
+        // LDS reads of this tile are done before the next tile's loads refill
+        // the stage buffers (a bare barrier: the stores above need no wait)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
 }
 
