@@ -69,19 +69,44 @@ __device__ __forceinline__ int hb(int r) {
     return (r & 3) | (((r >> 3) & 1) << 2);
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
-// lane (global_load_lds_dwordx4; M0 holds the wave-uniform LDS address, and
-// one wait state must separate the M0 write from the load).  Issued through
-// inline asm so that the compiler's wait-count tracking does not treat later
-// LDS reads of other stage buffers as dependent on it: the K-loop's explicit
-// vmcnt waits order every fill before the reads of its stage.
-__device__ __forceinline__ void load_to_lds(const void* gptr, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds_base), "v"(gptr) : "memory", "m0");
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for raw 32-bit byte offsets from a wave-uniform base (gfx9
+// descriptor: 48-bit base, stride 0, no range limit, raw dword format).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = (int32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu);
+    r[2] = -1;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from rsrc + soff + voff straight into LDS at lds_base +
+// 16 * lane (buffer_load_dwordx4 ... lds; M0 holds the wave-uniform LDS
+// address, and one wait state must separate the M0 write from the load).
+// Per lane the address is one 32-bit offset register, the per-stage K offset
+// rides in soff.  Issued through inline asm so that the compiler's wait-count
+// tracking does not treat later LDS reads of other stage buffers as dependent
+// on it: the K-loop's explicit vmcnt waits order every fill before the reads
+// of its stage.
+__device__ __forceinline__ void load_to_lds(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                            uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(lds_void_t*)p;
+}
+
+// x, hidden from the optimizer: values derived from it inside a loop are
+// recomputed there instead of being hoisted out and kept live (or spilled)
+// across the whole loop.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB>
@@ -117,6 +142,7 @@ struct Shape {
     static_assert(CPR <= 32 && CPR >= 8, "swizzle stays inside a row");
     static_assert(NA >= 2 && NA <= 4 && NB >= 2 && NB <= 8, "stage counts");
     static_assert(NA * A_BYTES + NB * B_BYTES + 4096 <= 160 * 1024, "LDS budget");
+    static_assert(A_LOADS <= KS * MI && B_LOADS <= KS * MI, "a slot per wave-load");
 };
 
 // Per-lane constants of the fragment reads.
@@ -126,12 +152,17 @@ struct FragLane {
 
 // One stage: KS steps of 32 in K.  B fragments through transposing reads, A
 // fragments prefetched one subtile ahead, MFMAs of the wave's valid 16-row
-// subtiles (FULL: all MI, no branches).
-template <int MI, int NJ, int KS, int A_ROWB, int RB, bool FULL>
+// subtiles (FULL: all MI, no branches).  iss(slot) is called once per
+// (ks, subtile) slot, before that subtile's MFMAs, to issue this wave's share
+// of a later stage's loads spread over the stage: issued in one burst, the
+// loads back up the CU's vector memory queue and stall the issuing wave while
+// its MFMAs wait.
+template <int MI, int NJ, int KS, int A_ROWB, int RB, bool FULL, typename Iss>
 __device__ __forceinline__ void mfma_stage(const char* __restrict__ sa,
                                            const char* __restrict__ sbb,
                                            f32x4 (&acc)[MI][NJ], int nvm, const FragLane& fl,
-                                           const int (&b_sub)[NJ], const int (&b_pair)[NJ]) {
+                                           const int (&b_sub)[NJ], const int (&b_pair)[NJ],
+                                           Iss&& iss) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         bf16x8 bfr[NJ];
@@ -147,6 +178,7 @@ __device__ __forceinline__ void mfma_stage(const char* __restrict__ sa,
         bf16x8 a_cur = *(const bf16x8*)(sa + fl.a_rd + a_ch);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
+            iss(ks * MI + i);
             const int in = (i + 1 < MI) ? i + 1 : i;
             const bf16x8 a_nxt = *(const bf16x8*)(sa + fl.a_rd + in * 16 * A_ROWB + a_ch);
             if (FULL || i < nvm) {
@@ -252,44 +284,42 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         const int nvm = __builtin_amdgcn_readfirstlane(
             max(0, min(MI, (rows - wm * MI * 16 + 15) >> 4)));
 
-        // uniform tile bases and this lane's 32-bit element offsets for each of
+        // uniform tile bases and this lane's 32-bit byte offsets for each of
         // its wave-loads (A loaders: A rows; B loaders: weight rows)
-        const uint16_t* a_base = A + (long long)row0 * K;
         const long long wofs = (long long)e * K * N + n0;
+        const i32x4 rs_a = buffer_rsrc(A + (long long)row0 * K);
+        const i32x4 rs_b0 = buffer_rsrc(B0 + wofs);
+        const i32x4 rs_b1 = buffer_rsrc((GATEUP ? B1 : B0) + wofs);
         constexpr int NL = S::A_LOADS > S::B_LOADS ? S::A_LOADS : S::B_LOADS;
-        int l_off[NL];
+        uint32_t l_off[NL];
+        const int ln = opaque(lane);
 #pragma unroll
         for (int q = 0; q < NL; ++q) {
             if (a_loader) {
-                const int r = (lw * S::A_LOADS + q) * S::A_RPK + lane / S::ACH;
-                const int c = (lane % S::ACH) ^ fa<BKT>(r);
-                l_off[q] = (q < S::A_LOADS) ? min(r, rows - 1) * K + c * 8 : 0;
+                const int r = (lw * S::A_LOADS + q) * S::A_RPK + ln / S::ACH;
+                const int c = (ln % S::ACH) ^ fa<BKT>(r);
+                l_off[q] = (q < S::A_LOADS) ? (min(r, rows - 1) * K + c * 8) * 2 : 0;
             } else {
                 const int gl = lw * S::B_LOADS + q;                 // wave-load index in the stage
-                const int r = (gl % S::SUB_LOADS) * S::RPK + lane / S::CPR;
-                const int c = (lane % S::CPR) ^ (hb<S::CPR>(r) << 1);
+                const int r = (gl % S::SUB_LOADS) * S::RPK + ln / S::CPR;
+                const int c = (ln % S::CPR) ^ (hb<S::CPR>(r) << 1);
                 const int col = min(n0 + c * 8, N - 8) - n0;
-                l_off[q] = (q < S::B_LOADS) ? r * N + col : 0;
+                l_off[q] = (q < S::B_LOADS) ? (r * N + col) * 2 : 0;
             }
         }
 
-        auto issue_a = [&](int kt, char* sa) {
-            const int ka = kt * BKT;
-            const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(sa));
-#pragma unroll
-            for (int q = 0; q < S::A_LOADS; ++q)
-                load_to_lds(a_base + (l_off[q] + ka), lb + (lw * S::A_LOADS + q) * 1024);
+        // wave-load q of A stage kt / B stage kt into the stage buffer at LDS
+        // address lb
+        auto load_a = [&](int kt, uint32_t lb, int q) {
+            load_to_lds(rs_a, l_off[q], (uint32_t)(kt * BKT * 2),
+                        lb + (lw * S::A_LOADS + q) * 1024);
         };
-        auto issue_b = [&](int kt, char* sb) {
-            const int kb = kt * BKT * N;
-            const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(sb));
-#pragma unroll
-            for (int q = 0; q < S::B_LOADS; ++q) {
-                const int gl = lw * S::B_LOADS + q;
-                const uint16_t* src = (GATEUP && gl >= S::SUB_LOADS) ? B1 : B0;
-                load_to_lds(src + wofs + (l_off[q] + kb), lb + gl * 1024);
-            }
+        auto load_b = [&](int kt, uint32_t lb, int q) {
+            const int gl = lw * S::B_LOADS + q;
+            load_to_lds((GATEUP && gl >= S::SUB_LOADS) ? rs_b1 : rs_b0, l_off[q],
+                        (uint32_t)kt * (uint32_t)(BKT * 2) * (uint32_t)N, lb + gl * 1024);
         };
+        auto lds_base = [](char* p) { return __builtin_amdgcn_readfirstlane(lds_addr(p)); };
 
         f32x4 acc[MI][NJ];
 #pragma unroll
@@ -302,37 +332,58 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         // prologue: A stages 0 .. NA-2, B stages 0 .. NB-2
         if (a_loader) {
 #pragma unroll
-            for (int q = 0; q + 1 < NA; ++q)
-                if (q < nk) issue_a(q, abuf[q]);
+            for (int kt = 0; kt + 1 < NA; ++kt)
+                if (kt < nk) {
+                    const uint32_t lb = lds_base(abuf[kt]);
+#pragma unroll
+                    for (int q = 0; q < S::A_LOADS; ++q) load_a(kt, lb, q);
+                }
         } else {
 #pragma unroll
-            for (int q = 0; q + 1 < NB; ++q)
-                if (q < nk) issue_b(q, bbuf[q]);
+            for (int kt = 0; kt + 1 < NB; ++kt)
+                if (kt < nk) {
+                    const uint32_t lb = lds_base(bbuf[kt]);
+#pragma unroll
+                    for (int q = 0; q < S::B_LOADS; ++q) load_b(kt, lb, q);
+                }
         }
 
-        // step k: wait for A and B stage k, refill the buffers read at step k-1
-        // with A stage k+NA-1 / B stage k+NB-1, run the MFMAs on stage k
-        auto k_loop = [&](auto full_tag) {
+        // step k: wait for A and B stage k, run the MFMAs on stage k and,
+        // spread among them, refill the buffers read at step k-1 with A stage
+        // k+NA-1 (A loaders) or B stage k+NB-1 (B loaders)
+        auto k_loop = [&](auto full_tag, auto role_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
+            constexpr bool ROLE_A = decltype(role_tag)::value;
+            constexpr int LOADS = ROLE_A ? S::A_LOADS : S::B_LOADS;
+            constexpr int NS = ROLE_A ? NA : NB;
+            constexpr int STRIDE = S::KS * MI / LOADS;   // slots per wave-load
             for (int kt = 0; kt < nk; kt += S::U) {
 #pragma unroll
                 for (int s = 0; s < S::U; ++s) {
                     const int k = kt + s;
                     if (k >= nk) break;
-                    if (a_loader) {
-                        stage_sync<S::A_LOADS>(min(nk - 1 - k, NA - 2));
-                        if (k + NA - 1 < nk) issue_a(k + NA - 1, abuf[(s + NA - 1) % NA]);
-                    } else {
-                        stage_sync<S::B_LOADS>(min(nk - 1 - k, NB - 2));
-                        if (k + NB - 1 < nk) issue_b(k + NB - 1, bbuf[(s + NB - 1) % NB]);
-                    }
+                    stage_sync<LOADS>(min(nk - 1 - k, NS - 2));
+                    const bool refill = k + NS - 1 < nk;
+                    const uint32_t lb = lds_base(ROLE_A ? abuf[(s + NA - 1) % NA]
+                                                        : bbuf[(s + NB - 1) % NB]);
+                    auto iss = [&](int slot) {
+                        if (slot % STRIDE == 0 && slot / STRIDE < LOADS && refill) {
+                            if constexpr (ROLE_A) load_a(k + NA - 1, lb, slot / STRIDE);
+                            else load_b(k + NB - 1, lb, slot / STRIDE);
+                        }
+                    };
                     mfma_stage<MI, NJ, S::KS, S::A_ROWB, S::RB, FULL>(
-                        abuf[s % NA], bbuf[s % NB], acc, nvm, fl, b_sub, b_pair);
+                        abuf[s % NA], bbuf[s % NB], acc, nvm, fl, b_sub, b_pair, iss);
                 }
             }
         };
-        if (nvm == MI) k_loop(std::true_type{});
-        else k_loop(std::false_type{});
+        if (a_loader) {
+            if (nvm == MI) k_loop(std::true_type{}, std::true_type{});
+            else k_loop(std::false_type{}, std::true_type{});
+        } else {
+            if (nvm == MI) k_loop(std::true_type{}, std::false_type{});
+            else k_loop(std::false_type{}, std::false_type{});
+        }
 
         // epilogue straight from the accumulators: lane (g4, c16) of block
         // (i, j) holds output columns 4 g4 .. 4 g4 + 3 of row c16, one 8-byte
