@@ -61,6 +61,33 @@ def algorithmic(cfg, counts, n_kept):
     }
 
 
+def roofline(cfg, a, launch_ms, peak, traffic, traffic_kernel):
+    """Roofline of the dominant kernel (gate/up GEMM + GeGLU): bound by whichever
+    of HBM bytes or matrix/vector flops takes longer at the chip's peak; achieved
+    = that algorithmic quantity / the average launch time."""
+    t_hbm = a["gate_up_bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_alu = a["gate_up_flops"] / (peak * 1e12)
+    sec = launch_ms * 1e-3
+    r = {"kernel": traffic_kernel or ("gemm_mfma_kernel<true, ...> (gate/up + GeGLU)"
+                                       if cfg.dtype == "bf16" else
+                                       "grouped_gemm_f32_kernel<true> (gate/up + GeGLU)")}
+    if t_hbm >= t_alu:
+        ach = a["gate_up_bytes"] / sec / 1e9
+        r.update(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                 frac=round(ach / PEAK_HBM_GBS, 4))
+    else:
+        ach = a["gate_up_flops"] / sec / 1e12
+        r.update(bound="mfma" if cfg.dtype == "bf16" else "alu", achieved=round(ach, 1),
+                 peak=peak, unit="TFLOP/s", frac=round(ach / peak, 4))
+    r.update(traffic=traffic, traffic_unit="bytes per launch",
+             algorithmic_bytes_per_launch=a["gate_up_bytes"],
+             flops_per_launch=a["gate_up_flops"],
+             hbm_frac=round(a["gate_up_bytes"] / sec / 1e9 / PEAK_HBM_GBS, 4),
+             flops_frac=round(a["gate_up_flops"] / sec / 1e12 / peak, 4),
+             avg_launch_ms=round(launch_ms, 4))
+    return r
+
+
 def measured_traffic(cfg):
     """HBM bytes per launch of the gate/up GEMM from the committed FETCH_SIZE /
     WRITE_SIZE counter runs (scaled by a plain copy of known size), or None when
@@ -266,15 +293,7 @@ def main():
                            "combine": round(gbs(a["combine_bytes"], stage_ms["combine"]) / PEAK_HBM_GBS, 4)},
         "gpu_ms_per_step_events": round(gpu_ms, 4),
         "fused_forward_ms_per_step": round(fused_ms, 4),
-        "roofline": {"kernel": traffic_kernel or ("gemm_mfma_kernel<true, ...> (gate/up + GeGLU)"
-                                                  if cfg.dtype == "bf16" else
-                                                  "grouped_gemm_f32_kernel<true> (gate/up + GeGLU)"),
-                     "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": round(gu_tflops, 1), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(gu_tflops / peak, 4), "traffic": traffic,
-                     "traffic_unit": "bytes per launch",
-                     "algorithmic_bytes_per_launch": a["gate_up_bytes"],
-                     "flops_per_launch": a["gate_up_flops"],
-                     "avg_launch_ms": round(stage_ms["gate_up"], 4)},
+        "roofline": roofline(cfg, a, stage_ms["gate_up"], peak, traffic, traffic_kernel),
     }
     if not args.no_cpu_baseline:
         host = {k2: (None if v is None else v.cpu()) for k2, v in dev.items()}
