@@ -190,6 +190,130 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     }
 }
 
+// K-split variant for E <= 128 (E % 8 == 0): a workgroup of 4 waves takes 16*MT
+// tokens and wave w accumulates the K-steps w, w+4, w+8, ... of all of them,
+// so a small batch still spreads over every CU and each wave keeps D K-steps
+// of token rows in flight.  Each wave stages its own K-step of W_r in LDS.
+// The four partial logits are summed in LDS in wave order (deterministic);
+// wave w then owns row r = w of every 4-row accumulator group for the top-k.
+template <int NT, int MT, int D>
+__global__ __launch_bounds__(256) void router_ks_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits, int32_t* __restrict__ idx,
+    float* __restrict__ gate, long long T, int d, int E, int k, float tau, int renorm) {
+    constexpr int EP = 16 * NT;
+    constexpr int W_LD = EP + 8;               // LDS row stride (elements)
+    constexpr int WCH = RBK * EP / 8 / 64;     // 16-byte W_r chunks per lane per K-step
+    __shared__ __attribute__((aligned(16))) uint16_t ws[4][RBK * W_LD];
+    __shared__ float part[4][MT][NT][4][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c16 = lane & 15, g4 = lane >> 4;
+    const long long t0 = (long long)blockIdx.x * (16 * MT);
+    const int nk = d / RBK;
+    const int nw = nk > wave ? (nk - wave + 3) / 4 : 0;   // K-steps of this wave
+
+    const uint16_t* xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        long long t = t0 + mt * 16 + c16;
+        if (t > T - 1) t = T - 1;
+        xrow[mt] = x + t * d + g4 * 8;
+    }
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // register ring of D K-steps: token-row fragments and this lane's W_r chunks
+    bf16x8 ra[D][MT][2];
+    u32x4 rw[D][WCH];
+    auto issue = [&](int i, bf16x8 (&a)[MT][2], u32x4 (&wv)[WCH]) {
+        const int k0 = (wave + 4 * i) * RBK;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) a[mt][ks] = *(const bf16x8*)(xrow[mt] + k0 + ks * 32);
+#pragma unroll
+        for (int c = 0; c < WCH; ++c) {
+            const int v = lane + 64 * c;
+            const int kr = v / (EP / 8), c8 = (v % (EP / 8)) * 8;
+            wv[c] = (c8 < E) ? *(const u32x4*)(wr + (long long)(k0 + kr) * E + c8)
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    uint16_t* wsw = ws[wave];
+    auto step = [&](const bf16x8 (&a)[MT][2], const u32x4 (&wv)[WCH]) {
+#pragma unroll
+        for (int c = 0; c < WCH; ++c) {
+            const int v = lane + 64 * c;
+            const int kr = v / (EP / 8), c8 = (v % (EP / 8)) * 8;
+            *(u32x4*)(&wsw[kr * W_LD + c8]) = wv[c];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int row = ks * 32 + g4 * 8 + (c16 >> 2);
+                const int col = nt * 16 + (c16 & 3) * 4;
+                s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(&wsw[row * W_LD + col]));
+                s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(&wsw[(row + 4) * W_LD + col]));
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const bf16x8 b = __builtin_bit_cast(
+                    bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][ks], b, acc[mt][nt], 0, 0, 0);
+            }
+        }
+    };
+#pragma unroll
+    for (int j = 0; j + 1 < D; ++j)
+        if (j < nw) issue(j, ra[j], rw[j]);
+    for (int i0 = 0; i0 < nw; i0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int i = i0 + j;
+            if (i >= nw) break;
+            if (i + D - 1 < nw) issue(i + D - 1, ra[(j + D - 1) % D], rw[(j + D - 1) % D]);
+            step(ra[j], rw[j]);
+        }
+    }
+
+    // sum the four partials in wave order; wave w finishes accumulator row w
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[wave][mt][nt][r][lane] = acc[mt][nt][r];
+    __syncthreads();
+    const int r = wave;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const long long t = t0 + mt * 16 + g4 * 4 + r;
+        float v[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int e = nt * 16 + c16;
+            float l = part[0][mt][nt][r][lane];
+            l += part[1][mt][nt][r][lane];
+            l += part[2][mt][nt][r][lane];
+            l += part[3][mt][nt][r][lane];
+            if (bias != nullptr && e < E) l += bias[e];
+            v[nt] = l;
+            if (t < T && e < E) logits[t * E + e] = l;
+        }
+        const bool ok = t < T;
+        const long long tt = ok ? t : 0;
+        topk_group16<NT>(v, c16, E, k, tau, renorm, ok, idx + tt * k, gate + tt * k);
+    }
+}
+
 // fp32 path: plain fp32 FMA dot products (64 tokens per workgroup) into an
 // LDS logits tile, then the same 16-lane top-k.
 template <int NT>
@@ -244,13 +368,40 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     topk_group16<NT>(v, q, E, k, tau, renorm, ok, idx + tt * k, gate + tt * k);
 }
 
+// K-split router launch: 16*MT tokens per workgroup, MT grown only while at
+// least 512 workgroups remain; D K-steps in flight per wave.
+template <int NT>
+hipError_t route_ks(const uint16_t* x, const uint16_t* w, const float* bias, float* logits,
+                    int32_t* idx, float* gate, long long T, int d, int E, int k, float tau,
+                    int renorm, hipStream_t s) {
+    // E > 64: W_r chunks take 64 registers per K-step in flight, so two steps
+    // and at most two token tiles per wave
+    constexpr int MT4 = NT <= 4 ? 4 : 2, D4 = 2;
+    constexpr int D2 = NT <= 4 ? 3 : 2, D1 = NT <= 4 ? 4 : 2;
+    if (T >= 16LL * MT4 * 512)
+        hipLaunchKernelGGL((router_ks_kernel<NT, MT4, D4>), dim3((unsigned)((T + 16 * MT4 - 1) / (16 * MT4))),
+                           dim3(256), 0, s, x, w, bias, logits, idx, gate, T, d, E, k, tau, renorm);
+    else if (T >= 16LL * 2 * 512)
+        hipLaunchKernelGGL((router_ks_kernel<NT, 2, D2>), dim3((unsigned)((T + 31) / 32)), dim3(256),
+                           0, s, x, w, bias, logits, idx, gate, T, d, E, k, tau, renorm);
+    else
+        hipLaunchKernelGGL((router_ks_kernel<NT, 1, D1>), dim3((unsigned)((T + 15) / 16)), dim3(256),
+                           0, s, x, w, bias, logits, idx, gate, T, d, E, k, tau, renorm);
+    return hipGetLastError();
+}
+
 template <int NT>
 hipError_t route_nt(int dtype, const void* x, const void* w, const float* bias, float* logits,
                     int32_t* idx, float* gate, long long T, int d, int E, int k, float tau,
                     int renorm, hipStream_t s) {
     if (dtype == 1) {
-        // two 16-row tiles per wave once there are enough tokens to fill the GPU
+        if constexpr (NT <= 8) {
+            if (E % 8 == 0)
+                return route_ks<NT>((const uint16_t*)x, (const uint16_t*)w, bias, logits, idx,
+                                    gate, T, d, E, k, tau, renorm, s);
+        }
         if (T >= 64LL * 1024 && NT <= 8) {
+            // two 16-row tiles per wave once there are enough tokens to fill the GPU
             const long long grid = (T + 127) / 128;
             hipLaunchKernelGGL((router_bf16_kernel<NT, 2>), dim3((unsigned)grid), dim3(256), 0, s,
                                (const uint16_t*)x, (const uint16_t*)w, bias, logits, idx, gate,
