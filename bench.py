@@ -4,9 +4,11 @@ A step is one pass of the whole layer -- route, dispatch, gate/up GEMM, down
 GEMM, combine -- over one batch of synthetic tokens, through the C ABI.
 Inputs sit in HBM before the timed region; the token batch rotates over
 several copies so that no step finds its activations in the 256 MB
-last-level cache (the weights, 1.6 GB here, never fit).  HIP events recorded
-on the launch stream between the stages give each stage's time inside the
-same timed region.
+last-level cache (the weights, 1.6 GB here, never fit).  Two timed regions:
+the fused entry point moe_forward gives the step time and `value` (tokens/s);
+the same steps through the five per-stage entry points, with HIP events
+recorded on the launch stream between them, give each stage's time (and the
+roofline of the dominant kernel).
 
 Prints ONE JSON line.  Default workload: the ZAYA1-like layer (T = 4096,
 d = 2048, E = 16, top-1, GeGLU d_ff = 8192, bf16).  ``--config`` selects
@@ -230,7 +232,7 @@ def main():
     gpu_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][5]) for i in range(K)]))
     ms_step = wall * 1e3 / K
 
-    # the fused entry point, same work, for reference
+    # the fused entry point: the step time that `value` reports
     fwd = moe.Forward(cfg)
     for i in range(3):
         fwd(xs[i % n_rot], wr, bias, wg, wu, wd, y)
@@ -266,12 +268,12 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(cfg.T / (ms_step * 1e-3), 1),
+        "value": round(cfg.T / (fused_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(fused_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -291,8 +293,8 @@ def main():
                       "combine": round(gbs(a["combine_bytes"], stage_ms["combine"]), 1)},
         "stage_hbm_frac": {"dispatch": round(gbs(a["dispatch_bytes"], stage_ms["dispatch"]) / PEAK_HBM_GBS, 4),
                            "combine": round(gbs(a["combine_bytes"], stage_ms["combine"]) / PEAK_HBM_GBS, 4)},
-        "gpu_ms_per_step_events": round(gpu_ms, 4),
-        "fused_forward_ms_per_step": round(fused_ms, 4),
+        "staged_ms_per_step": round(ms_step, 4),
+        "staged_gpu_ms_per_step_events": round(gpu_ms, 4),
         "roofline": roofline(cfg, a, stage_ms["gate_up"], peak, traffic, traffic_kernel),
     }
     if not args.no_cpu_baseline:

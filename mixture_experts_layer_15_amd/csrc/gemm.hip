@@ -85,10 +85,11 @@ int grid_for(long long tiles, int grid_cap) {
 
 hipError_t launch_gate_up(int dtype, const void* x_perm, const int32_t* off, const void* w_gate,
                           const void* w_up, void* h, int E, int d, int d_ff, long long max_rows,
-                          int grid_cap, hipStream_t s) {
+                          int grid_cap, hipStream_t s, const int32_t* gather_rows) {
     if (max_rows == 0) return hipSuccess;
+    if (gather_rows != nullptr && dtype != 1) return hipErrorInvalidValue;   // bf16 only
     if (dtype == 1)
-        return launch_mfma_gate_up((const uint16_t*)x_perm, off, (const uint16_t*)w_gate,
+        return launch_mfma_gate_up((const uint16_t*)x_perm, gather_rows, off, (const uint16_t*)w_gate,
                                    (const uint16_t*)w_up, (uint16_t*)h, E, d, d_ff, max_rows,
                                    grid_cap / 2, s);
     {

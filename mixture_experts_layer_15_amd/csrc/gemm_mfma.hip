@@ -218,7 +218,7 @@ template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB>
 __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
-    const int32_t* __restrict__ off, int E, int K, int N) {
+    const int32_t* __restrict__ off, const int32_t* __restrict__ a_rows, int E, int K, int N) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB>;
     // one distinct __shared__ array per stage buffer, so that the compiler can
     // tell the reads of one stage from the fills of the others
@@ -287,7 +287,10 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         // uniform tile bases and this lane's 32-bit byte offsets for each of
         // its wave-loads (A loaders: A rows; B loaders: weight rows)
         const long long wofs = (long long)e * K * N + n0;
-        const i32x4 rs_a = buffer_rsrc(A + (long long)row0 * K);
+        // A rows: rows row0.. of A, or (a_rows != nullptr) the rows a_rows[row0..]
+        // of A gathered (byte offsets then span all of A: the host checks they
+        // fit 32 bits)
+        const i32x4 rs_a = buffer_rsrc(a_rows ? A : A + (long long)row0 * K);
         const i32x4 rs_b0 = buffer_rsrc(B0 + wofs);
         const i32x4 rs_b1 = buffer_rsrc((GATEUP ? B1 : B0) + wofs);
         constexpr int NL = S::A_LOADS > S::B_LOADS ? S::A_LOADS : S::B_LOADS;
@@ -298,7 +301,9 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
             if (a_loader) {
                 const int r = (lw * S::A_LOADS + q) * S::A_RPK + ln / S::ACH;
                 const int c = (ln % S::ACH) ^ fa<BKT>(r);
-                l_off[q] = (q < S::A_LOADS) ? (min(r, rows - 1) * K + c * 8) * 2 : 0;
+                const int rr = min(r, rows - 1);
+                const int src = a_rows ? a_rows[row0 + rr] : rr;
+                l_off[q] = (q < S::A_LOADS) ? ((uint32_t)src * (uint32_t)K + c * 8) * 2u : 0u;
             } else {
                 const int gl = lw * S::B_LOADS + q;                 // wave-load index in the stage
                 const int r = (gl % S::SUB_LOADS) * S::RPK + ln / S::CPR;
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
 
 template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB>
 hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
-                        const int32_t* off, int E, int K, int N, long long max_rows, int cus,
+                        const int32_t* off, const int32_t* a_rows, int E, int K, int N, long long max_rows, int cus,
                         hipStream_t s) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB>;
     const long long mt = (max_rows + S::BM - 1) / S::BM + E;   // >= sum_e ceil(rows_e / BM)
@@ -424,7 +429,7 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
     long long g = std::min<long long>(cus, (tiles + 7) / 8 * 8);
     g = std::max<long long>(8, g / 8 * 8);
     hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NA, NB>), dim3((unsigned)g),
-                       dim3(S::THREADS), 0, s, A, B0, B1, C, off, E, K, N);
+                       dim3(S::THREADS), 0, s, A, B0, B1, C, off, a_rows, E, K, N);
     return hipGetLastError();
 }
 
@@ -438,13 +443,14 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
 // 256 x 256 tiles (the most flops per byte moved into a CU).
 static bool small_experts(long long max_rows, int E) { return max_rows <= 320LL * E; }
 
-hipError_t launch_mfma_gate_up(const uint16_t* x_perm, const int32_t* off, const uint16_t* w_gate,
+hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const int32_t* off,
+                               const uint16_t* w_gate,
                                const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
                                long long max_rows, int cus, hipStream_t s) {
     if (small_experts(max_rows, E))
-        return launch_shape<true, 10, 4, 64, 2, 2>(x_perm, w_gate, w_up, h, off, E, d, d_ff,
+        return launch_shape<true, 10, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, E, d, d_ff,
                                                 max_rows, cus, s);
-    return launch_shape<true, 8, 4, 64, 2, 2>(x_perm, w_gate, w_up, h, off, E, d, d_ff, max_rows,
+    return launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, E, d, d_ff, max_rows,
                                            cus, s);
 }
 
@@ -452,9 +458,9 @@ hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
                             int cus, hipStream_t s) {
     if (small_experts(max_rows, E))
-        return launch_shape<false, 10, 2, 64, 2, 4>(h, w_down, nullptr, y_perm, off, E, d_ff, d,
+        return launch_shape<false, 10, 2, 64, 2, 4>(h, w_down, nullptr, y_perm, off, nullptr, E, d_ff, d,
                                                  max_rows, cus, s);
-    return launch_shape<false, 8, 4, 64, 2, 2>(h, w_down, nullptr, y_perm, off, E, d_ff, d,
+    return launch_shape<false, 8, 4, 64, 2, 2>(h, w_down, nullptr, y_perm, off, nullptr, E, d_ff, d,
                                             max_rows, cus, s);
 }
 

@@ -29,9 +29,12 @@ struct DispatchPlan {
 };
 DispatchPlan plan_dispatch(long long T, int E, int k, long long C);
 size_t dispatch_workspace_bytes(const DispatchPlan& p);
+// scatter = false leaves x_perm unwritten (for a consumer that gathers rows of
+// x through token_of_row itself).
 hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx, const void* x,
                            void* x_perm, int32_t* count, int32_t* offset, int32_t* row_of,
-                           int32_t* token_of_row, void* workspace, int d, hipStream_t s);
+                           int32_t* token_of_row, void* workspace, int d, hipStream_t s,
+                           bool scatter = true);
 
 // Grouped GeGLU expert FFN (gate/up GEMM with fused epilogue, then down GEMM).
 hipError_t launch_expert_ffn(int dtype, const void* x_perm, const int32_t* off,
@@ -42,13 +45,16 @@ hipError_t launch_expert_ffn(int dtype, const void* x_perm, const int32_t* off,
 // The two halves of the expert FFN, one launch each.
 hipError_t launch_gate_up(int dtype, const void* x_perm, const int32_t* off, const void* w_gate,
                           const void* w_up, void* h, int E, int d, int d_ff, long long max_rows,
-                          int grid_cap, hipStream_t s);
+                          int grid_cap, hipStream_t s, const int32_t* gather_rows = nullptr);
 hipError_t launch_down(int dtype, const void* h, const int32_t* off, const void* w_down,
                        void* y_perm, int E, int d, int d_ff, long long max_rows, int grid_cap,
                        hipStream_t s);
 
 // bf16 MFMA kernels (gemm_mfma.hip); cus = workgroups of the persistent grid.
-hipError_t launch_mfma_gate_up(const uint16_t* x_perm, const int32_t* off, const uint16_t* w_gate,
+// gate/up reads its rows from a: x_perm (a_rows == nullptr), or x gathered
+// through a_rows = token_of_row.
+hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const int32_t* off,
+                               const uint16_t* w_gate,
                                const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
                                long long max_rows, int cus, hipStream_t s);
 hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_t* w_down,

@@ -333,14 +333,20 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     hipError_t e = moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T,
                                      cfg->d, cfg->E, cfg->k, cfg->temperature, cfg->renormalize, s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
+    // bf16: the gate/up GEMM gathers its rows of x through token_of_row, so
+    // x_perm is never written (its 32-bit byte offsets must span x)
+    const bool gather = cfg->dtype == MOE_BF16 && T * d * es < ((size_t)1 << 32);
     const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg));
     e = moe::launch_dispatch(p, cfg->dtype, idx, x, w + L.x_perm, count, offset, row_of, tor,
-                             w + L.dsp, cfg->d, s);
+                             w + L.dsp, cfg->d, s, !gather);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/dispatch");
-    e = moe::launch_expert_ffn(cfg->dtype, w + L.x_perm, offset, w_gate, w_up, w_down, w + L.h,
-                               w + L.y_perm, cfg->E, cfg->d, cfg->d_ff, max_rows(cfg),
-                               gemm_grid_cap(), s);
-    if (e != hipSuccess) return hip_fail(e, "moe_forward/expert_ffn");
+    e = moe::launch_gate_up(cfg->dtype, gather ? x : (const void*)(w + L.x_perm), offset, w_gate,
+                            w_up, w + L.h, cfg->E, cfg->d, cfg->d_ff, max_rows(cfg),
+                            gemm_grid_cap(), s, gather ? tor : nullptr);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/gate_up");
+    e = moe::launch_down(cfg->dtype, w + L.h, offset, w_down, w + L.y_perm, cfg->E, cfg->d,
+                         cfg->d_ff, max_rows(cfg), gemm_grid_cap(), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/down");
     e = moe::launch_combine(cfg->dtype, w + L.y_perm, row_of, gate, y, cfg->T, cfg->d, cfg->k, s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
     return MOE_OK;
