@@ -124,23 +124,39 @@ int64_t orc_capacity(int64_t T, int64_t E, int64_t k, int64_t cap_num, int64_t c
     return (num + den - 1) / den;
 }
 
-/* Step 4 -- token-order positions, capacity drops and the permutation.
- * pos[t][j] = number of earlier assignments (t' < t) to the same expert;
- * kept when pos < C.  count = assignments per expert before drops,
- * kept_e = min(count_e, C), offset = exclusive prefix sum of kept (E + 1
- * entries, offset[E] = rows kept in total).  Rows are grouped by expert,
- * ascending token inside an expert: row = offset[e] + pos, or -1 if dropped;
- * token_of_row[row] = t. */
+/* Step 4 -- positions, capacity drops and the permutation.
+ * An assignment (t, j) of token t to expert e = idx[t][j] is kept when fewer
+ * than C assignments to e come before it in the priority order:
+ *  - policy 0, token order (the reading of "drop the overflow in token order",
+ *    TorchTitan 1K-GPU article, section 2.1): (t', j') comes first when t' < t
+ *    (a token never picks an expert twice, so j does not matter);
+ *  - policy 1, choice order (GShard-style priority, a variant): all first
+ *    choices in token order, then all second choices, ...: (t', j') comes
+ *    first when j' < j, or j' == j and t' < t.
+ * pos[t][j] = number of assignments to the same expert before (t, j) in that
+ * order.  count = assignments per expert before drops, kept_e = min(count_e,
+ * C), offset = exclusive prefix sum of kept (E + 1 entries, offset[E] = rows
+ * kept in total).  Rows are grouped by expert in priority order:
+ * row = offset[e] + pos, or -1 if dropped; token_of_row[row] = t. */
 void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C, const int32_t* idx,
                   int32_t* count, int32_t* kept, int32_t* offset, int32_t* pos,
-                  int32_t* row_of, int32_t* token_of_row) {
+                  int32_t* row_of, int32_t* token_of_row, int policy) {
     for (int64_t e = 0; e < E; ++e) count[e] = 0;
-    for (int64_t t = 0; t < T; ++t)
-        for (int64_t j = 0; j < k; ++j) {
-            int32_t e = idx[t * k + j];
-            pos[t * k + j] = count[e];
-            count[e] += 1;
-        }
+    if (policy == 0) {
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t j = 0; j < k; ++j) {
+                int32_t e = idx[t * k + j];
+                pos[t * k + j] = count[e];
+                count[e] += 1;
+            }
+    } else {
+        for (int64_t j = 0; j < k; ++j)
+            for (int64_t t = 0; t < T; ++t) {
+                int32_t e = idx[t * k + j];
+                pos[t * k + j] = count[e];
+                count[e] += 1;
+            }
+    }
     offset[0] = 0;
     for (int64_t e = 0; e < E; ++e) {
         kept[e] = count[e] < C ? count[e] : (int32_t)C;
@@ -157,6 +173,46 @@ void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C, const int32_t* idx
                 row_of[a] = -1;
             }
         }
+}
+
+/* Expert-load telemetry from the per-expert assignment counts before drops.
+ * The ZAYA1 page (section 3.2) reports keeping the expert load balance within
+ * +-5%, and advises monitoring the load balance during training (section on
+ * routing practice); the balance figure read here is the largest deviation of
+ * an expert's load from the mean load, relative to the mean.
+ * out[0] mean load m = sum_e count_e / E
+ * out[1] max_e count_e            out[2] min_e count_e
+ * out[3] max / m                  out[4] max_e |count_e - m| / m
+ * out[5] sqrt(sum_e (count_e - m)^2 / E) / m   (coefficient of variation)
+ * out[6] dropped assignments = sum_e max(0, count_e - C)
+ * out[7] experts with no assignment
+ * With no assignments at all (m = 0) the three ratios are 0. */
+void orc_load_stats(int64_t E, const int32_t* count, int64_t C, double* out) {
+    double sum = 0.0, mx = (double)count[0], mn = (double)count[0], dropped = 0.0, empty = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+        double c = (double)count[e];
+        sum += c;
+        if (c > mx) mx = c;
+        if (c < mn) mn = c;
+        if (c > (double)C) dropped += c - (double)C;
+        if (count[e] == 0) empty += 1.0;
+    }
+    double m = sum / (double)E;
+    double dev = 0.0, ss = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+        double diff = (double)count[e] - m;
+        double ad = diff < 0 ? -diff : diff;
+        if (ad > dev) dev = ad;
+        ss += diff * diff;
+    }
+    out[0] = m;
+    out[1] = mx;
+    out[2] = mn;
+    out[3] = m > 0 ? mx / m : 0.0;
+    out[4] = m > 0 ? dev / m : 0.0;
+    out[5] = m > 0 ? sqrt(ss / (double)E) / m : 0.0;
+    out[6] = dropped;
+    out[7] = empty;
 }
 
 /* Step 5 -- the GeGLU expert FFN for a list of (token, expert) rows.

@@ -62,8 +62,10 @@ def _declare(lib):
     lib.orc_route.restype = None
     lib.orc_capacity.argtypes = [_I64, _I64, _I64, _I64, _I64]
     lib.orc_capacity.restype = _I64
-    lib.orc_dispatch.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]
+    lib.orc_dispatch.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int]
     lib.orc_dispatch.restype = None
+    lib.orc_load_stats.argtypes = [_I64, _P, _I64, _P]
+    lib.orc_load_stats.restype = None
     lib.orc_ffn_rows.argtypes = [_I64, _P, _P, _I64, _I64, ctypes.c_int,
                                  _P, _P, _P, _P, _P, _P]
     lib.orc_ffn_rows.restype = None
@@ -125,8 +127,9 @@ def capacity(T: int, E: int, k: int, cap_num: int, cap_den: int) -> int:
     return int(_load().orc_capacity(T, E, k, cap_num, cap_den))
 
 
-def dispatch(idx: np.ndarray, E: int, C: int) -> Dict[str, np.ndarray]:
-    """Token-order positions, drops, counts, offsets and the permutation maps."""
+def dispatch(idx: np.ndarray, E: int, C: int, policy: int = 0) -> Dict[str, np.ndarray]:
+    """Positions in priority order (0: token order, 1: choice order), drops,
+    counts, offsets and the permutation maps."""
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     T, k = idx.shape
     count = np.empty(E, dtype=np.int32)
@@ -136,7 +139,7 @@ def dispatch(idx: np.ndarray, E: int, C: int) -> Dict[str, np.ndarray]:
     row_of = np.empty((T, k), dtype=np.int32)
     token_of_row = np.full(T * k, -1, dtype=np.int32)
     _load().orc_dispatch(T, E, k, C, _ptr(idx), _ptr(count), _ptr(kept), _ptr(offset),
-                         _ptr(pos), _ptr(row_of), _ptr(token_of_row))
+                         _ptr(pos), _ptr(row_of), _ptr(token_of_row), int(policy))
     n_kept = int(offset[E])
     return dict(count=count, kept=kept, offset=offset, pos=pos, row_of=row_of,
                 token_of_row=token_of_row[:n_kept].copy(), n_kept=n_kept)
@@ -181,8 +184,16 @@ def combine(tokens: Sequence[int], row_of: np.ndarray, gate: np.ndarray,
     return y
 
 
+def load_stats(count: np.ndarray, C: int) -> np.ndarray:
+    """Expert-load telemetry (8 values, see orc_load_stats) from counts before drops."""
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    out = np.empty(8, dtype=np.float64)
+    _load().orc_load_stats(count.shape[0], _ptr(count), int(C), _ptr(out))
+    return out
+
+
 def forward(x, w_router, bias, w_gate, w_up, w_down, *, k: int, tau: float,
-            renormalize: bool, cap_num: int, cap_den: int,
+            renormalize: bool, cap_num: int, cap_den: int, drop_policy: int = 0,
             logits_in: Optional[np.ndarray] = None,
             tokens: Optional[Sequence[int]] = None, want_h: bool = False) -> Dict:
     """The whole layer in fp64.
@@ -198,7 +209,7 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, *, k: int, tau: float,
     lg = logits(x, w_router, bias) if logits_in is None else np.asarray(logits_in, np.float64)
     idx, gate = route(lg, k, tau, renormalize)
     C = capacity(T, E, k, cap_num, cap_den)
-    dsp = dispatch(idx, E, C)
+    dsp = dispatch(idx, E, C, drop_policy)
     toks = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
     slot_tok = np.repeat(toks, k)
     slot_ex = idx[toks].reshape(-1)

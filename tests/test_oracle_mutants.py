@@ -27,10 +27,19 @@ MUTANTS = {
     "capacity floor": ("return (num + den - 1) / den;", "return num / den;"),
     "keep one too many": ("if (pos[a] < C) {", "if (pos[a] <= C) {"),
     "choice-major drops": (
-        "for (int64_t t = 0; t < T; ++t)\n        for (int64_t j = 0; j < k; ++j) {\n"
-        "            int32_t e = idx[t * k + j];",
-        "for (int64_t j = 0; j < k; ++j)\n        for (int64_t t = 0; t < T; ++t) {\n"
-        "            int32_t e = idx[t * k + j];"),
+        "for (int64_t t = 0; t < T; ++t)\n            for (int64_t j = 0; j < k; ++j) {\n"
+        "                int32_t e = idx[t * k + j];",
+        "for (int64_t j = 0; j < k; ++j)\n            for (int64_t t = 0; t < T; ++t) {\n"
+        "                int32_t e = idx[t * k + j];"),
+    "choice order ignored": (
+        "for (int64_t j = 0; j < k; ++j)\n            for (int64_t t = 0; t < T; ++t) {\n"
+        "                int32_t e = idx[t * k + j];",
+        "for (int64_t t = 0; t < T; ++t)\n            for (int64_t j = 0; j < k; ++j) {\n"
+        "                int32_t e = idx[t * k + j];"),
+    "load deviation signed": ("double ad = diff < 0 ? -diff : diff;", "double ad = diff;"),
+    "load CV with E - 1": ("sqrt(ss / (double)E)", "sqrt(ss / (double)(E - 1))"),
+    "mean load over busy experts": ("double m = sum / (double)E;",
+                                    "double m = sum / (double)(E - empty);"),
     "tanh GELU": ("0.5 * v * (1.0 + erf(v / sqrt(2.0)))",
                   "0.5 * v * (1.0 + tanh(0.7978845608028654 * (v + 0.044715 * v * v * v)))"),
     "GELU on the up branch": ("g[n] = gelu(g[n]) * u[n];", "g[n] = g[n] * gelu(u[n]);"),

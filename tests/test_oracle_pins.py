@@ -197,6 +197,86 @@ def test_drops_follow_token_order_not_choice_rank():
     assert got["kept"].tolist() == [1, 1, 1] and got["count"].tolist() == [2, 1, 1]
 
 
+def _brute_keep_choice_order(idx, C):
+    """keep[t][j] iff fewer than C assignments to the same expert come before
+    (t, j) when all first choices (in token order) precede all second choices."""
+    T, k = idx.shape
+    keep = np.zeros((T, k), dtype=bool)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            earlier = sum(1 for jp in range(k) for tp in range(T)
+                          if (jp, tp) < (j, t) and idx[tp, jp] == e)
+            keep[t, j] = earlier < C
+    return keep
+
+
+@pytest.mark.parametrize("C", [0, 1, 3, 7, 40])
+@pytest.mark.parametrize("E,k", [(5, 2), (4, 1), (6, 3), (3, 3)])
+def test_choice_order_dispatch_matches_bruteforce(C, E, k):
+    T = 40
+    idx = _random_choices(T, E, k, seed=C * 37 + E * 11 + k)
+    got = orc.dispatch(idx, E, C, policy=1)
+    keep = _brute_keep_choice_order(idx, C)
+    count = np.bincount(idx.reshape(-1), minlength=E)
+    np.testing.assert_array_equal(got["count"], count)
+    kept = np.bincount(idx[keep], minlength=E)
+    np.testing.assert_array_equal(got["kept"], kept)
+    np.testing.assert_array_equal(got["offset"], np.concatenate([[0], np.cumsum(kept)]))
+    # rows of an expert in priority order: (expert, choice rank, token) -- lexsort
+    tt, jj = np.nonzero(keep)
+    order = np.lexsort((tt, jj, idx[tt, jj]))
+    np.testing.assert_array_equal(got["token_of_row"], tt[order])
+    row_of = np.full((T, k), -1)
+    row_of[tt[order], jj[order]] = np.arange(order.size)
+    np.testing.assert_array_equal(got["row_of"], row_of)
+
+
+def test_choice_order_differs_from_token_order():
+    # worked by hand: expert 1 is token 0's second choice and token 1's first;
+    # with C = 1 token order keeps token 0's, choice order keeps token 1's
+    idx = np.array([[0, 1], [1, 0], [0, 1]], dtype=np.int32)
+    tok = orc.dispatch(idx, 2, 1, policy=0)
+    cho = orc.dispatch(idx, 2, 1, policy=1)
+    assert tok["row_of"].tolist() == [[0, 1], [-1, -1], [-1, -1]]
+    assert cho["row_of"].tolist() == [[0, -1], [1, -1], [-1, -1]]
+    assert tok["token_of_row"].tolist() == [0, 0] and cho["token_of_row"].tolist() == [0, 1]
+    # k = 1: the two orders coincide
+    one = np.array([[2], [0], [2], [1], [2]], dtype=np.int32)
+    for C in (0, 1, 2):
+        a, b = orc.dispatch(one, 3, C, 0), orc.dispatch(one, 3, C, 1)
+        assert a["row_of"].tolist() == b["row_of"].tolist()
+
+
+# ---------------------------------------------------------------- load telemetry
+
+def test_load_stats_closed_forms():
+    E = 8
+    # uniform load: every ratio at its floor
+    s = orc.load_stats(np.full(E, 5, np.int32), C=5)
+    assert s.tolist() == [5.0, 5.0, 5.0, 1.0, 0.0, 0.0, 0.0, 0.0]
+    # everything on one expert: max/mean = E, deviation E - 1, CV = sqrt(E - 1)
+    one = np.zeros(E, np.int32)
+    one[3] = 64
+    s = orc.load_stats(one, C=10)
+    assert s[0] == 8.0 and s[1] == 64.0 and s[2] == 0.0 and s[3] == E
+    assert s[4] == E - 1 and abs(s[5] - np.sqrt(E - 1)) < 1e-15
+    assert s[6] == 64 - 10 and s[7] == E - 1
+    # worked by hand: counts 3, 1, 0, 4 (mean 2), C = 2
+    s = orc.load_stats(np.array([3, 1, 0, 4], np.int32), C=2)
+    assert s[:5].tolist() == [2.0, 4.0, 0.0, 2.0, 1.0]
+    assert abs(s[5] - np.sqrt(10.0 / 4.0) / 2.0) < 1e-15
+    assert s[6] == 3.0 and s[7] == 1.0
+    # no assignments at all: ratios 0, every expert empty
+    assert orc.load_stats(np.zeros(4, np.int32), C=0).tolist() == [0.0] * 7 + [4.0]
+
+
+def test_load_stats_deviation_is_largest_either_side():
+    # the largest deviation may sit below the mean: counts 10, 10, 10, 2
+    s = orc.load_stats(np.array([10, 10, 10, 2], np.int32), C=100)
+    assert s[0] == 8.0 and s[4] == 6.0 / 8.0 and s[3] == 10.0 / 8.0
+
+
 # ---------------------------------------------------------------- expert FFN
 
 def test_gelu_is_erf_form_against_normal_table():
