@@ -68,7 +68,8 @@ typedef enum {
  *   1 <= E <= 256, 1 <= k <= min(E, 8)
  *   temperature > 0 and finite
  *   cap_den == 0: no capacity limit (C = T); else cap_num >= 0, cap_den > 0
- *   renormalize: 0 or 1;  dtype: a moe_dtype */
+ *   renormalize: 0 or 1;  dtype: a moe_dtype
+ *   drop_policy: a moe_drop_policy (appended field; zero = the default) */
 typedef struct {
     int64_t T;
     int32_t d;
@@ -80,7 +81,20 @@ typedef struct {
     int32_t cap_den;
     int32_t renormalize;
     int32_t dtype;
+    int32_t drop_policy;
 } moe_config;
+
+/* Which assignments fill an expert's C slots first when it overflows. */
+typedef enum {
+    /* token order: (t', j') before (t, j) iff t' < t -- the reading of the
+     * TorchTitan 1K-GPU article's "drop the overflow in token order"
+     * (section 2.1) */
+    MOE_DROP_TOKEN_ORDER = 0,
+    /* choice order (GShard-style priority, a variant): every first choice, in
+     * token order, before every second choice, and so on: (t', j') before
+     * (t, j) iff j' < j, or j' == j and t' < t */
+    MOE_DROP_CHOICE_ORDER = 1
+} moe_drop_policy;
 
 /* Host.  Expert capacity C = ceil(cap_num * k * T / (cap_den * E)) in exact
  * integer arithmetic, or T when cap_den == 0.  Returns -1 for an invalid
@@ -128,7 +142,8 @@ moe_status moe_route_from_logits(const moe_config* cfg, const float* logits,
  *   x             [T, d]         dtype  in
  *   x_perm        [max_rows, d]  dtype  out  row r = x[token_of_row[r]]; rows of
  *                                            expert e are offset[e]..offset[e+1)-1,
- *                                            ascending token order inside
+ *                                            in cfg->drop_policy's priority order
+ *                                            (token order: ascending token)
  *   expert_count  [E]            int32  out  assignments per expert before drops
  *   expert_offset [E + 1]        int32  out  exclusive prefix of kept counts
  *                                            min(count, C); [E] = rows kept
@@ -136,12 +151,30 @@ moe_status moe_route_from_logits(const moe_config* cfg, const float* logits,
  *   token_of_row  [T * k]        int32  out  token of each kept row; entries at and
  *                                            past offset[E] are set to -1
  *   workspace     ws_bytes >= moe_workspace_size(cfg, 1, .)
- * An assignment (t, j) to expert e is kept iff fewer than C earlier tokens
- * (t' < t, at any rank) chose e ("drop overflow in token order"). */
+ * An assignment (t, j) to expert e is kept iff fewer than C assignments to e
+ * come before it in cfg->drop_policy's order; with MOE_DROP_TOKEN_ORDER, iff
+ * fewer than C earlier tokens (t' < t, at any rank) chose e ("drop overflow
+ * in token order"). */
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                         void* x_perm, int32_t* expert_count, int32_t* expert_offset,
                         int32_t* row_of, int32_t* token_of_row, void* workspace,
                         size_t ws_bytes, void* stream);
+
+/* Expert-load telemetry from the per-expert assignment counts before drops
+ * (expert_count as written by moe_dispatch).  The ZAYA1 page keeps the expert
+ * load balance within +-5% (section 3.2) and monitors it during training; the
+ * balance figure here is the largest deviation of an expert's load from the
+ * mean, relative to the mean.
+ *   expert_count [E]  int32 in
+ *   stats        [8]  fp64  out  (device)
+ *     [0] mean load m = sum_e count_e / E  [1] max count   [2] min count
+ *     [3] max / m                          [4] max_e |count_e - m| / m
+ *     [5] population std / m               [6] dropped assignments
+ *         sum_e max(0, count_e - C)        [7] experts with no assignment
+ *     (the three ratios are 0 when there are no assignments)
+ * One workgroup; fp64 throughout, so the integers are exact. */
+moe_status moe_load_stats(const moe_config* cfg, const int32_t* expert_count, double* stats,
+                          void* stream);
 
 /* Step 6: grouped GeGLU expert FFN over the permuted rows.
  *   x_perm        [max_rows, d]    dtype in   (rows past expert_offset[E] ignored)

@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
+MOE_DROP_TOKEN_ORDER, MOE_DROP_CHOICE_ORDER = 0, 1
 
 EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_status_string",
            "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_forward")
+           "moe_forward", "moe_load_stats")
 
 
 class CConfig(ctypes.Structure):
@@ -33,7 +34,7 @@ class CConfig(ctypes.Structure):
                 ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("cap_num", ctypes.c_int32),
                 ("cap_den", ctypes.c_int32), ("renormalize", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("drop_policy", ctypes.c_int32)]
 
 
 class MoEError(RuntimeError):
@@ -73,8 +74,10 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_down.argtypes = [cp, _P, _P, _P, _P, _P]
         L.moe_combine.argtypes = [cp, _P, _P, _P, _P, _P]
         L.moe_forward.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_load_stats.argtypes = [cp, _P, _P, _P]
         for n in ("moe_route", "moe_route_from_logits", "moe_dispatch", "moe_expert_ffn",
-                  "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward"):
+                  "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
+                  "moe_load_stats"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -84,7 +87,8 @@ def cconfig(cfg: MoEConfig, T: Optional[int] = None) -> CConfig:
     return CConfig(T=cfg.T if T is None else T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff,
                    temperature=cfg.temperature, cap_num=cfg.cap_num, cap_den=cfg.cap_den,
                    renormalize=int(cfg.renormalize),
-                   dtype=MOE_BF16 if cfg.dtype == "bf16" else MOE_F32)
+                   dtype=MOE_BF16 if cfg.dtype == "bf16" else MOE_F32,
+                   drop_policy=int(cfg.drop_policy))
 
 
 def _check(status: int, where: str) -> None:
@@ -183,6 +187,18 @@ def dispatch(cfg: MoEConfig, topk_idx, x) -> Dict:
            "moe_dispatch")
     out["_workspace"] = ws   # keep alive until the stream has run
     return out
+
+
+def load_stats(cfg: MoEConfig, expert_count):
+    """moe_load_stats -> fp64 [8]: mean, max, min, max/mean, max |count - mean| / mean,
+    std / mean, dropped assignments, empty experts (counts before drops)."""
+    import torch
+    dev = expert_count.device
+    _need(expert_count, "expert_count", torch.int32, (cfg.E,), dev)
+    stats = torch.empty(8, dtype=torch.float64, device=dev)
+    _check(lib().moe_load_stats(ctypes.byref(cconfig(cfg)), _ptr(expert_count), _ptr(stats),
+                                _stream()), "moe_load_stats")
+    return stats
 
 
 def expert_ffn(cfg: MoEConfig, x_perm, expert_offset, w_gate, w_up, w_down) -> Tuple:

@@ -40,6 +40,7 @@ class MoEConfig:
     renormalize: bool    # gates renormalised over the chosen k experts
     dtype: str           # "f32" or "bf16" for activations and weights
     zipf_bias: Optional[float] = None  # Zipf exponent of the router bias, or None for no bias
+    drop_policy: int = 0  # 0: overflow dropped in token order; 1: choice order (first choices first)
 
     def scaled(self, **kw) -> "MoEConfig":
         """A copy with some fields replaced (used to make small test cases)."""

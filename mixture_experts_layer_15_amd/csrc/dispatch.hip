@@ -27,9 +27,24 @@ namespace {
 
 constexpr int kInvalid = 256;   // expert code of an empty / out-of-range slot
 
+// Slot (index into topk_idx / row_of) of choice j of walked token v, and the
+// real token it belongs to.  Token order walks the real tokens (slot v*k + j);
+// choice order walks the Tr*kr single choices v = j'*Tr + t (k = 1), whose
+// slot is t*kr + j'.
+template <bool CM>
+__device__ __forceinline__ int slot_of(int v, int j, int k, int Tr, int kr) {
+    return CM ? (v % Tr) * kr + v / Tr : v * k + j;
+}
+template <bool CM>
+__device__ __forceinline__ int token_of(int v, int Tr) {
+    return CM ? v % Tr : v;
+}
+
+template <bool CM>
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx,
                                                    int32_t* __restrict__ blockcount,
-                                                   long long T, int E, int k, int blk_tokens) {
+                                                   long long T, int E, int k, int blk_tokens,
+                                                   int Tr, int kr) {
     __shared__ int h[256];
     for (int e = threadIdx.x; e < 256; e += 256) h[e] = 0;
     __syncthreads();
@@ -37,7 +52,7 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
     const long long te = min(T, tb + blk_tokens);
     for (long long t = tb + threadIdx.x; t < te; t += 256)
         for (int j = 0; j < k; ++j) {
-            const int e = idx[t * k + j];
+            const int e = idx[slot_of<CM>((int)t, j, k, Tr, kr)];
             if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
         }
     __syncthreads();
@@ -82,10 +97,11 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ b
 // entry, the number of assignments to e by tokens before tb (in LDS); on exit
 // it also counts this chunk's.  offset[] may live in LDS or global memory.
 // All 256 threads call this together.
+template <bool CM>
 __device__ __forceinline__ void place_chunk(const int32_t* __restrict__ idx, int* run,
                                             int (*wcnt)[256], const int32_t* offset, int n_kept,
                                             long long C, long long T, int E, int k, long long tb,
-                                            int32_t* __restrict__ row_of,
+                                            int Tr, int kr, int32_t* __restrict__ row_of,
                                             int32_t* __restrict__ token_of_row) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -99,7 +115,7 @@ __device__ __forceinline__ void place_chunk(const int32_t* __restrict__ idx, int
         code[j] = kInvalid;
         rank[j] = 0;
         if (j < k && valid) {
-            const int e = idx[t * k + j];
+            const int e = idx[slot_of<CM>((int)t, j, k, Tr, kr)];
             if ((unsigned)e < (unsigned)E) code[j] = e;
         }
     }
@@ -137,10 +153,10 @@ __device__ __forceinline__ void place_chunk(const int32_t* __restrict__ idx, int
                 for (int i = 0; i < w; ++i) pos += wcnt[i][e];
                 if (pos < C) {
                     row = offset[e] + pos;
-                    token_of_row[row] = (int32_t)t;
+                    token_of_row[row] = token_of<CM>((int)t, Tr);
                 }
             }
-            row_of[a] = row;
+            row_of[slot_of<CM>((int)t, j, k, Tr, kr)] = row;
             // every slot index a >= rows kept is past the kept rows: mark it empty
             if (a >= n_kept) token_of_row[a] = -1;
         }
@@ -150,10 +166,12 @@ __device__ __forceinline__ void place_chunk(const int32_t* __restrict__ idx, int
     __syncthreads();
 }
 
+template <bool CM>
 __global__ __launch_bounds__(256) void place_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ blockbase,
     const int32_t* __restrict__ offset, long long C, long long T, int E, int k,
-    int blk_tokens, int32_t* __restrict__ row_of, int32_t* __restrict__ token_of_row) {
+    int blk_tokens, int Tr, int kr, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ token_of_row) {
     __shared__ int run[256];
     __shared__ int wcnt[4][256];
     for (int e = threadIdx.x; e < 256; e += 256)
@@ -161,7 +179,8 @@ __global__ __launch_bounds__(256) void place_kernel(
     const int n_kept = offset[E];
     const long long tb = (long long)blockIdx.x * blk_tokens;
     for (int c = 0; c < blk_tokens; c += 256)
-        place_chunk(idx, run, wcnt, offset, n_kept, C, T, E, k, tb + c, row_of, token_of_row);
+        place_chunk<CM>(idx, run, wcnt, offset, n_kept, C, T, E, k, tb + c, Tr, kr, row_of,
+                        token_of_row);
 }
 
 // Small batches (T*k <= kSmallAssign): histogram, capacity, offsets and
@@ -171,8 +190,9 @@ __global__ __launch_bounds__(256) void place_kernel(
 // another; workgroup 0 publishes count[] and offset[].
 constexpr long long kSmallAssign = 16384;
 
+template <bool CM>
 __global__ __launch_bounds__(256) void dispatch_small_kernel(
-    const int32_t* __restrict__ idx, long long C, long long T, int E, int k,
+    const int32_t* __restrict__ idx, long long C, long long T, int E, int k, int Tr, int kr,
     int32_t* __restrict__ count, int32_t* __restrict__ offset_out,
     int32_t* __restrict__ row_of, int32_t* __restrict__ token_of_row) {
     __shared__ int h_all[256], run[256];
@@ -186,7 +206,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     const long long tb = (long long)blockIdx.x * 256;
     const long long n_assign = T * k, pre = tb * k;
     for (long long a = tid; a < n_assign; a += 256) {
-        const int e = idx[a];
+        const int e = idx[CM ? slot_of<CM>((int)a, 0, 1, Tr, kr) : a];
         if ((unsigned)e < (unsigned)E) {
             atomicAdd(&h_all[e], 1);
             if (a < pre) atomicAdd(&run[e], 1);
@@ -215,7 +235,8 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
         if (e == E - 1) offset_out[E] = incl;
     }
     __syncthreads();
-    place_chunk(idx, run, wcnt, s_off, s_off[E], C, T, E, k, tb, row_of, token_of_row);
+    place_chunk<CM>(idx, run, wcnt, s_off, s_off[E], C, T, E, k, tb, Tr, kr, row_of,
+                    token_of_row);
 }
 
 // One wave per token: copy x[t] to each kept row (16-byte vectors).
@@ -253,11 +274,15 @@ __global__ __launch_bounds__(256) void scatter_kernel(const u32x4* __restrict__ 
 
 }  // namespace
 
-DispatchPlan plan_dispatch(long long T, int E, int k, long long C) {
+DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy) {
     DispatchPlan p;
-    p.T = T;
+    p.Tr = T;
+    p.kr = k;
+    p.choice_order = policy == 1 && k > 1;   // with one choice the orders coincide
+    p.T = p.choice_order ? T * k : T;
+    p.k = p.choice_order ? 1 : k;
+    T = p.T;
     p.E = E;
-    p.k = k;
     p.C = C;
     const long long chunks = (T + 255) / 256;            // 256-token chunks
     const long long per_blk = (chunks + 255) / 256;      // chunks per block, so nblk <= 256
@@ -270,25 +295,24 @@ size_t dispatch_workspace_bytes(const DispatchPlan& p) {
     return (size_t)2 * (size_t)std::max(p.nblk, 1) * (size_t)p.E * sizeof(int32_t);
 }
 
-hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx, const void* x,
-                           void* x_perm, int32_t* count, int32_t* offset, int32_t* row_of,
-                           int32_t* token_of_row, void* workspace, int d, hipStream_t s,
-                           bool scatter) {
-    const int nvec = d * (dtype == 1 ? 2 : 4) / 16;
+namespace {
+
+template <bool CM>
+hipError_t dispatch_kernels(const DispatchPlan& p, const int32_t* idx, int32_t* count,
+                            int32_t* offset, int32_t* row_of, int32_t* token_of_row,
+                            void* workspace, hipStream_t s) {
+    const int Tr = (int)p.Tr, kr = p.kr;
     if (p.T > 0 && p.T * p.k <= kSmallAssign) {
-        hipLaunchKernelGGL(dispatch_small_kernel, dim3((unsigned)((p.T + 255) / 256)), dim3(256), 0,
-                           s, idx, p.C, p.T, p.E, p.k, count, offset, row_of, token_of_row);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess || !scatter) return err;
-        hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((p.T + 3) / 4)), dim3(256), 0, s,
-                           (const u32x4*)x, row_of, (u32x4*)x_perm, p.T, nvec, p.k);
+        hipLaunchKernelGGL(dispatch_small_kernel<CM>, dim3((unsigned)((p.T + 255) / 256)),
+                           dim3(256), 0, s, idx, p.C, p.T, p.E, p.k, Tr, kr, count, offset,
+                           row_of, token_of_row);
         return hipGetLastError();
     }
     int32_t* blockcount = (int32_t*)workspace;
     int32_t* blockbase = blockcount + (size_t)std::max(p.nblk, 1) * p.E;
     if (p.nblk > 0) {
-        hipLaunchKernelGGL(hist_kernel, dim3(p.nblk), dim3(256), 0, s, idx, blockcount, p.T,
-                           p.E, p.k, p.blk_tokens);
+        hipLaunchKernelGGL(hist_kernel<CM>, dim3(p.nblk), dim3(256), 0, s, idx, blockcount, p.T,
+                           p.E, p.k, p.blk_tokens, Tr, kr);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -296,12 +320,80 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
                        p.E, p.C, count, offset);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || p.nblk == 0) return err;
-    hipLaunchKernelGGL(place_kernel, dim3(p.nblk), dim3(256), 0, s, idx, blockbase, offset, p.C,
-                       p.T, p.E, p.k, p.blk_tokens, row_of, token_of_row);
-    err = hipGetLastError();
-    if (err != hipSuccess || !scatter) return err;
-    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((p.T + 3) / 4)), dim3(256), 0, s,
-                       (const u32x4*)x, row_of, (u32x4*)x_perm, p.T, nvec, p.k);
+    hipLaunchKernelGGL(place_kernel<CM>, dim3(p.nblk), dim3(256), 0, s, idx, blockbase, offset,
+                       p.C, p.T, p.E, p.k, p.blk_tokens, Tr, kr, row_of, token_of_row);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx, const void* x,
+                           void* x_perm, int32_t* count, int32_t* offset, int32_t* row_of,
+                           int32_t* token_of_row, void* workspace, int d, hipStream_t s,
+                           bool scatter) {
+    hipError_t err = p.choice_order
+        ? dispatch_kernels<true>(p, idx, count, offset, row_of, token_of_row, workspace, s)
+        : dispatch_kernels<false>(p, idx, count, offset, row_of, token_of_row, workspace, s);
+    if (err != hipSuccess || !scatter || p.Tr == 0) return err;
+    const int nvec = d * (dtype == 1 ? 2 : 4) / 16;
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((p.Tr + 3) / 4)), dim3(256), 0, s,
+                       (const u32x4*)x, row_of, (u32x4*)x_perm, p.Tr, nvec, p.kr);
+    return hipGetLastError();
+}
+
+// Expert-load telemetry: one workgroup, fp64.  stats as documented in moe.h.
+__global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restrict__ count,
+                                                         int E, long long C,
+                                                         double* __restrict__ stats) {
+    __shared__ double s_sum[4], s_max[4], s_min[4], s_drop[4], s_empty[4], s_dev[4], s_ss[4];
+    const int e = threadIdx.x, lane = e & 63, w = e >> 6;
+    const bool ok = e < E;
+    const double c = ok ? (double)count[e] : 0.0;
+    auto wave_sum = [](double v) {
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+        return v;
+    };
+    auto wave_max = [](double v) {
+        for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+        return v;
+    };
+    const double sum = wave_sum(c);
+    const double mx = wave_max(ok ? c : -1.0);
+    const double mn = -wave_max(ok ? -c : -1e300);
+    const double drop = wave_sum(ok && c > (double)C ? c - (double)C : 0.0);
+    const double empty = wave_sum(ok && c == 0.0 ? 1.0 : 0.0);
+    if (lane == 0) { s_sum[w] = sum; s_max[w] = mx; s_min[w] = mn; s_drop[w] = drop; s_empty[w] = empty; }
+    __syncthreads();
+    // fixed order over the four waves: the same sums on every run
+    const double tot = ((s_sum[0] + s_sum[1]) + s_sum[2]) + s_sum[3];
+    const double m = tot / (double)E;
+    const double diff = ok ? c - m : 0.0;
+    const double dev = wave_max(diff < 0 ? -diff : diff);
+    const double ss = wave_sum(diff * diff);
+    if (lane == 0) { s_dev[w] = dev; s_ss[w] = ss; }
+    __syncthreads();
+    if (e == 0) {
+        double gmax = s_max[0], gmin = s_min[0], gdev = s_dev[0];
+        for (int i = 1; i < 4; ++i) {
+            gmax = fmax(gmax, s_max[i]);
+            gmin = fmin(gmin, s_min[i]);
+            gdev = fmax(gdev, s_dev[i]);
+        }
+        const double gss = ((s_ss[0] + s_ss[1]) + s_ss[2]) + s_ss[3];
+        stats[0] = m;
+        stats[1] = gmax;
+        stats[2] = gmin;
+        stats[3] = m > 0 ? gmax / m : 0.0;
+        stats[4] = m > 0 ? gdev / m : 0.0;
+        stats[5] = m > 0 ? sqrt(gss / (double)E) / m : 0.0;
+        stats[6] = ((s_drop[0] + s_drop[1]) + s_drop[2]) + s_drop[3];
+        stats[7] = ((s_empty[0] + s_empty[1]) + s_empty[2]) + s_empty[3];
+    }
+}
+
+hipError_t launch_load_stats(const int32_t* count, int E, long long C, double* stats,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(load_stats_kernel, dim3(1), dim3(256), 0, s, count, E, C, stats);
     return hipGetLastError();
 }
 

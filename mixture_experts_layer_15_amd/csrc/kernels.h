@@ -21,13 +21,19 @@ hipError_t launch_route_from_logits(const float* logits, int32_t* idx, float* ga
 
 // Dispatch.  Tokens are cut into nblk blocks of blk_tokens (a multiple of 256)
 // with nblk <= 256; workspace holds two [nblk][E] int32 tables.
+// The kernels walk "tokens" of k choices each.  In token order those are the
+// real tokens; in choice order they are the T*k single choices in (choice,
+// token) order (T = Tr * kr, k = 1), mapped back to the real slots.
 struct DispatchPlan {
-    long long T;
-    int E, k;
+    long long T;           // tokens the kernels walk
+    int E, k;              // experts; choices per walked token
     long long C;
     int blk_tokens, nblk;
+    long long Tr;          // real tokens
+    int kr;                // real choices per token
+    bool choice_order;
 };
-DispatchPlan plan_dispatch(long long T, int E, int k, long long C);
+DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy = 0);
 size_t dispatch_workspace_bytes(const DispatchPlan& p);
 // scatter = false leaves x_perm unwritten (for a consumer that gathers rows of
 // x through token_of_row itself).
@@ -35,6 +41,10 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
                            void* x_perm, int32_t* count, int32_t* offset, int32_t* row_of,
                            int32_t* token_of_row, void* workspace, int d, hipStream_t s,
                            bool scatter = true);
+
+// Expert-load telemetry (8 fp64 values, see moe_load_stats).
+hipError_t launch_load_stats(const int32_t* count, int E, long long C, double* stats,
+                             hipStream_t s);
 
 // Grouped GeGLU expert FFN (gate/up GEMM with fused epilogue, then down GEMM).
 hipError_t launch_expert_ffn(int dtype, const void* x_perm, const int32_t* off,

@@ -75,6 +75,8 @@ moe_status check_cfg(const moe_config* c) {
         return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1");
     if (c->dtype != MOE_F32 && c->dtype != MOE_BF16)
         return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
+    if (c->drop_policy != MOE_DROP_TOKEN_ORDER && c->drop_policy != MOE_DROP_CHOICE_ORDER)
+        return fail(MOE_ERR_INVALID_ARG, "drop_policy %d is not a moe_drop_policy", c->drop_policy);
     return MOE_OK;
 }
 
@@ -127,7 +129,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 FwdLayout fwd_layout(const moe_config* c) {
     const size_t T = (size_t)c->T, E = (size_t)c->E, k = (size_t)c->k;
     const size_t R = (size_t)max_rows(c);
-    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c));
+    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy);
     FwdLayout L;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -165,7 +167,7 @@ moe_status moe_workspace_size(const moe_config* cfg, int dispatch_only, size_t* 
     if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
     if (dispatch_only) {
         *bytes = moe::dispatch_workspace_bytes(
-            moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg)));
+            moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy));
     } else {
         *bytes = fwd_layout(cfg).total;
     }
@@ -230,7 +232,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const vo
     CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
     CHECK(check_ptr(row_of, "row_of", T * k * 4));
     CHECK(check_ptr(token_of_row, "token_of_row", T * k * 4));
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg));
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy);
     const size_t need = moe::dispatch_workspace_bytes(p);
     if (workspace == nullptr || ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "dispatch workspace: need %zu bytes, got %zu", need, ws_bytes);
@@ -304,6 +306,19 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine");
 }
 
+moe_status moe_load_stats(const moe_config* cfg, const int32_t* expert_count, double* stats,
+                          void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    if (expert_count == nullptr) return fail(MOE_ERR_INVALID_ARG, "expert_count is NULL");
+    CHECK(check_ptr(expert_count, "expert_count", E * 4));
+    if (stats == nullptr) return fail(MOE_ERR_INVALID_ARG, "stats is NULL");
+    CHECK(check_ptr(stats, "stats", 8 * sizeof(double)));
+    hipError_t e = moe::launch_load_stats(expert_count, cfg->E, capacity_eff(cfg), stats,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_load_stats");
+}
+
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* bias, const void* w_gate, const void* w_up,
                        const void* w_down, void* y, void* workspace, size_t ws_bytes,
@@ -336,7 +351,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     // bf16: the gate/up GEMM gathers its rows of x through token_of_row, so
     // x_perm is never written (its 32-bit byte offsets must span x)
     const bool gather = cfg->dtype == MOE_BF16 && T * d * es < ((size_t)1 << 32);
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg));
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy);
     e = moe::launch_dispatch(p, cfg->dtype, idx, x, w + L.x_perm, count, offset, row_of, tor,
                              w + L.dsp, cfg->d, s, !gather);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/dispatch");

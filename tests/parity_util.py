@@ -89,7 +89,7 @@ def check_route(cfg, logits_gpu, idx_gpu, gate_gpu):
 def check_dispatch(cfg, oidx, dsp):
     """Integer outputs of dispatch bit-exact against the oracle."""
     C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
-    od = orc.dispatch(oidx, cfg.E, C)
+    od = orc.dispatch(oidx, cfg.E, C, cfg.drop_policy)
     n = od["n_kept"]
     np.testing.assert_array_equal(dsp["expert_count"].cpu().numpy(), od["count"])
     np.testing.assert_array_equal(dsp["expert_offset"].cpu().numpy(), od["offset"])

@@ -74,7 +74,8 @@ BAD = [
     (dict(T=1 << 30, k=2, E=4), "T * k"), (dict(temperature=0.0), "temperature"),
     (dict(temperature=-1.0), "temperature"), (dict(temperature=float("inf")), "temperature"),
     (dict(temperature=float("nan")), "temperature"), (dict(cap_num=-1, cap_den=4), "capacity"),
-    (dict(cap_den=-1), "capacity"),
+    (dict(cap_den=-1), "capacity"), (dict(drop_policy=2), "drop_policy"),
+    (dict(drop_policy=-1), "drop_policy"),
 ]
 
 
@@ -113,6 +114,25 @@ def test_null_and_misaligned_pointers_rejected(L):
     assert L.moe_combine(ctypes.byref(c), ok, ok, ok, None, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_expert_ffn(ctypes.byref(c), ok, None, ok, ok, ok, ok, ok, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_route_from_logits(ctypes.byref(c), ok, ok, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_load_stats(ctypes.byref(c), None, ok, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"expert_count is NULL" in L.moe_last_error()
+    assert L.moe_load_stats(ctypes.byref(c), ok, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_load_stats(ctypes.byref(c), ok, odd, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_choice_order_workspace_is_sized_for_the_walked_choices(L):
+    # the dispatch tables hold 2 * nblk * E int32, nblk <= 256 blocks of whole
+    # 256-token chunks over the walked tokens: T in token order, T*k single
+    # choices in choice order
+    def want(walked, E):
+        chunks = -(-walked // 256)
+        blk = max(-(-chunks // 256), 1) * 256
+        return 2 * max(-(-walked // blk), 1) * E * 4
+    for name in ("wide", "skewed", "longseq"):
+        cfg = configs.get(name)
+        assert moe.workspace_bytes(cfg, dispatch_only=True) == want(cfg.T, cfg.E)
+        assert moe.workspace_bytes(cfg.scaled(drop_policy=1), dispatch_only=True) == \
+            want(cfg.T * cfg.k, cfg.E)
 
 
 def test_workspace_too_small_rejected(L):

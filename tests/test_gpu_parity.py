@@ -81,6 +81,7 @@ def run_layer(cfg, dev, host, full, seed=0, label=""):
                           host["w_up"], host["w_down"], k=cfg.k,
                           tau=float(np.float32(cfg.temperature)), renormalize=cfg.renormalize,
                           cap_num=cfg.cap_num, cap_den=cfg.cap_den,
+                          drop_policy=cfg.drop_policy,
                           logits_in=lg_h.double().numpy(), tokens=stoks)
         ey = rel_err(to_np(y[torch.from_numpy(stoks).cuda()]), ofw["y"])
         say(f"[{label}] y err {ey:.3g} over {stoks.size} tokens")

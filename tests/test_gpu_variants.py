@@ -1,0 +1,87 @@
+"""GPU parity of the routing variants against the fp64 oracle, through the C ABI:
+the choice-order drop priority (every first choice before every second
+choice) and the expert-load telemetry.  Integer outputs bit-exact; the layer
+output within the same tolerance as the main parity tests."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_15_amd as moe
+from mixture_experts_layer_15_amd import configs
+from oracle import oracle as orc
+
+from parity_util import gpu_inputs, say
+from test_gpu_parity import run_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+SMALL = configs.get("tiny").scaled(dtype="bf16", temperature=0.3, renormalize=True,
+                                   cap_num=5, cap_den=4, drop_policy=1)
+CHOICE_CASES = {
+    # one-launch dispatch (T*k <= 16384), every output compared
+    "choice_small": SMALL.scaled(T=1500, d=128, E=12, k=3, d_ff=192),
+    # hot expert: Zipf bias, most assignments dropped
+    "choice_hot": SMALL.scaled(T=3000, d=128, E=16, k=2, d_ff=128, zipf_bias=1.2),
+    # multi-block histogram / scan / place path
+    "choice_blocks": SMALL.scaled(T=20000, d=128, E=64, k=2, d_ff=128),
+}
+
+
+@pytest.mark.parametrize("name", list(CHOICE_CASES))
+def test_choice_order_layer(name):
+    cfg = CHOICE_CASES[name]
+    dev, host = gpu_inputs(cfg, seed=3)
+    run_layer(cfg, dev, host, full=cfg.T <= 3000, seed=3, label=name)
+
+
+def test_choice_order_full_size_skewed():
+    cfg = configs.get("skewed").scaled(drop_policy=1)
+    dev, host = gpu_inputs(cfg, seed=0)
+    out = run_layer(cfg, dev, host, full=False, seed=0, label="skewed/choice")
+    # the two priorities keep different assignment sets on this layer
+    C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    tok = orc.dispatch(out["idx"].cpu().numpy(), cfg.E, C, 0)
+    cho = orc.dispatch(out["idx"].cpu().numpy(), cfg.E, C, 1)
+    say(f"[skewed/choice] kept {cho['n_kept']} (token order {tok['n_kept']}), "
+        f"assignments kept by one order only: "
+        f"{int(((tok['row_of'] >= 0) != (cho['row_of'] >= 0)).sum())}")
+    assert ((tok["row_of"] >= 0) != (cho["row_of"] >= 0)).any()
+
+
+@pytest.mark.parametrize("name,policy", [("zaya1", 0), ("skewed", 0), ("skewed", 1), ("wide", 0)])
+def test_load_stats_match_oracle(name, policy):
+    cfg = configs.get(name).scaled(drop_policy=policy)
+    dev, _ = gpu_inputs(cfg, seed=0)
+    _, idx, _ = moe.route(cfg, dev["x"], dev["w_router"], dev["bias"])
+    dsp = moe.dispatch(cfg, idx, dev["x"])
+    st = moe.load_stats(cfg, dsp["expert_count"])
+    torch.cuda.synchronize()
+    got = st.cpu().numpy()
+    C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    want = orc.load_stats(dsp["expert_count"].cpu().numpy(), C)
+    say(f"[{name}/{policy}] load: mean {want[0]:.1f} max/mean {want[3]:.3f} "
+        f"max deviation {100 * want[4]:.1f}% CV {want[5]:.3f} dropped {int(want[6])} "
+        f"empty {int(want[7])}")
+    # counts, sums and the max/min-based ratios are exact in fp64; the CV sums
+    # its squares in another order
+    np.testing.assert_array_equal(got[[0, 1, 2, 3, 4, 6, 7]], want[[0, 1, 2, 3, 4, 6, 7]])
+    assert abs(got[5] - want[5]) <= 1e-12 * max(1.0, abs(want[5]))
+
+
+def test_load_stats_edge_counts():
+    cfg = configs.get("tiny").scaled(E=256, k=1, cap_num=1, cap_den=2)
+    for counts in (np.zeros(256, np.int32), np.r_[np.full(255, 0), 777].astype(np.int32),
+                   np.arange(256, dtype=np.int32)):
+        st = moe.load_stats(cfg, torch.from_numpy(counts).cuda())
+        torch.cuda.synchronize()
+        C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+        want = orc.load_stats(counts, C)
+        np.testing.assert_allclose(st.cpu().numpy(), want, rtol=1e-12, atol=0)
