@@ -247,6 +247,7 @@ def main():
     # up to token order; recompute from the first batch for exactness)
     step(xs[0])
     torch.cuda.synchronize()
+    ls = moe.load_stats(cfg, count).cpu().numpy()   # expert-load telemetry of this batch
     cnt = count.cpu().numpy()
     off = offset.cpu().numpy()
     n_kept = int(off[-1])
@@ -285,6 +286,10 @@ def main():
                    "temperature": cfg.temperature,
                    "capacity_factor": None if cfg.cap_den == 0 else cfg.cap_num / cfg.cap_den,
                    "rows_kept": n_kept, "parallelism": "single GPU"},
+        "expert_load": {"mean": round(float(ls[0]), 2), "max": int(ls[1]), "min": int(ls[2]),
+                        "max_over_mean": round(float(ls[3]), 4),
+                        "max_deviation": round(float(ls[4]), 4), "cv": round(float(ls[5]), 4),
+                        "dropped": int(ls[6]), "empty_experts": int(ls[7])},
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
