@@ -74,6 +74,74 @@ void orc_logits(int64_t T, int64_t d, int64_t E, int dtype, const void* x,
     }
 }
 
+/* Variant of step 1 -- ZAYA1's MLP router ("AMD MI300X平台上的MoE模型训练实践",
+ * section 3.2), forward, per token:
+ *   u  = x Wd + bd                          down-projection to r (256 there)
+ *   v  = u + gamma * prev                   depth averaging with the previous
+ *                                           layer's router state (prev may be NULL)
+ *   z  = v / sqrt(sum_j v_j^2 / r + eps)    RMS norm without a learned scale
+ *   h1 = GELU(z W1 + b1), h2 = GELU(h1 W2 + b2)   two layers m wide (1024 there)
+ *   l  = h2 W3 + b3 + pid                   pid: the load-balance controller's
+ *                                           per-expert bias on the logits
+ * Wd [d][r], W1 [r][m], W2 [m][m], W3 [m][E] row-major in dtype; prev [T][r]
+ * in dtype; biases fp32, each may be NULL (zero).  The page leaves gamma, eps
+ * and the controller's update rule open: gamma and eps are parameters and the
+ * controller enters only through its output, pid.  z, h1, h2 may be NULL. */
+void orc_mlp_router(int64_t T, int64_t d, int64_t r, int64_t m, int64_t E, int dtype,
+                    const void* x, const void* prev, double gamma, double eps,
+                    const void* wd, const float* bd, const void* w1, const float* b1,
+                    const void* w2, const float* b2, const void* w3, const float* b3,
+                    const float* pid, double* logits, double* z_out, double* h1_out,
+                    double* h2_out) {
+    #pragma omp parallel
+    {
+        double* v = (double*)malloc(sizeof(double) * (size_t)r);
+        double* a = (double*)malloc(sizeof(double) * (size_t)m);
+        double* b = (double*)malloc(sizeof(double) * (size_t)m);
+        #pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int64_t j = 0; j < r; ++j) {
+                double s = 0.0;
+                for (int64_t i = 0; i < d; ++i) s += load(x, t * d + i, dtype) * load(wd, i * r + j, dtype);
+                if (bd) s += (double)bd[j];
+                if (prev) s += gamma * load(prev, t * r + j, dtype);
+                v[j] = s;
+            }
+            double ss = 0.0;
+            for (int64_t j = 0; j < r; ++j) ss += v[j] * v[j];
+            double inv = 1.0 / sqrt(ss / (double)r + eps);
+            for (int64_t j = 0; j < r; ++j) {
+                v[j] *= inv;
+                if (z_out) z_out[t * r + j] = v[j];
+            }
+            for (int64_t n = 0; n < m; ++n) {
+                double s = 0.0;
+                for (int64_t j = 0; j < r; ++j) s += v[j] * load(w1, j * m + n, dtype);
+                if (b1) s += (double)b1[n];
+                a[n] = gelu(s);
+                if (h1_out) h1_out[t * m + n] = a[n];
+            }
+            for (int64_t n = 0; n < m; ++n) {
+                double s = 0.0;
+                for (int64_t j = 0; j < m; ++j) s += a[j] * load(w2, j * m + n, dtype);
+                if (b2) s += (double)b2[n];
+                b[n] = gelu(s);
+                if (h2_out) h2_out[t * m + n] = b[n];
+            }
+            for (int64_t e = 0; e < E; ++e) {
+                double s = 0.0;
+                for (int64_t j = 0; j < m; ++j) s += b[j] * load(w3, j * E + e, dtype);
+                if (b3) s += (double)b3[e];
+                if (pid) s += (double)pid[e];
+                logits[t * E + e] = s;
+            }
+        }
+        free(v);
+        free(a);
+        free(b);
+    }
+}
+
 /* Step 2 -- top-k expert choice and gate weights, per token.
  * Experts are ranked by their logit (largest first); equal logits rank the
  * lower expert index first.  The ranking uses the logits themselves, never

@@ -66,6 +66,9 @@ def _declare(lib):
     lib.orc_dispatch.restype = None
     lib.orc_load_stats.argtypes = [_I64, _P, _I64, _P]
     lib.orc_load_stats.restype = None
+    lib.orc_mlp_router.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int, _P, _P,
+                                   ctypes.c_double, ctypes.c_double] + [_P] * 13
+    lib.orc_mlp_router.restype = None
     lib.orc_ffn_rows.argtypes = [_I64, _P, _P, _I64, _I64, ctypes.c_int,
                                  _P, _P, _P, _P, _P, _P]
     lib.orc_ffn_rows.restype = None
@@ -182,6 +185,34 @@ def combine(tokens: Sequence[int], row_of: np.ndarray, gate: np.ndarray,
         _load().orc_combine(toks.shape[0], _ptr(toks), k, d, _ptr(row_of), _ptr(gate),
                             _ptr(o_slots), _ptr(y))
     return y
+
+
+def _f32_or_none(b):
+    return None if b is None else np.ascontiguousarray(_raw(b)[0], dtype=np.float32)
+
+
+def mlp_router(x, prev, gamma: float, eps: float, wd, bd, w1, b1, w2, b2, w3, b3, pid,
+               want_hidden: bool = False) -> Dict[str, np.ndarray]:
+    """The MLP router's logits (and, if asked, z, h1, h2) in fp64; inputs as
+    torch tensors of one dtype (bf16 or fp32), biases fp32 or None."""
+    xr, dt = _raw(x)
+    T, d = xr.shape
+    wdr, _ = _raw(wd)
+    w1r, _ = _raw(w1)
+    w2r, _ = _raw(w2)
+    w3r, _ = _raw(w3)
+    r, m, E = wdr.shape[1], w1r.shape[1], w3r.shape[1]
+    prr = None if prev is None else _raw(prev)[0]
+    bs = [_f32_or_none(b) for b in (bd, b1, b2, b3, pid)]
+    lg = np.empty((T, E), dtype=np.float64)
+    z = np.empty((T, r)) if want_hidden else None
+    h1 = np.empty((T, m)) if want_hidden else None
+    h2 = np.empty((T, m)) if want_hidden else None
+    _load().orc_mlp_router(T, d, r, m, E, dt, _ptr(xr), _ptr(prr), float(gamma), float(eps),
+                           _ptr(wdr), _ptr(bs[0]), _ptr(w1r), _ptr(bs[1]), _ptr(w2r), _ptr(bs[2]),
+                           _ptr(w3r), _ptr(bs[3]), _ptr(bs[4]), _ptr(lg), _ptr(z), _ptr(h1),
+                           _ptr(h2))
+    return dict(logits=lg, z=z, h1=h1, h2=h2)
 
 
 def load_stats(count: np.ndarray, C: int) -> np.ndarray:

@@ -40,6 +40,14 @@ MUTANTS = {
     "load CV with E - 1": ("sqrt(ss / (double)E)", "sqrt(ss / (double)(E - 1))"),
     "mean load over busy experts": ("double m = sum / (double)E;",
                                     "double m = sum / (double)(E - empty);"),
+    "MLP router W1 transposed": ("s += v[j] * load(w1, j * m + n, dtype);",
+                                 "s += v[j] * load(w1, n * r + j, dtype);"),
+    "RMS norm over the sum": ("double inv = 1.0 / sqrt(ss / (double)r + eps);",
+                              "double inv = 1.0 / sqrt(ss + eps);"),
+    "depth average subtracted": ("if (prev) s += gamma * load(prev, t * r + j, dtype);",
+                                 "if (prev) s -= gamma * load(prev, t * r + j, dtype);"),
+    "no GELU on the second layer": ("b[n] = gelu(s);", "b[n] = s;"),
+    "router output bias dropped": ("if (b3) s += (double)b3[e];", "if (0) s += (double)b3[e];"),
     "tanh GELU": ("0.5 * v * (1.0 + erf(v / sqrt(2.0)))",
                   "0.5 * v * (1.0 + tanh(0.7978845608028654 * (v + 0.044715 * v * v * v)))"),
     "GELU on the up branch": ("g[n] = gelu(g[n]) * u[n];", "g[n] = g[n] * gelu(u[n]);"),

@@ -277,6 +277,106 @@ def test_load_stats_deviation_is_largest_either_side():
     assert s[0] == 8.0 and s[4] == 6.0 / 8.0 and s[3] == 10.0 / 8.0
 
 
+# ---------------------------------------------------------------- MLP router (variant)
+
+def _gelu(v):
+    return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+
+
+def _mlp_shapes(T=6, d=64, r=16, m=24, E=5):
+    z = lambda *sh: torch.zeros(sh)
+    return T, d, r, m, E, z
+
+
+def test_mlp_router_zero_hidden_weights_give_output_biases():
+    T, d, r, m, E, z = _mlp_shapes()
+    x = _rand((T, d), 1)
+    b3 = _rand((E,), 2)
+    pid = _rand((E,), 3)
+    out = orc.mlp_router(x, _rand((T, r), 4), 0.7, 1e-6, _rand((d, r), 5), _rand((r,), 6),
+                         z(r, m), None, z(m, m), None, _rand((m, E), 7), b3, pid)
+    want = (b3.double() + pid.double()).numpy()    # GELU(0) = 0 ends every path before W3
+    np.testing.assert_array_equal(out["logits"], np.tile(want, (T, 1)))
+
+
+def test_mlp_router_single_path_chain():
+    # one nonzero weight per matrix: x[i0] -> u[j0] -> h1[n0] -> h2[n1] -> l[e0];
+    # non-square widths so that any transposed index lands elsewhere
+    T, d, r, m, E, z = _mlp_shapes()
+    i0, j0, n0, n1, e0 = 5, 3, 7, 11, 2
+    a, b, c, w = (float(np.float32(v)) for v in (0.8, 1.3, -0.9, 2.1))   # as stored (fp32)
+    x = _rand((T, d), 11)
+    wd, w1, w2, w3 = z(d, r), z(r, m), z(m, m), z(m, E)
+    wd[i0, j0], w1[j0, n0], w2[n0, n1], w3[n1, e0] = a, b, c, w
+    out = orc.mlp_router(x, None, 0.0, 1e-3, wd, None, w1, None, w2, None, w3, None, None,
+                         want_hidden=True)
+    v = a * x[:, i0].double().numpy()
+    zz = v / np.sqrt(v * v / r + 1e-3)
+    want = np.zeros((T, E))
+    want[:, e0] = w * _gelu(c * _gelu(b * zz))
+    np.testing.assert_allclose(out["logits"], want, rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(out["z"][:, j0], zz, rtol=1e-15)
+    assert (np.delete(out["z"], j0, axis=1) == 0).all()
+
+
+def test_mlp_router_rms_norm_closed_form_and_depth_average():
+    # u = 0.5 on every coordinate plus gamma * prev: z = v / sqrt(mean v^2 + eps)
+    T, d, r, m, E, z = _mlp_shapes(T=3, d=64, r=4, m=8, E=3)
+    x = torch.zeros((T, d))
+    x[:, 0] = 1.0
+    wd = torch.zeros((d, r))
+    wd[0, :] = 0.5
+    prev = torch.tensor([[1.0, -1.0, 2.0, 0.0], [0.0, 0.0, 0.0, 0.0], [4.0, 4.0, 4.0, 4.0]])
+    gamma, eps = 0.25, 0.0625
+    out = orc.mlp_router(x, prev, gamma, eps, wd, None, z(r, m), None, z(m, m), None,
+                         z(m, E), None, None, want_hidden=True)
+    v = 0.5 + gamma * prev.double().numpy()
+    want = v / np.sqrt((v * v).mean(1, keepdims=True) + eps)
+    np.testing.assert_allclose(out["z"], want, rtol=1e-15)
+    # row 1: v = 0.5 everywhere -> z = 0.5 / sqrt(0.25 + 0.0625) = 0.894427...
+    assert abs(out["z"][1, 0] - 0.5 / np.sqrt(0.3125)) < 1e-15
+
+
+def test_mlp_router_scale_invariance_without_eps():
+    T, d, r, m, E, z = _mlp_shapes()
+    x, prev = _rand((T, d), 21), _rand((T, r), 22)
+    ws = [_rand((d, r), 23, d ** -0.5), _rand((r,), 24), _rand((r, m), 25, r ** -0.5),
+          _rand((m,), 26), _rand((m, m), 27, m ** -0.5), _rand((m,), 28),
+          _rand((m, E), 29, m ** -0.5), _rand((E,), 30)]
+    a = orc.mlp_router(x, prev, 0.6, 0.0, ws[0], ws[1], *ws[2:], None)["logits"]
+    # scaling x, bd and prev by 4 (exact in fp32) scales v by 4; the norm removes it
+    b = orc.mlp_router(x * 4, prev * 4, 0.6, 0.0, ws[0], ws[1] * 4, *ws[2:], None)["logits"]
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_mlp_router_identity_layers_and_biases():
+    # W1 = [I | 0] (r < m) and W2 = I: h1 = GELU(z + b1) on the first r units, GELU(b1) on
+    # the rest; h2 = GELU(h1 + b2)
+    T, d, r, m, E, z = _mlp_shapes(T=4, d=64, r=8, m=12, E=3)
+    x = _rand((T, d), 31)
+    w1 = z(r, m)
+    w1[:, :r] = torch.eye(r)
+    b1, b2 = _rand((m,), 32), _rand((m,), 33)
+    out = orc.mlp_router(x, None, 0.0, 1e-6, _rand((d, r), 34, d ** -0.5), None, w1, b1,
+                         torch.eye(m), b2, _rand((m, E), 35), None, None, want_hidden=True)
+    zz = out["z"]
+    pre1 = np.concatenate([zz, np.zeros((T, m - r))], 1) + b1.double().numpy()
+    np.testing.assert_allclose(out["h1"], _gelu(pre1), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(out["h2"], _gelu(out["h1"] + b2.double().numpy()), rtol=1e-14,
+                               atol=1e-300)
+
+
+def test_mlp_router_expert_permutation():
+    T, d, r, m, E, z = _mlp_shapes()
+    args = [_rand((T, d), 41), _rand((T, r), 42), 0.3, 1e-6, _rand((d, r), 43), _rand((r,), 44),
+            _rand((r, m), 45), _rand((m,), 46), _rand((m, m), 47), _rand((m,), 48)]
+    w3, b3, pid = _rand((m, E), 49), _rand((E,), 50), _rand((E,), 51)
+    perm = np.array([3, 0, 4, 1, 2])
+    a = orc.mlp_router(*args, w3, b3, pid)["logits"]
+    b = orc.mlp_router(*args, w3[:, perm].contiguous(), b3[perm], pid[perm])["logits"]
+    np.testing.assert_array_equal(a[:, perm], b)
+
+
 # ---------------------------------------------------------------- expert FFN
 
 def test_gelu_is_erf_form_against_normal_table():
