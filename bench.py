@@ -90,6 +90,32 @@ def roofline(cfg, a, launch_ms, peak, traffic, traffic_kernel):
     return r
 
 
+def mlp_router_ms(cfg, xs, n_rot, K):
+    """Mean time of moe_route_mlp (the ZAYA1 MLP router variant, r = 256,
+    m = 1024, seeded random weights) over K calls, HIP events on the stream."""
+    import torch
+    import mixture_experts_layer_15_amd as moe
+    g = torch.Generator(device="cuda").manual_seed(1)
+    n = lambda *sh, sc=1.0: torch.randn(*sh, generator=g, device="cuda") * sc
+    r, m = 256, 1024
+    rt = dict(w_down=n(cfg.d, r, sc=cfg.d ** -0.5).bfloat16(), b_down=n(r, sc=0.1),
+              w1=n(r, m, sc=r ** -0.5).bfloat16(), b1=n(m, sc=0.1),
+              w2=n(m, m, sc=m ** -0.5).bfloat16(), b2=n(m, sc=0.1),
+              w3=n(m, cfg.E, sc=m ** -0.5).bfloat16(), b3=n(cfg.E, sc=0.1),
+              pid_bias=n(cfg.E, sc=0.05))
+    prev = n(cfg.T, r).bfloat16()
+    for i in range(3):
+        moe.route_mlp(cfg, xs[i % n_rot], prev, rt, 0.5, 1e-6)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(K):
+        moe.route_mlp(cfg, xs[i % n_rot], prev, rt, 0.5, 1e-6)
+    b.record()
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) / K, 4)
+
+
 def measured_traffic(cfg):
     """HBM bytes per launch of the gate/up GEMM from the committed FETCH_SIZE /
     WRITE_SIZE counter runs (scaled by a plain copy of known size), or None when
@@ -232,6 +258,8 @@ def main():
     gpu_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][5]) for i in range(K)]))
     ms_step = wall * 1e3 / K
 
+    mlp_ms = mlp_router_ms(cfg, xs, n_rot, K) if cfg.dtype == "bf16" else None
+
     # the fused entry point: the step time that `value` reports
     fwd = moe.Forward(cfg)
     for i in range(3):
@@ -290,6 +318,8 @@ def main():
                         "max_over_mean": round(float(ls[3]), 4),
                         "max_deviation": round(float(ls[4]), 4), "cv": round(float(ls[5]), 4),
                         "dropped": int(ls[6]), "empty_experts": int(ls[7])},
+        "variants": {"mlp_router_ms": mlp_ms,
+                     "mlp_router_widths": "r=256 m=1024 (ZAYA1 MLP router, random weights)"},
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},

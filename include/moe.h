@@ -137,6 +137,49 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
 moe_status moe_route_from_logits(const moe_config* cfg, const float* logits,
                                  int32_t* topk_idx, float* topk_gate, void* stream);
 
+/* Variant of steps 1-3: the ZAYA1 MLP router ("AMD MI300X平台上的MoE模型训练实践",
+ * section 3.2), forward.  Per token:
+ *   u  = x W_down + b_down                  [r]
+ *   z  = RMSnorm(u + gamma * prev)          v / sqrt(mean_j v_j^2 + eps), no scale
+ *   h1 = GELU(z W1 + b1), h2 = GELU(h1 W2 + b2)   [m], GELU in its erf form
+ *   l  = h2 W3 + b3 + pid_bias              [E]
+ * then the temperature softmax, top-k and gates of moe_route (same code, same
+ * outputs).  The page gives r = 256 and m = 1024 and leaves gamma, eps and the
+ * load-balance controller's update rule open: gamma and eps are parameters
+ * here, and the controller enters through its output, pid_bias.  bf16 only
+ * (MOE_ERR_UNSUPPORTED for fp32); fp32 accumulation, u, z, h1 and h2 rounded
+ * once each to bf16, logits fp32.  Weights row-major in the layer's dtype,
+ * biases fp32 and optional (NULL = zero). */
+typedef struct {
+    int32_t r;              /* down-projection width, 64 <= r <= 1024, r % 64 == 0 */
+    int32_t m;              /* hidden width, 64 <= m <= 16384, m % 64 == 0 */
+    float gamma;            /* weight of prev, finite */
+    float eps;              /* RMS-norm epsilon, finite, >= 0 */
+    const void* w_down;     /* [d, r] */
+    const float* b_down;    /* [r] or NULL */
+    const void* w1;         /* [r, m] */
+    const float* b1;        /* [m] or NULL */
+    const void* w2;         /* [m, m] */
+    const float* b2;        /* [m] or NULL */
+    const void* w3;         /* [m, E] */
+    const float* b3;        /* [E] or NULL */
+    const float* pid_bias;  /* [E] or NULL */
+} moe_mlp_router;
+
+/* Host.  Workspace bytes moe_route_mlp needs (u, z [T, r], h1, h2 [T, m]
+ * bf16 and E fp32). */
+moe_status moe_mlp_router_workspace_size(const moe_config* cfg, const moe_mlp_router* router,
+                                         size_t* bytes);
+
+/*   x         [T, d]  dtype in
+ *   prev      [T, r]  dtype in   the previous layer's router state, or NULL
+ *   logits    [T, E]  fp32  out
+ *   topk_idx, topk_gate  as for moe_route
+ *   workspace ws_bytes >= moe_mlp_router_workspace_size(cfg, router, .) */
+moe_status moe_route_mlp(const moe_config* cfg, const moe_mlp_router* router, const void* x,
+                         const void* prev, float* logits, int32_t* topk_idx, float* topk_gate,
+                         void* workspace, size_t ws_bytes, void* stream);
+
 /* Steps 4-5: capacity, token-order drops and the expert-grouped permutation.
  *   topk_idx      [T, k]         int32  in
  *   x             [T, d]         dtype  in

@@ -25,7 +25,7 @@ MOE_DROP_TOKEN_ORDER, MOE_DROP_CHOICE_ORDER = 0, 1
 EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_status_string",
            "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_forward", "moe_load_stats")
+           "moe_forward", "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp")
 
 
 class CConfig(ctypes.Structure):
@@ -35,6 +35,15 @@ class CConfig(ctypes.Structure):
                 ("temperature", ctypes.c_float), ("cap_num", ctypes.c_int32),
                 ("cap_den", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("drop_policy", ctypes.c_int32)]
+
+
+class CMLPRouter(ctypes.Structure):
+    """Mirror of moe_mlp_router (include/moe.h)."""
+    _fields_ = [("r", ctypes.c_int32), ("m", ctypes.c_int32), ("gamma", ctypes.c_float),
+                ("eps", ctypes.c_float), ("w_down", ctypes.c_void_p), ("b_down", ctypes.c_void_p),
+                ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("b3", ctypes.c_void_p),
+                ("pid_bias", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -75,9 +84,12 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [cp, _P, _P, _P, _P, _P]
         L.moe_forward.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_load_stats.argtypes = [cp, _P, _P, _P]
+        rp = ctypes.POINTER(CMLPRouter)
+        L.moe_mlp_router_workspace_size.argtypes = [cp, rp, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_route_mlp.argtypes = [cp, rp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         for n in ("moe_route", "moe_route_from_logits", "moe_dispatch", "moe_expert_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
-                  "moe_load_stats"):
+                  "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -187,6 +199,42 @@ def dispatch(cfg: MoEConfig, topk_idx, x) -> Dict:
            "moe_dispatch")
     out["_workspace"] = ws   # keep alive until the stream has run
     return out
+
+
+MLP_ROUTER_KEYS = ("w_down", "b_down", "w1", "b1", "w2", "b2", "w3", "b3", "pid_bias")
+
+
+def route_mlp(cfg: MoEConfig, x, prev, router: Dict, gamma: float, eps: float):
+    """moe_route_mlp -> (logits [T,E] fp32, topk_idx [T,k] int32, topk_gate [T,k] fp32).
+    router: dict of the weights (w_down [d,r], w1 [r,m], w2 [m,m], w3 [m,E], layer dtype)
+    and optional fp32 biases (b_down, b1, b2, b3, pid_bias)."""
+    import torch
+    dev = x.device
+    r, m = router["w_down"].shape[1], router["w1"].shape[1]
+    _need(x, "x", _dt(cfg), (cfg.T, cfg.d), dev)
+    if prev is not None:
+        _need(prev, "prev", _dt(cfg), (cfg.T, r), dev)
+    for key, shape in (("w_down", (cfg.d, r)), ("w1", (r, m)), ("w2", (m, m)), ("w3", (m, cfg.E))):
+        _need(router[key], key, _dt(cfg), shape, dev)
+    for key, n in (("b_down", r), ("b1", m), ("b2", m), ("b3", cfg.E), ("pid_bias", cfg.E)):
+        if router.get(key) is not None:
+            _need(router[key], key, torch.float32, (n,), dev)
+    addr = lambda t: None if t is None else t.data_ptr()
+    cr = CMLPRouter(r=r, m=m, gamma=gamma, eps=eps,
+                    **{key: addr(router.get(key)) for key in MLP_ROUTER_KEYS})
+    c = cconfig(cfg)
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_mlp_router_workspace_size(ctypes.byref(c), ctypes.byref(cr), ctypes.byref(n)),
+           "moe_mlp_router_workspace_size")
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    _check(lib().moe_route_mlp(ctypes.byref(c), ctypes.byref(cr), _ptr(x), _ptr(prev),
+                               _ptr(logits), _ptr(idx), _ptr(gate), _ptr(ws), n.value, _stream()),
+           "moe_route_mlp")
+    route_mlp._last_ws = ws   # keep the workspace alive until the stream has run
+    return logits, idx, gate
 
 
 def load_stats(cfg: MoEConfig, expert_count):

@@ -218,7 +218,8 @@ template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB>
 __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ a_rows, int E, int K, int N) {
+    const int32_t* __restrict__ off, const int32_t* __restrict__ a_rows, int E, int K, int N,
+    int dense_rows, const float* __restrict__ bias, int act) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB>;
     // one distinct __shared__ array per stage buffer, so that the compiler can
     // tell the reads of one stage from the fills of the others
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     __shared__ long long s_wave[S::WAVES];
 
     const int ntn = (N + S::OUTC - 1) / S::OUTC;
-    build_tile_table<S::BM>(off, E, ntn, tt, s_wave);
+    build_tile_table<S::BM>(off, E, ntn, tt, s_wave, dense_rows);
     const long long total = tt.start[E];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -278,8 +279,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         if (t >= total) continue;   // uniform across the workgroup
         int e, mtile, ntile;
         decode_tile<GM>(tt, E, ntn, t, e, mtile, ntile);
-        const int row0 = off[e] + mtile * S::BM;
-        const int rows = min(S::BM, off[e + 1] - row0);
+        const int row0 = (off ? off[e] : 0) + mtile * S::BM;
+        const int rows = min(S::BM, (off ? off[e + 1] : dense_rows) - row0);
         const int n0 = ntile * S::OUTC;
         const int nvm = __builtin_amdgcn_readfirstlane(
             max(0, min(MI, (rows - wm * MI * 16 + 15) >> 4)));
@@ -392,7 +393,16 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
 
         // epilogue straight from the accumulators: lane (g4, c16) of block
         // (i, j) holds output columns 4 g4 .. 4 g4 + 3 of row c16, one 8-byte
-        // store per block
+        // store per block.  Plain GEMMs may add a per-column fp32 bias and
+        // apply GELU (act == 1).
+        float bv[S::OUTW / 16][4];
+#pragma unroll
+        for (int jj = 0; jj < S::OUTW / 16; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int gc = n0 + wn * S::OUTW + jj * 16 + g4 * 4 + q;
+                bv[jj][q] = (!GATEUP && bias != nullptr && gc < N) ? bias[gc] : 0.f;
+            }
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int r = wm * MI * 16 + i * 16 + c16;
@@ -405,7 +415,14 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float a = acc[i][jj][q];
-                        v[q] = (__bf16)(GATEUP ? gelu_erf_bf16(a) * acc[i][jj + NJ / 2][q] : a);
+                        float o;
+                        if constexpr (GATEUP) {
+                            o = gelu_erf_bf16(a) * acc[i][jj + NJ / 2][q];
+                        } else {
+                            o = a + bv[jj][q];
+                            if (act == 1) o = gelu_erf_bf16(o);
+                        }
+                        v[q] = (__bf16)o;
                     }
                     if (n0 + col < N) *(u32x2*)(crow + col) = __builtin_bit_cast(u32x2, v);
                 }
@@ -421,7 +438,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
 
 template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB>
 hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
-                        const int32_t* off, const int32_t* a_rows, int E, int K, int N, long long max_rows, int cus,
+                        const int32_t* off, const int32_t* a_rows, int dense_rows,
+                        const float* bias, int act, int E, int K, int N, long long max_rows, int cus,
                         hipStream_t s) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB>;
     const long long mt = (max_rows + S::BM - 1) / S::BM + E;   // >= sum_e ceil(rows_e / BM)
@@ -429,7 +447,8 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
     long long g = std::min<long long>(cus, (tiles + 7) / 8 * 8);
     g = std::max<long long>(8, g / 8 * 8);
     hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NA, NB>), dim3((unsigned)g),
-                       dim3(S::THREADS), 0, s, A, B0, B1, C, off, a_rows, E, K, N);
+                       dim3(S::THREADS), 0, s, A, B0, B1, C, off, a_rows, E, K, N, dense_rows,
+                       bias, act);
     return hipGetLastError();
 }
 
@@ -448,9 +467,9 @@ hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const i
                                const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
                                long long max_rows, int cus, hipStream_t s) {
     if (small_experts(max_rows, E))
-        return launch_shape<true, 10, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, E, d, d_ff,
+        return launch_shape<true, 10, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0, E, d, d_ff,
                                                 max_rows, cus, s);
-    return launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, E, d, d_ff, max_rows,
+    return launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0, E, d, d_ff, max_rows,
                                            cus, s);
 }
 
@@ -458,10 +477,25 @@ hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
                             int cus, hipStream_t s) {
     if (small_experts(max_rows, E))
-        return launch_shape<false, 10, 2, 64, 2, 4>(h, w_down, nullptr, y_perm, off, nullptr, E, d_ff, d,
+        return launch_shape<false, 10, 2, 64, 2, 4>(h, w_down, nullptr, y_perm, off, nullptr, 0, nullptr, 0, E, d_ff, d,
                                                  max_rows, cus, s);
-    return launch_shape<false, 8, 4, 64, 2, 2>(h, w_down, nullptr, y_perm, off, nullptr, E, d_ff, d,
+    return launch_shape<false, 8, 4, 64, 2, 2>(h, w_down, nullptr, y_perm, off, nullptr, 0, nullptr, 0, E, d_ff, d,
                                             max_rows, cus, s);
+}
+
+// Dense bf16 GEMM C [M][N] = A [M][K] B [K][N] (+ bias[N]) (GELU when act ==
+// 1), fp32 accumulation, one rounding to bf16: the same kernel with a single
+// group of M rows.  Small products take 64 x 64 tiles so that they still
+// spread over the CUs.
+hipError_t launch_mfma_dense(const uint16_t* A, const uint16_t* B, const float* bias, int act,
+                             uint16_t* C, int M, int K, int N, int cus, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const long long big_tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
+    if (big_tiles >= cus)
+        return launch_shape<false, 4, 2, 64, 2, 2>(A, B, nullptr, C, nullptr, nullptr, M, bias,
+                                                    act, 1, K, N, M, cus, s);
+    return launch_shape<false, 2, 1, 64, 2, 2>(A, B, nullptr, C, nullptr, nullptr, M, bias, act,
+                                                1, K, N, M, cus, s);
 }
 
 }  // namespace moe

@@ -71,6 +71,22 @@ hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
                             int cus, hipStream_t s);
 
+// Dense bf16 GEMM with optional bias and GELU epilogue (gemm_mfma.hip).
+hipError_t launch_mfma_dense(const uint16_t* A, const uint16_t* B, const float* bias, int act,
+                             uint16_t* C, int M, int K, int N, int cus, hipStream_t s);
+
+// ZAYA1-style MLP router (mlp_router.hip): down-projection, depth averaging,
+// RMS norm, two GELU layers, output layer + controller bias, then the usual
+// softmax / top-k.  ws holds u, z [T][r], h1, h2 [T][m] bf16 and [E] fp32.
+size_t mlp_router_workspace_bytes(long long T, int r, int m, int E);
+hipError_t launch_route_mlp(const uint16_t* x, const uint16_t* prev, float gamma, float eps,
+                            const uint16_t* wd, const float* bd, const uint16_t* w1,
+                            const float* b1, const uint16_t* w2, const float* b2,
+                            const uint16_t* w3, const float* b3, const float* pid,
+                            float* logits, int32_t* idx, float* gate, long long T, int d, int r,
+                            int m, int E, int k, float tau, int renorm, void* ws, int cus,
+                            hipStream_t s);
+
 // Gate-weighted combine.
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
                           const float* gate, void* y, long long T, int d, int k,

@@ -306,6 +306,70 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine");
 }
 
+}  // extern "C"
+
+namespace {
+
+moe_status check_mlp(const moe_config* cfg, const moe_mlp_router* rt) {
+    CHECK(check_cfg(cfg));
+    if (rt == nullptr) return fail(MOE_ERR_INVALID_ARG, "router is NULL");
+    if (rt->r < 64 || rt->r > 1024 || rt->r % 64 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "router r = %d: need a multiple of 64 in [64, 1024]", rt->r);
+    if (rt->m < 64 || rt->m > 16384 || rt->m % 64 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "router m = %d: need a multiple of 64 in [64, 16384]", rt->m);
+    if (!std::isfinite(rt->gamma)) return fail(MOE_ERR_INVALID_ARG, "router gamma must be finite");
+    if (!(rt->eps >= 0.f) || !std::isfinite(rt->eps))
+        return fail(MOE_ERR_INVALID_ARG, "router eps must be finite and >= 0");
+    if (cfg->dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "the MLP router runs on bf16 layers only");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_mlp_router_workspace_size(const moe_config* cfg, const moe_mlp_router* router,
+                                         size_t* bytes) {
+    CHECK(check_mlp(cfg, router));
+    if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = moe::mlp_router_workspace_bytes(cfg->T, router->r, router->m, cfg->E);
+    return MOE_OK;
+}
+
+moe_status moe_route_mlp(const moe_config* cfg, const moe_mlp_router* rt, const void* x,
+                         const void* prev, float* logits, int32_t* topk_idx, float* topk_gate,
+                         void* workspace, size_t ws_bytes, void* stream) {
+    CHECK(check_mlp(cfg, rt));
+    SIZES(cfg);
+    const size_t r = (size_t)rt->r, m = (size_t)rt->m;
+    CHECK(check_ptr(x, "x", T * d * es));
+    CHECK(check_ptr(prev, "prev", T * r * es, true));
+    CHECK(check_ptr(rt->w_down, "w_down", d * r * es));
+    CHECK(check_ptr(rt->b_down, "b_down", r * 4, true));
+    CHECK(check_ptr(rt->w1, "w1", r * m * es));
+    CHECK(check_ptr(rt->b1, "b1", m * 4, true));
+    CHECK(check_ptr(rt->w2, "w2", m * m * es));
+    CHECK(check_ptr(rt->b2, "b2", m * 4, true));
+    CHECK(check_ptr(rt->w3, "w3", m * E * es));
+    CHECK(check_ptr(rt->b3, "b3", E * 4, true));
+    CHECK(check_ptr(rt->pid_bias, "pid_bias", E * 4, true));
+    CHECK(check_ptr(logits, "logits", T * E * 4));
+    CHECK(check_ptr(topk_idx, "topk_idx", T * k * 4));
+    CHECK(check_ptr(topk_gate, "topk_gate", T * k * 4));
+    const size_t need = moe::mlp_router_workspace_bytes(cfg->T, rt->r, rt->m, cfg->E);
+    if (T > 0 && (workspace == nullptr || ws_bytes < need))
+        return fail(MOE_ERR_WORKSPACE, "MLP router workspace: need %zu bytes, got %zu", need, ws_bytes);
+    CHECK(check_ptr(workspace, "workspace", T > 0 ? need : 0));
+    hipError_t e = moe::launch_route_mlp(
+        (const uint16_t*)x, (const uint16_t*)prev, rt->gamma, rt->eps,
+        (const uint16_t*)rt->w_down, rt->b_down, (const uint16_t*)rt->w1, rt->b1,
+        (const uint16_t*)rt->w2, rt->b2, (const uint16_t*)rt->w3, rt->b3, rt->pid_bias, logits,
+        topk_idx, topk_gate, cfg->T, cfg->d, rt->r, rt->m, cfg->E, cfg->k, cfg->temperature,
+        cfg->renormalize, workspace, gemm_grid_cap() / 2, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_mlp");
+}
+
 moe_status moe_load_stats(const moe_config* cfg, const int32_t* expert_count, double* stats,
                           void* stream) {
     CHECK(check_cfg(cfg));

@@ -120,6 +120,38 @@ def test_null_and_misaligned_pointers_rejected(L):
     assert L.moe_load_stats(ctypes.byref(c), ok, odd, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_mlp_router_validation_on_host(L):
+    cfg = configs.get("zaya1")
+    c = moe.cconfig(cfg)
+    ok = 1 << 20
+    n = ctypes.c_size_t(0)
+    good = dict(r=256, m=1024, gamma=0.5, eps=1e-6, w_down=ok, w1=ok, w2=ok, w3=ok)
+    r = moe.CMLPRouter(**good)
+    assert L.moe_mlp_router_workspace_size(ctypes.byref(c), ctypes.byref(r), ctypes.byref(n)) == 0
+    T, rr, m, E = cfg.T, 256, 1024, cfg.E
+    al = lambda v: (v + 255) // 256 * 256
+    assert n.value == 2 * al(T * rr * 2) + 2 * al(T * m * 2) + al(E * 4)
+    for bad, word in [(dict(r=96), "r ="), (dict(r=2048), "r ="), (dict(m=100), "m ="),
+                      (dict(gamma=float("nan")), "gamma"), (dict(eps=-1.0), "eps")]:
+        rb = moe.CMLPRouter(**dict(good, **bad))
+        assert L.moe_mlp_router_workspace_size(ctypes.byref(c), ctypes.byref(rb),
+                                               ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+        assert word in L.moe_last_error().decode()
+    assert L.moe_mlp_router_workspace_size(ctypes.byref(c), None, ctypes.byref(n)) == \
+        moe.MOE_ERR_INVALID_ARG
+    f32 = moe.cconfig(configs.get("tiny"))
+    assert L.moe_mlp_router_workspace_size(ctypes.byref(f32), ctypes.byref(r), ctypes.byref(n)) == \
+        moe.MOE_ERR_UNSUPPORTED
+    # missing weight, missing workspace: rejected before any launch
+    rw = moe.CMLPRouter(**dict(good, w2=None))
+    v = ctypes.c_void_p(ok)
+    assert L.moe_route_mlp(ctypes.byref(c), ctypes.byref(rw), v, None, v, v, v, v, 1 << 40,
+                           None) == moe.MOE_ERR_INVALID_ARG
+    assert b"w2 is NULL" in L.moe_last_error()
+    assert L.moe_route_mlp(ctypes.byref(c), ctypes.byref(r), v, None, v, v, v, None, 0,
+                           None) == moe.MOE_ERR_WORKSPACE
+
+
 def test_choice_order_workspace_is_sized_for_the_walked_choices(L):
     # the dispatch tables hold 2 * nblk * E int32, nblk <= 256 blocks of whole
     # 256-token chunks over the walked tokens: T in token order, T*k single

@@ -85,3 +85,61 @@ def test_load_stats_edge_counts():
         C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
         want = orc.load_stats(counts, C)
         np.testing.assert_allclose(st.cpu().numpy(), want, rtol=1e-12, atol=0)
+
+
+# ---------------------------------------------------------------- MLP router
+# Logits of a bf16 network (four intermediate roundings): compared with the
+# R13 metric at the layer's bf16 tolerance; the top-k and gates then follow the
+# same-fp32-logits protocol as the linear router.
+TOL_MLP_LOGITS = 2e-2
+
+
+def _mlp_router_inputs(cfg, r, m, seed):
+    g = torch.Generator().manual_seed(seed)
+    n = lambda *s, sc=1.0: (torch.randn(*s, generator=g) * sc)
+    bf = lambda t: t.to(torch.bfloat16)
+    host = dict(w_down=bf(n(cfg.d, r, sc=cfg.d ** -0.5)), b_down=n(r, sc=0.1),
+                w1=bf(n(r, m, sc=r ** -0.5)), b1=n(m, sc=0.1),
+                w2=bf(n(m, m, sc=m ** -0.5)), b2=n(m, sc=0.1),
+                w3=bf(n(m, cfg.E, sc=m ** -0.5)), b3=n(cfg.E, sc=0.1),
+                pid_bias=n(cfg.E, sc=0.05))
+    prev = bf(n(cfg.T, r))
+    return host, prev
+
+
+MLP_CASES = {
+    "mlp_small": (configs.get("tiny").scaled(T=300, d=128, E=16, k=2, dtype="bf16",
+                                             renormalize=True, temperature=0.3), 64, 128, True),
+    "mlp_ragged": (configs.get("tiny").scaled(T=1001, d=192, E=24, k=3, dtype="bf16",
+                                              renormalize=True), 128, 192, True),
+    # the page's widths on the ZAYA1-like layer
+    "mlp_zaya1": (configs.get("zaya1"), 256, 1024, False),
+}
+
+
+@pytest.mark.parametrize("name", list(MLP_CASES))
+def test_mlp_router_matches_oracle(name):
+    from parity_util import check_route, rel_err
+    cfg, r, m, with_prev = MLP_CASES[name]
+    dev_in, _ = gpu_inputs(cfg, seed=7)
+    x = dev_in["x"]
+    host, prev = _mlp_router_inputs(cfg, r, m, seed=11)
+    rt = {k: v.cuda() for k, v in host.items()}
+    prev_d = prev.cuda() if with_prev else None
+    gamma, eps = 0.5, 1e-6
+    say(f"[{name}] moe_route_mlp T={cfg.T} d={cfg.d} r={r} m={m} E={cfg.E} k={cfg.k}")
+    lg, idx, gate = moe.route_mlp(cfg, x, prev_d, rt, gamma, eps)
+    torch.cuda.synchronize()
+    toks = np.arange(cfg.T) if cfg.T <= 1024 else np.unique(
+        np.random.default_rng(0).integers(0, cfg.T, 384))
+    want = orc.mlp_router(x.cpu()[toks], prev[toks] if with_prev else None, gamma, eps,
+                          host["w_down"], host["b_down"], host["w1"], host["b1"], host["w2"],
+                          host["b2"], host["w3"], host["b3"], host["pid_bias"])["logits"]
+    err = rel_err(lg.cpu().double().numpy()[toks], want)
+    say(f"[{name}] logits err {err:.3g} over {toks.size} tokens")
+    assert err <= TOL_MLP_LOGITS
+    check_route(cfg, lg.cpu(), idx.cpu(), gate.cpu())
+    # the same logits through the linear router's top-k entry point
+    idx2, gate2 = moe.route_from_logits(cfg, lg)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(gate2, gate)
