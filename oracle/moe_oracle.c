@@ -38,6 +38,9 @@
  * dtype codes: 0 = fp32, 1 = bf16 (raw 16-bit patterns, the upper half of an
  * IEEE fp32).  Every input value is widened exactly to fp64 before use.
  */
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -321,6 +324,154 @@ void orc_ffn_rows(int64_t n_rows, const int64_t* tok, const int32_t* ex, int64_t
         }
         free(g); free(u); free(o);
     }
+}
+
+/* GELU'(v) = Phi(v) + v phi(v), the derivative of the erf form. */
+static double gelu_grad(double v) {
+    return 0.5 * (1.0 + erf(v / sqrt(2.0))) + v * exp(-0.5 * v * v) / sqrt(2.0 * M_PI);
+}
+
+/* Backward of the whole layer for an upstream gradient dy = dL/dy [T][d]
+ * (the step after the forward: every page trains this layer).  Routing is
+ * given (idx, gate, row_of from the forward, logits the values it ranked):
+ * the top-k choice and the drops are piecewise constant, so no gradient flows
+ * through them.  With p = softmax(l / tau) and, per kept assignment (t, j) of
+ * expert e: g = x Wg[e], u = x Wu[e], a = GELU(g), h = a * u, o = h Wd[e],
+ * y_t = sum_j gate_tj o_tj:
+ *   dO = gate_tj dy_t, dgate_tj = dy_t . o_tj (0 for a dropped assignment)
+ *   dh = dO Wd[e]^T, dWd[e] += h^T dO
+ *   du = dh * a, dg = dh * u * GELU'(g)
+ *   dWg[e] += x^T dg, dWu[e] += x^T du, dx_t += dg Wg[e]^T + du Wu[e]^T
+ * gates: renormalised, gate_j = p_j / S (S = sum of the chosen p):
+ *   dp_j = (dgate_j - sum_j' dgate_j' gate_j') / S; raw: dp_j = dgate_j;
+ *   dp = 0 for experts not chosen;
+ * softmax with temperature: dl_e = p_e (dp_e - sum_e' p_e' dp_e') / tau;
+ * router: dWr += x^T dl, db += dl, dx_t += dl Wr^T.
+ * Every sum in ascending index order; expert gradients are built one expert
+ * per thread (tokens ascending), token gradients one token per thread
+ * (choices ascending).  dgate may be NULL. */
+void orc_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t d_ff, int dtype,
+                  double tau, int renorm, const void* x, const void* wr, const double* logits,
+                  const int32_t* idx, const double* gate, const int32_t* row_of,
+                  const void* wg, const void* wu, const void* wd, const double* dy,
+                  double* dx, double* dwr, double* db, double* dwg, double* dwu, double* dwd,
+                  double* dgate) {
+    double* dxa = (double*)calloc((size_t)(T * k * d), sizeof(double));   /* per assignment */
+    double* dga = (double*)calloc((size_t)(T * k), sizeof(double));
+    double* dl = (double*)calloc((size_t)(T * E), sizeof(double));
+    memset(dwg, 0, sizeof(double) * (size_t)(E * d * d_ff));
+    memset(dwu, 0, sizeof(double) * (size_t)(E * d * d_ff));
+    memset(dwd, 0, sizeof(double) * (size_t)(E * d_ff * d));
+    #pragma omp parallel
+    {
+        double* g = (double*)malloc(sizeof(double) * (size_t)d_ff);
+        double* u = (double*)malloc(sizeof(double) * (size_t)d_ff);
+        double* h = (double*)malloc(sizeof(double) * (size_t)d_ff);
+        double* dh = (double*)malloc(sizeof(double) * (size_t)d_ff);
+        double* dO = (double*)malloc(sizeof(double) * (size_t)d);
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t e = 0; e < E; ++e) {
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t j = 0; j < k; ++j) {
+                    int64_t a = t * k + j;
+                    if (idx[a] != e || row_of[a] < 0) continue;
+                    for (int64_t n = 0; n < d_ff; ++n) { g[n] = 0.0; u[n] = 0.0; }
+                    for (int64_t i = 0; i < d; ++i) {
+                        double xi = load(x, t * d + i, dtype);
+                        int64_t wrow = (e * d + i) * d_ff;
+                        for (int64_t n = 0; n < d_ff; ++n) {
+                            g[n] += xi * load(wg, wrow + n, dtype);
+                            u[n] += xi * load(wu, wrow + n, dtype);
+                        }
+                    }
+                    for (int64_t n = 0; n < d_ff; ++n) h[n] = gelu(g[n]) * u[n];
+                    double dgt = 0.0;
+                    for (int64_t c = 0; c < d; ++c) {
+                        double o = 0.0;
+                        for (int64_t n = 0; n < d_ff; ++n) o += h[n] * load(wd, (e * d_ff + n) * d + c, dtype);
+                        dgt += dy[t * d + c] * o;
+                        dO[c] = gate[a] * dy[t * d + c];
+                    }
+                    dga[a] = dgt;
+                    for (int64_t n = 0; n < d_ff; ++n) {
+                        double s = 0.0;
+                        int64_t wrow = (e * d_ff + n) * d;
+                        for (int64_t c = 0; c < d; ++c) {
+                            s += dO[c] * load(wd, wrow + c, dtype);
+                            dwd[wrow + c] += h[n] * dO[c];
+                        }
+                        dh[n] = s;
+                    }
+                    for (int64_t n = 0; n < d_ff; ++n) {
+                        double du = dh[n] * gelu(g[n]);
+                        double dg = dh[n] * u[n] * gelu_grad(g[n]);
+                        g[n] = dg;   /* g now holds dg, u holds du */
+                        u[n] = du;
+                    }
+                    for (int64_t i = 0; i < d; ++i) {
+                        double xi = load(x, t * d + i, dtype), s = 0.0;
+                        int64_t wrow = (e * d + i) * d_ff;
+                        for (int64_t n = 0; n < d_ff; ++n) {
+                            s += g[n] * load(wg, wrow + n, dtype) + u[n] * load(wu, wrow + n, dtype);
+                            dwg[wrow + n] += xi * g[n];
+                            dwu[wrow + n] += xi * u[n];
+                        }
+                        dxa[a * d + i] = s;
+                    }
+                }
+        }
+        free(g); free(u); free(h); free(dh); free(dO);
+    }
+    #pragma omp parallel
+    {
+        double* dp = (double*)malloc(sizeof(double) * (size_t)E);
+        double* p = (double*)malloc(sizeof(double) * (size_t)E);
+        #pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const double* l = logits + t * E;
+            double m = l[0];
+            for (int64_t e = 1; e < E; ++e) if (l[e] > m) m = l[e];
+            double z = 0.0;
+            for (int64_t e = 0; e < E; ++e) {
+                const double q = (l[e] - m) / tau;
+                p[e] = exp(q);
+                z += p[e];
+            }
+            for (int64_t e = 0; e < E; ++e) { p[e] /= z; dp[e] = 0.0; }
+            if (renorm) {
+                double S = 0.0, sg = 0.0;
+                for (int64_t j = 0; j < k; ++j) S += p[idx[t * k + j]];
+                for (int64_t j = 0; j < k; ++j) sg += dga[t * k + j] * gate[t * k + j];
+                for (int64_t j = 0; j < k; ++j) dp[idx[t * k + j]] = (dga[t * k + j] - sg) / S;
+            } else {
+                for (int64_t j = 0; j < k; ++j) dp[idx[t * k + j]] = dga[t * k + j];
+            }
+            double pd = 0.0;
+            for (int64_t e = 0; e < E; ++e) pd += p[e] * dp[e];
+            for (int64_t e = 0; e < E; ++e) dl[t * E + e] = p[e] * (dp[e] - pd) / tau;
+            for (int64_t i = 0; i < d; ++i) {
+                double s = 0.0;
+                for (int64_t j = 0; j < k; ++j) s += dxa[(t * k + j) * d + i];
+                for (int64_t e = 0; e < E; ++e) s += dl[t * E + e] * load(wr, i * E + e, dtype);
+                dx[t * d + i] = s;
+            }
+            if (dgate) for (int64_t j = 0; j < k; ++j) dgate[t * k + j] = dga[t * k + j];
+        }
+        free(dp); free(p);
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < d; ++i)
+        for (int64_t e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int64_t t = 0; t < T; ++t) s += load(x, t * d + i, dtype) * dl[t * E + e];
+            dwr[i * E + e] = s;
+        }
+    for (int64_t e = 0; e < E; ++e) {
+        double s = 0.0;
+        for (int64_t t = 0; t < T; ++t) s += dl[t * E + e];
+        db[e] = s;
+    }
+    free(dxa); free(dga); free(dl);
 }
 
 /* Step 6 -- gate-weighted combine for a list of tokens.

@@ -69,6 +69,9 @@ def _declare(lib):
     lib.orc_mlp_router.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int, _P, _P,
                                    ctypes.c_double, ctypes.c_double] + [_P] * 13
     lib.orc_mlp_router.restype = None
+    lib.orc_backward.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_double,
+                                 ctypes.c_int] + [_P] * 17
+    lib.orc_backward.restype = None
     lib.orc_ffn_rows.argtypes = [_I64, _P, _P, _I64, _I64, ctypes.c_int,
                                  _P, _P, _P, _P, _P, _P]
     lib.orc_ffn_rows.restype = None
@@ -213,6 +216,39 @@ def mlp_router(x, prev, gamma: float, eps: float, wd, bd, w1, b1, w2, b2, w3, b3
                            _ptr(w3r), _ptr(bs[3]), _ptr(bs[4]), _ptr(lg), _ptr(z), _ptr(h1),
                            _ptr(h2))
     return dict(logits=lg, z=z, h1=h1, h2=h2)
+
+
+def backward(x, w_router, bias, w_gate, w_up, w_down, dy, *, k: int, tau: float,
+             renormalize: bool, cap_num: int, cap_den: int, drop_policy: int = 0,
+             logits_in: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of the layer for an upstream dy [T, d] (fp64 or castable), in
+    fp64: dx, dw_router, dbias, dw_gate, dw_up, dw_down, dgate, plus the routing
+    they used.  Routing as in forward(): from logits_in when given."""
+    xr, dt = _raw(x)
+    T, d = xr.shape
+    wrr, _ = _raw(w_router)
+    E = wrr.shape[1]
+    wgr, _ = _raw(w_gate)
+    wur, _ = _raw(w_up)
+    wdr, _ = _raw(w_down)
+    d_ff = wgr.shape[2]
+    lg = logits(x, w_router, bias) if logits_in is None else np.asarray(logits_in, np.float64)
+    lg = np.ascontiguousarray(lg)
+    idx, gate = route(lg, k, tau, renormalize)
+    C = capacity(T, E, k, cap_num, cap_den)
+    dsp = dispatch(idx, E, C, drop_policy)
+    dyr = np.ascontiguousarray(np.asarray(dy, dtype=np.float64))
+    out = dict(dx=np.empty((T, d)), dw_router=np.empty((d, E)), dbias=np.empty(E),
+               dw_gate=np.empty((E, d, d_ff)), dw_up=np.empty((E, d, d_ff)),
+               dw_down=np.empty((E, d_ff, d)), dgate=np.empty((T, k)))
+    _load().orc_backward(T, d, E, k, d_ff, dt, float(tau), int(bool(renormalize)), _ptr(xr),
+                         _ptr(wrr), _ptr(lg), _ptr(idx), _ptr(np.ascontiguousarray(gate)),
+                         _ptr(dsp["row_of"]), _ptr(wgr), _ptr(wur), _ptr(wdr), _ptr(dyr),
+                         _ptr(out["dx"]), _ptr(out["dw_router"]), _ptr(out["dbias"]),
+                         _ptr(out["dw_gate"]), _ptr(out["dw_up"]), _ptr(out["dw_down"]),
+                         _ptr(out["dgate"]))
+    out.update(logits=lg, idx=idx, gate=gate, row_of=dsp["row_of"], C=C)
+    return out
 
 
 def load_stats(count: np.ndarray, C: int) -> np.ndarray:

@@ -13,11 +13,13 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
-PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+        os.path.join(ROOT, "tests", "test_oracle_backward.py")]
 
 MUTANTS = {
     "bias dropped": ("if (bias) s += (double)bias[e];", "if (0) s += (double)bias[e];"),
-    "router weight transposed": ("load(wr, i * E + e, dtype)", "load(wr, e * d + i, dtype)"),
+    "router weight transposed": ("s += load(x, t * d + i, dtype) * load(wr, i * E + e, dtype);",
+                                 "s += load(x, t * d + i, dtype) * load(wr, e * d + i, dtype);"),
     "ties to the higher index": ("l[e] > l[best]) best = e;", "l[e] >= l[best]) best = e;"),
     "temperature multiplies": ("exp((l[e] - m) / tau)", "exp((l[e] - m) * tau)"),
     "no renormalisation": ("renorm ? p[idx[t * k + j]] / s : p[idx[t * k + j]]",
@@ -48,6 +50,16 @@ MUTANTS = {
                                  "if (prev) s -= gamma * load(prev, t * r + j, dtype);"),
     "no GELU on the second layer": ("b[n] = gelu(s);", "b[n] = s;"),
     "router output bias dropped": ("if (b3) s += (double)b3[e];", "if (0) s += (double)b3[e];"),
+    "GELU derivative without the density term": (
+        "+ v * exp(-0.5 * v * v) / sqrt(2.0 * M_PI);", "+ 0.0 * v;"),
+    "renormalised gate gradient without the shared term": (
+        "dp[idx[t * k + j]] = (dga[t * k + j] - sg) / S;", "dp[idx[t * k + j]] = dga[t * k + j] / S;"),
+    "softmax backward without the temperature": (
+        "dl[t * E + e] = p[e] * (dp[e] - pd) / tau;", "dl[t * E + e] = p[e] * (dp[e] - pd);"),
+    "expert output gradient without the gate": (
+        "dO[c] = gate[a] * dy[t * d + c];", "dO[c] = dy[t * d + c];"),
+    "router path missing from dx": (
+        "for (int64_t e = 0; e < E; ++e) s += dl[t * E + e] * load(wr, i * E + e, dtype);", ""),
     "tanh GELU": ("0.5 * v * (1.0 + erf(v / sqrt(2.0)))",
                   "0.5 * v * (1.0 + tanh(0.7978845608028654 * (v + 0.044715 * v * v * v)))"),
     "GELU on the up branch": ("g[n] = gelu(g[n]) * u[n];", "g[n] = g[n] * gelu(u[n]);"),
@@ -68,7 +80,7 @@ def _run(name, src_text, tmp):
     subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
                     "-std=c11", c, "-o", lib, "-lm"], check=True)
     env = dict(os.environ, MOE_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", PINS],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PINS],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return r.returncode
 
