@@ -259,6 +259,45 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        const void* w_down, void* y, void* workspace, size_t ws_bytes,
                        void* stream);
 
+/* Host.  Bytes of workspace moe_backward needs (the recomputed routing and
+ * dispatch maps, the expert pre-activations, the per-row gradients). */
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Backward of steps 1-7 for an upstream gradient dy = dL/dy (training, the
+ * step that follows the forward on every page: the TorchTitan 1K-GPU
+ * article trains this layer, section 2.1; the MegaBlocks paper derives its
+ * grouped backward GEMMs, section 5).  bf16 layers only (MOE_ERR_UNSUPPORTED
+ * otherwise).  The forward's routing and expert pre-activations are
+ * recomputed from the inputs (same kernels, same values as moe_forward);
+ * top-k selection and capacity drops are piecewise constant, so no gradient
+ * passes through them.  With p = softmax(logits / temperature), per kept
+ * assignment (t, j) of expert e, g = x_t W_gate[e], u = x_t W_up[e],
+ * h = GELU_erf(g) u, o = h W_down[e]:
+ *   dgate[t][j] = dy_t . o (0 for a dropped assignment)
+ *   dh = gate dy_t W_down[e]^T; du = dh GELU(g); dg = dh u GELU'(g)
+ *   dw_down[e] += (gate h)^T dy_t, dw_gate[e] += x_t^T dg, dw_up[e] += x_t^T du
+ *   gates: renormalised (gate_j = p_j / S): dp_j = (dgate_j - sum dgate gate) / S,
+ *   raw: dp_j = dgate_j; dlogit = p (dp - p . dp) / temperature
+ *   dw_router = x^T dlogit, dbias = sum_t dlogit,
+ *   dx_t = sum_j (dg W_gate[e]^T + du W_up[e]^T) + dlogit_t W_router^T
+ *   x, dy       [T, d]          bf16 in      dx [T, d] bf16 out
+ *   w_router    [d, E]          bf16 in      dw_router [d, E] fp32 out
+ *   bias        [E]             fp32 in, may be NULL (zero bias)
+ *   dbias       [E]             fp32 out, may be NULL (not written)
+ *   w_gate, w_up [E, d, d_ff]   bf16 in      dw_gate, dw_up [E, d, d_ff] fp32 out
+ *   w_down      [E, d_ff, d]    bf16 in      dw_down [E, d_ff, d] fp32 out
+ *   dgate       [T, k]          fp32 out, may be NULL (not written)
+ * Gradients overwrite their outputs (no accumulation); an expert with no kept
+ * rows gets zero weight gradients.  Products accumulate in fp32; the expert
+ * pre-activations and the per-row gradients fed to the next product are
+ * rounded to bf16; the sums over tokens and experts run in a fixed order
+ * (the results are deterministic). */
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const float* bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* dy, void* dx, float* dw_router,
+                        float* dbias, float* dw_gate, float* dw_up, float* dw_down, float* dgate,
+                        void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,8 @@ MOE_DROP_TOKEN_ORDER, MOE_DROP_CHOICE_ORDER = 0, 1
 EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_status_string",
            "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_forward", "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp")
+           "moe_forward", "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",
+           "moe_backward_workspace_size", "moe_backward")
 
 
 class CConfig(ctypes.Structure):
@@ -87,9 +88,12 @@ def lib() -> ctypes.CDLL:
         rp = ctypes.POINTER(CMLPRouter)
         L.moe_mlp_router_workspace_size.argtypes = [cp, rp, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_route_mlp.argtypes = [cp, rp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_backward_workspace_size.argtypes = [cp, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_backward.argtypes = [cp] + [_P] * 15 + [ctypes.c_size_t, _P]
         for n in ("moe_route", "moe_route_from_logits", "moe_dispatch", "moe_expert_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
-                  "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp"):
+                  "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",
+                  "moe_backward_workspace_size", "moe_backward"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -346,3 +350,63 @@ class Forward:
 def forward(cfg: MoEConfig, x, w_router, bias, w_gate, w_up, w_down):
     """moe_forward -> y [T, d] (allocates a fresh workspace)."""
     return Forward(cfg, device=x.device)(x, w_router, bias, w_gate, w_up, w_down)
+
+
+def backward_workspace_bytes(cfg: MoEConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_backward_workspace_size(ctypes.byref(cconfig(cfg)), ctypes.byref(n)),
+           "moe_backward_workspace_size")
+    return int(n.value)
+
+
+class Backward:
+    """moe_backward with a workspace allocated once and reused across calls."""
+
+    def __init__(self, cfg: MoEConfig, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.c = cconfig(cfg)
+        self.ws_bytes = backward_workspace_bytes(cfg)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+
+    def __call__(self, x, w_router, bias, w_gate, w_up, w_down, dy, out: Optional[Dict] = None,
+                 want_dgate: bool = True, want_dbias: bool = True) -> Dict:
+        """Gradients dx (layer dtype), dw_router, dbias, dw_gate, dw_up, dw_down and
+        dgate (fp32); ``out`` may hold preallocated tensors under those names."""
+        import torch
+        cfg = self.cfg
+        dev = x.device
+        dt = _dt(cfg)
+        _need(x, "x", dt, (cfg.T, cfg.d), dev)
+        _need(w_router, "w_router", dt, (cfg.d, cfg.E), dev)
+        if bias is not None:
+            _need(bias, "bias", torch.float32, (cfg.E,), dev)
+        _need(w_gate, "w_gate", dt, (cfg.E, cfg.d, cfg.d_ff), dev)
+        _need(w_up, "w_up", dt, (cfg.E, cfg.d, cfg.d_ff), dev)
+        _need(w_down, "w_down", dt, (cfg.E, cfg.d_ff, cfg.d), dev)
+        _need(dy, "dy", dt, (cfg.T, cfg.d), dev)
+        shapes = dict(dx=((cfg.T, cfg.d), dt), dw_router=((cfg.d, cfg.E), torch.float32),
+                      dbias=((cfg.E,), torch.float32),
+                      dw_gate=((cfg.E, cfg.d, cfg.d_ff), torch.float32),
+                      dw_up=((cfg.E, cfg.d, cfg.d_ff), torch.float32),
+                      dw_down=((cfg.E, cfg.d_ff, cfg.d), torch.float32),
+                      dgate=((cfg.T, cfg.k), torch.float32))
+        g = dict(out or {})
+        for name, (shape, tdt) in shapes.items():
+            if (name == "dgate" and not want_dgate) or (name == "dbias" and not want_dbias):
+                g[name] = None
+                continue
+            if g.get(name) is None:
+                g[name] = torch.empty(shape, dtype=tdt, device=dev)
+            _need(g[name], name, tdt, shape, dev)
+        _check(lib().moe_backward(ctypes.byref(self.c), _ptr(x), _ptr(w_router), _ptr(bias),
+                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dy), _ptr(g["dx"]),
+                                  _ptr(g["dw_router"]), _ptr(g["dbias"]), _ptr(g["dw_gate"]),
+                                  _ptr(g["dw_up"]), _ptr(g["dw_down"]), _ptr(g["dgate"]),
+                                  _ptr(self.ws), self.ws_bytes, _stream()), "moe_backward")
+        return g
+
+
+def backward(cfg: MoEConfig, x, w_router, bias, w_gate, w_up, w_down, dy) -> Dict:
+    """moe_backward -> dict of gradients (allocates a fresh workspace)."""
+    return Backward(cfg, device=x.device)(x, w_router, bias, w_gate, w_up, w_down, dy)

@@ -1,0 +1,387 @@
+// backward.hip -- the non-GEMM kernels of the layer's backward pass (bf16
+// layers): GeGLU backward with the gate gradient, softmax/top-k backward into
+// the router logits, the router's weight, bias and input gradients, and the
+// token-side gather-sum of the expert input gradients.
+//
+// Notation (per kept assignment (t, j) of expert e, row r of the expert-
+// grouped layout): g = x Wg[e], u = x Wu[e], a = GELU(g), h = a u,
+// o = h Wd[e], y_t = sum_j gate_tj o_tj.  With dHr = dy_t Wd[e]^T (the
+// gradient of h before the gate):  dgate_tj = dy_t . o = h . dHr, dh = gate
+// dHr, du = dh a, dg = dh u GELU'(g).  The softmax with temperature tau and
+// optional renormalisation over the chosen experts is differentiated in the
+// router kernel; top-k selection and capacity drops are piecewise constant.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Phi(v) and phi(v) (standard normal CDF and density) in fp32: Phi through
+// the complementary error function of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7), whose
+// exp(-z^2) = exp(-v^2 / 2) also gives the density.
+__device__ __forceinline__ void normal_cdf_pdf(float v, float& Phi, float& phi) {
+    const float z = fabsf(v) * 0.70710678118654752440f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float p = fmaf(t, 1.061405429f, -1.453152027f);
+    p = fmaf(t, p, 1.421413741f);
+    p = fmaf(t, p, -0.284496736f);
+    p = fmaf(t, p, 0.254829592f);
+    const float ez = __builtin_amdgcn_exp2f(-z * z * 1.44269504088896341f);
+    const float half_erfc = 0.5f * t * p * ez;
+    Phi = v >= 0.0f ? 1.0f - half_erfc : half_erfc;
+    phi = ez * 0.39894228040143267794f;   // 1 / sqrt(2 pi)
+}
+
+// Sum over the 64 lanes of a wave, the same butterfly order every time.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// One workgroup per row r < n_kept (rows past it exit).  In place: G -> dG,
+// U -> dU.  gH = gate h (bf16), dgate_row[r] = h . dHr.
+__global__ __launch_bounds__(256) void geglu_bwd_kernel(
+    uint16_t* __restrict__ G, uint16_t* __restrict__ U, const float* __restrict__ dHr,
+    uint16_t* __restrict__ gH, float* __restrict__ dgate_row, const int32_t* __restrict__ offset,
+    const int32_t* __restrict__ token_of_row, const int32_t* __restrict__ row_of,
+    const float* __restrict__ gate, int E, int k, int F) {
+    const int r = blockIdx.x;
+    if (r >= offset[E]) return;
+    const int t = token_of_row[r];
+    float gt = 0.f;
+    for (int j = 0; j < k; ++j)
+        if (row_of[(long long)t * k + j] == r) gt = gate[(long long)t * k + j];
+    const long long base = (long long)r * F;
+    float dot = 0.f;
+    for (int c = threadIdx.x * 8; c < F; c += 256 * 8) {
+        const u32x4 gv = *(const u32x4*)(G + base + c);
+        const u32x4 uv = *(const u32x4*)(U + base + c);
+        const f32x4 d0 = *(const f32x4*)(dHr + base + c);
+        const f32x4 d1 = *(const f32x4*)(dHr + base + c + 4);
+        u32x4 dg_o, du_o, gh_o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float dgv[2], duv[2], ghv[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const float g = Elem<uint16_t>::to_f32(gv, 2 * q + s);
+                const float u = Elem<uint16_t>::to_f32(uv, 2 * q + s);
+                const float dh_raw = (2 * q + s < 4) ? d0[2 * q + s] : d1[2 * q + s - 4];
+                float Phi, phi;
+                normal_cdf_pdf(g, Phi, phi);
+                const float a = g * Phi;
+                const float h = a * u;
+                dot = fmaf(h, dh_raw, dot);
+                const float dh = gt * dh_raw;
+                duv[s] = dh * a;
+                dgv[s] = dh * u * fmaf(g, phi, Phi);
+                ghv[s] = gt * h;
+            }
+            dg_o[q] = pack_bf16x2(dgv[0], dgv[1]);
+            du_o[q] = pack_bf16x2(duv[0], duv[1]);
+            gh_o[q] = pack_bf16x2(ghv[0], ghv[1]);
+        }
+        *(u32x4*)(G + base + c) = dg_o;
+        *(u32x4*)(U + base + c) = du_o;
+        *(u32x4*)(gH + base + c) = gh_o;
+    }
+    __shared__ float part[4];
+    dot = wave_sum(dot);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = dot;
+    __syncthreads();
+    if (threadIdx.x == 0) dgate_row[r] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+// One wave per token: p = softmax(l / tau) from the fp32 logits, dp from the
+// gate gradients of the chosen experts (renormalised: gate_j = p_j / S,
+// dp_j = (dgate_j - sum_j' dgate_j' gate_j') / S), dl = p (dp - p . dp) / tau.
+__global__ __launch_bounds__(256) void router_bwd_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ gate, const int32_t* __restrict__ row_of,
+    const float* __restrict__ dgate_row, long long T, int E, int k, float tau, int renorm,
+    float* __restrict__ dl, float* __restrict__ dgate) {
+    __shared__ float sp[4][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const long long t = (long long)blockIdx.x * 4 + w;
+    if (t >= T) return;   // whole wave
+    const float* l = logits + t * E;
+    float lv[4], p[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        lv[q] = e < E ? l[e] : -INFINITY;
+        m = fmaxf(m, lv[q]);
+    }
+    m = wave_max(m);
+    const float sc = 1.44269504088896341f / tau;
+    float z = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        p[q] = e < E ? __builtin_amdgcn_exp2f((lv[q] - m) * sc) : 0.f;
+        z += p[q];
+    }
+    z = wave_sum(z);
+    const float rz = 1.0f / z;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        p[q] *= rz;
+        const int e = lane + 64 * q;
+        if (e < E) sp[w][e] = p[q];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // every lane walks the k choices (k <= 8)
+    float S = 0.f, sg = 0.f;
+    float dga[8];
+    int ej[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        dga[j] = 0.f;
+        ej[j] = -1;
+        if (j < k) {
+            const long long a = t * k + j;
+            const int rr = row_of[a];
+            dga[j] = rr >= 0 ? dgate_row[rr] : 0.f;
+            ej[j] = idx[a];
+            S += sp[w][ej[j]];
+            sg = fmaf(dga[j], gate[a], sg);
+        }
+    }
+    const float rS = 1.0f / S;
+    float dp[4], pd = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        dp[q] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k && ej[j] == e) dp[q] = renorm ? (dga[j] - sg) * rS : dga[j];
+        pd = fmaf(p[q], dp[q], pd);
+    }
+    pd = wave_sum(pd);
+    const float rt = 1.0f / tau;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        if (e < E) dl[t * E + e] = p[q] * (dp[q] - pd) * rt;
+    }
+    if (dgate != nullptr && lane < k) {
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j == lane) v = dga[j];
+        dgate[t * k + lane] = v;
+    }
+}
+
+// dx[t][i] = sum_j dXp[row_of[t, j]][i] + sum_e dl[t][e] Wr[i][e]  (bf16 out).
+// Tile 64 tokens x 64 columns, 4 x 4 per thread, e in chunks of 16 via LDS.
+__global__ __launch_bounds__(256) void dx_kernel(
+    const float* __restrict__ dl, const uint16_t* __restrict__ wr,
+    const float* __restrict__ dXp, const int32_t* __restrict__ row_of, uint16_t* __restrict__ dx,
+    long long T, int d, int E, int k) {
+    __shared__ float s_l[16][64 + 4];
+    __shared__ float s_w[16][64 + 4];
+    const int tid = threadIdx.x, tt = tid >> 4, ti = tid & 15;
+    const long long t0 = (long long)blockIdx.x * 64;
+    const int i0 = blockIdx.y * 64;
+    float acc[4][4] = {};
+    for (int e0 = 0; e0 < E; e0 += 16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int q = tid + 256 * s, mm = q >> 4, kk = q & 15;
+            const long long t = t0 + mm;
+            const int e = e0 + kk;
+            s_l[kk][mm] = (t < T && e < E) ? dl[t * E + e] : 0.f;
+            s_w[kk][mm] = e < E ? bf16_bits_to_f32(wr[(long long)(i0 + mm) * E + e]) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            const f32x4 a = *(const f32x4*)&s_l[kk][tt * 4];
+            const f32x4 b = *(const f32x4*)&s_w[kk][ti * 4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+        }
+        __syncthreads();
+    }
+    const int i = i0 + ti * 4;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const long long t = t0 + tt * 4 + x;
+        if (t >= T) continue;
+        f32x4 v = {acc[x][0], acc[x][1], acc[x][2], acc[x][3]};
+        for (int j = 0; j < k; ++j) {
+            const int rr = row_of[t * k + j];
+            if (rr >= 0) v += *(const f32x4*)(dXp + (long long)rr * d + i);
+        }
+        *(u32x2*)(dx + t * d + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+}
+
+// Partial router weight gradients over one split of the tokens:
+// part[s][i][e] = sum_{t in split s} x[t][i] dl[t][e]; the first column tile
+// also writes bpart[s][e] = sum_t dl[t][e].  Tile 64 (i) x 64 (e).
+__global__ __launch_bounds__(256) void dwr_part_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ dl, float* __restrict__ part,
+    float* __restrict__ bpart, long long T, int d, int E, long long split) {
+    __shared__ float s_x[16][64 + 4];
+    __shared__ float s_l[16][64 + 4];
+    const int tid = threadIdx.x, ti = tid >> 4, te = tid & 15;
+    const int i0 = blockIdx.x * 64, e0 = blockIdx.y * 64, s = blockIdx.z;
+    const long long ta = (long long)s * split, tb = min(T, ta + split);
+    float acc[4][4] = {};
+    float bacc[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool do_b = blockIdx.x == 0 && ti == 0;
+    for (long long tc = ta; tc < tb; tc += 16) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int q = tid + 256 * r, kk = q >> 6, c = q & 63;
+            const long long t = tc + kk;
+            s_x[kk][c] = t < tb ? bf16_bits_to_f32(x[t * d + i0 + c]) : 0.f;
+            s_l[kk][c] = (t < tb && e0 + c < E) ? dl[t * E + e0 + c] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            const f32x4 a = *(const f32x4*)&s_x[kk][ti * 4];
+            const f32x4 b = *(const f32x4*)&s_l[kk][te * 4];
+#pragma unroll
+            for (int xx = 0; xx < 4; ++xx)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[xx][y] = fmaf(a[xx], b[y], acc[xx][y]);
+            if (do_b)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) bacc[y] += b[y];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int xx = 0; xx < 4; ++xx) {
+        const int i = i0 + ti * 4 + xx;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const int e = e0 + te * 4 + y;
+            if (e < E) part[((long long)s * d + i) * E + e] = acc[xx][y];
+        }
+    }
+    if (do_b)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const int e = e0 + te * 4 + y;
+            if (e < E) bpart[(long long)s * E + e] = bacc[y];
+        }
+}
+
+// Sum of the splits in split order: dwr [d][E], dbias [E] (may be null).
+__global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* __restrict__ part,
+                                                         const float* __restrict__ bpart,
+                                                         float* __restrict__ dwr,
+                                                         float* __restrict__ dbias, int d, int E,
+                                                         int nsplit) {
+    const long long n = (long long)d * E;
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (q < n) {
+        float v = 0.f;
+        for (int s = 0; s < nsplit; ++s) v += part[(long long)s * n + q];
+        dwr[q] = v;
+    } else if (dbias != nullptr && q < n + E) {
+        const int e = (int)(q - n);
+        float v = 0.f;
+        for (int s = 0; s < nsplit; ++s) v += bpart[(long long)s * E + e];
+        dbias[e] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, long long n) {
+    for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < n;
+         q += (long long)gridDim.x * 256)
+        p[q] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_geglu_bwd(uint16_t* G, uint16_t* U, const float* dHr, uint16_t* gH,
+                            float* dgate_row, const int32_t* offset, const int32_t* token_of_row,
+                            const int32_t* row_of, const float* gate, int E, int k, int F,
+                            long long max_rows, hipStream_t s) {
+    if (max_rows == 0) return hipSuccess;
+    if (F % 8 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(geglu_bwd_kernel, dim3((unsigned)max_rows), dim3(256), 0, s, G, U, dHr, gH,
+                       dgate_row, offset, token_of_row, row_of, gate, E, k, F);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
+                             const int32_t* row_of, const float* dgate_row, long long T, int E,
+                             int k, float tau, int renorm, float* dl, float* dgate,
+                             hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (E > 256 || k > 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits,
+                       idx, gate, row_of, dgate_row, T, E, k, tau, renorm, dl, dgate);
+    return hipGetLastError();
+}
+
+hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp,
+                     const int32_t* row_of, uint16_t* dx, long long T, int d, int E, int k,
+                     hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (d % 64 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dx_kernel, dim3((unsigned)((T + 63) / 64), d / 64), dim3(256), 0, s, dl,
+                       wr, dXp, row_of, dx, T, d, E, k);
+    return hipGetLastError();
+}
+
+int dwr_splits(long long T, int d, int E) {
+    const long long tiles = (long long)(d / 64) * ((E + 63) / 64);
+    long long ns = (1024 + tiles - 1) / tiles;
+    ns = std::min<long long>(ns, std::max<long long>(1, (T + 63) / 64));
+    return (int)std::max<long long>(1, std::min<long long>(ns, 4096));
+}
+
+size_t dwr_workspace_bytes(long long T, int d, int E) {
+    const int ns = dwr_splits(T, d, E);
+    return (size_t)ns * ((size_t)d * E + E) * sizeof(float);
+}
+
+hipError_t launch_dwr(const uint16_t* x, const float* dl, float* dwr, float* dbias, long long T,
+                      int d, int E, void* ws, hipStream_t s) {
+    if (d % 64 != 0) return hipErrorInvalidValue;
+    const int ns = dwr_splits(T, d, E);
+    const long long split = T == 0 ? 1 : ((T + ns - 1) / ns + 15) / 16 * 16;
+    float* part = (float*)ws;
+    float* bpart = part + (size_t)ns * d * E;
+    hipLaunchKernelGGL(dwr_part_kernel, dim3(d / 64, (E + 63) / 64, ns), dim3(256), 0, s, x, dl,
+                       part, bpart, T, d, E, split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long n = (long long)d * E + E;
+    hipLaunchKernelGGL(dwr_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
+                       bpart, dwr, dbias, d, E, ns);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t s) {
+    if (n == 0 || p == nullptr) return hipSuccess;
+    const long long blocks = std::min<long long>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

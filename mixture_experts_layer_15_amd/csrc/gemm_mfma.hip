@@ -478,14 +478,20 @@ hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const i
                                            cus, s);
 }
 
+hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const int32_t* off,
+                               const uint16_t* B, uint16_t* C, int E, int K, int N,
+                               long long max_rows, int cus, hipStream_t s) {
+    if (small_experts(max_rows, E))
+        return launch_shape<false, 5, 4, 64, 2, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0,
+                                                      E, K, N, max_rows, cus, s);
+    return launch_shape<false, 8, 4, 64, 2, 2>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E, K,
+                                               N, max_rows, cus, s);
+}
+
 hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_t* w_down,
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
                             int cus, hipStream_t s) {
-    if (small_experts(max_rows, E))
-        return launch_shape<false, 5, 4, 64, 2, 4, 4>(h, w_down, nullptr, y_perm, off, nullptr, 0, nullptr, 0, E, d_ff, d,
-                                                 max_rows, cus, s);
-    return launch_shape<false, 8, 4, 64, 2, 2>(h, w_down, nullptr, y_perm, off, nullptr, 0, nullptr, 0, E, d_ff, d,
-                                            max_rows, cus, s);
+    return launch_mfma_grouped(h, nullptr, off, w_down, y_perm, E, d_ff, d, max_rows, cus, s);
 }
 
 // Dense bf16 GEMM C [M][N] = A [M][K] B [K][N] (+ bias[N]) (GELU when act ==

@@ -71,6 +71,12 @@ hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
                             int cus, hipStream_t s);
 
+// Plain grouped GEMM C[rows][N] = A[rows][K] B[e] (bf16 out), A's rows read
+// directly (a_rows == nullptr) or gathered through a_rows (gemm_mfma.hip).
+hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const int32_t* off,
+                               const uint16_t* B, uint16_t* C, int E, int K, int N,
+                               long long max_rows, int cus, hipStream_t s);
+
 // Dense bf16 GEMM with optional bias and GELU epilogue (gemm_mfma.hip).
 hipError_t launch_mfma_dense(const uint16_t* A, const uint16_t* B, const float* bias, int act,
                              uint16_t* C, int M, int K, int N, int cus, hipStream_t s);
@@ -91,5 +97,35 @@ hipError_t launch_route_mlp(const uint16_t* x, const uint16_t* prev, float gamma
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
                           const float* gate, void* y, long long T, int d, int k,
                           hipStream_t s);
+
+// Backward GEMMs (gemm_bw.hip), fp32 results.
+// NT: C[r][N] (+)= A[r'][K] W[e]^T over the rows r of each expert, W[e] stored
+// [N][K]; r' = act_rows[r] when act_rows is given.
+hipError_t launch_bw_nt(const uint16_t* act, const int32_t* act_rows, const uint16_t* W,
+                        float* C, const int32_t* off, int E, int N, int K, long long max_rows,
+                        bool accumulate, hipStream_t s);
+// TN: C[e][M][N] = sum over the rows r of expert e of A[a(r)][m] B[b(r)][n]
+// (a(r) = a_rows[r] or r, likewise b): the weight gradients, a ragged
+// reduction length per expert; experts with no rows get zeros.
+hipError_t launch_bw_tn(const uint16_t* A, const int32_t* a_rows, const uint16_t* B,
+                        const int32_t* b_rows, float* C, const int32_t* off, int E, int M, int N,
+                        hipStream_t s);
+
+// Backward elementwise and router kernels (backward.hip).
+hipError_t launch_geglu_bwd(uint16_t* G, uint16_t* U, const float* dHr, uint16_t* gH,
+                            float* dgate_row, const int32_t* offset, const int32_t* token_of_row,
+                            const int32_t* row_of, const float* gate, int E, int k, int F,
+                            long long max_rows, hipStream_t s);
+hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
+                             const int32_t* row_of, const float* dgate_row, long long T, int E,
+                             int k, float tau, int renorm, float* dl, float* dgate,
+                             hipStream_t s);
+hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp,
+                     const int32_t* row_of, uint16_t* dx, long long T, int d, int E, int k,
+                     hipStream_t s);
+size_t dwr_workspace_bytes(long long T, int d, int E);
+hipError_t launch_dwr(const uint16_t* x, const float* dl, float* dwr, float* dbias, long long T,
+                      int d, int E, void* ws, hipStream_t s);
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t s);
 
 }  // namespace moe

@@ -432,3 +432,154 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
 }
 
 }  // extern "C"
+
+namespace {
+
+// bf16 backward: the forward's maps, then the recomputed pre-activations and
+// the gradients of every product.  x_perm only when x is too large to be
+// gathered through 32-bit offsets.
+struct BwdLayout {
+    size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, G, U, gH, dHr,
+        dXp, dgrow, dl, dwr, total;
+    bool gather;
+};
+
+BwdLayout bwd_layout(const moe_config* c) {
+    const size_t T = (size_t)c->T, E = (size_t)c->E, k = (size_t)c->k, d = (size_t)c->d;
+    const size_t F = (size_t)c->d_ff, R = (size_t)max_rows(c);
+    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy);
+    BwdLayout L;
+    L.gather = T * d * 2 < ((size_t)1 << 32);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+    L.logits = take(T * E * 4);
+    L.idx = take(T * k * 4);
+    L.gate = take(T * k * 4);
+    L.count = take(E * 4);
+    L.offset = take((E + 1) * 4);
+    L.row_of = take(T * k * 4);
+    L.token_of_row = take(T * k * 4);
+    L.dsp = take(moe::dispatch_workspace_bytes(p));
+    L.x_perm = take(L.gather ? 0 : R * d * 2);
+    L.G = take(R * F * 2);
+    L.U = take(R * F * 2);
+    L.gH = take(R * F * 2);
+    L.dHr = take(R * F * 4);
+    L.dXp = take(R * d * 4);
+    L.dgrow = take(R * 4);
+    L.dl = take(T * E * 4);
+    L.dwr = take(moe::dwr_workspace_bytes(c->T, c->d, c->E));
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
+    CHECK(check_cfg(cfg));
+    if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
+    *bytes = bwd_layout(cfg).total;
+    return MOE_OK;
+}
+
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const float* bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* dy, void* dx, float* dw_router,
+                        float* dbias, float* dw_gate, float* dw_up, float* dw_down, float* dgate,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    CHECK(check_cfg(cfg));
+    if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
+    SIZES(cfg);
+    CHECK(check_ptr(x, "x", T * d * es));
+    CHECK(check_ptr(w_router, "w_router", d * E * es));
+    CHECK(check_ptr(bias, "bias", E * 4, true));
+    CHECK(check_ptr(w_gate, "w_gate", E * d * F * es));
+    CHECK(check_ptr(w_up, "w_up", E * d * F * es));
+    CHECK(check_ptr(w_down, "w_down", E * d * F * es));
+    CHECK(check_ptr(dy, "dy", T * d * es));
+    CHECK(check_ptr(dx, "dx", T * d * es));
+    CHECK(check_ptr(dw_router, "dw_router", d * E * 4));
+    CHECK(check_ptr(dbias, "dbias", E * 4, true));
+    CHECK(check_ptr(dw_gate, "dw_gate", E * d * F * 4));
+    CHECK(check_ptr(dw_up, "dw_up", E * d * F * 4));
+    CHECK(check_ptr(dw_down, "dw_down", E * d * F * 4));
+    CHECK(check_ptr(dgate, "dgate", T * k * 4, true));
+    const BwdLayout L = bwd_layout(cfg);
+    if (workspace == nullptr || ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE, "backward workspace: need %zu bytes, got %zu", L.total, ws_bytes);
+    CHECK(check_ptr(workspace, "workspace", 1));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+#define BWD(call, where)                                   \
+    do {                                                   \
+        e = (call);                                        \
+        if (e != hipSuccess) return hip_fail(e, where);    \
+    } while (0)
+    if (T == 0) {   // no tokens: every weight gradient is zero
+        BWD(moe::launch_zero_f32(dw_router, (long long)(d * E), s), "moe_backward/zero");
+        BWD(moe::launch_zero_f32(dbias, (long long)E, s), "moe_backward/zero");
+        BWD(moe::launch_zero_f32(dw_gate, (long long)(E * d * F), s), "moe_backward/zero");
+        BWD(moe::launch_zero_f32(dw_up, (long long)(E * d * F), s), "moe_backward/zero");
+        BWD(moe::launch_zero_f32(dw_down, (long long)(E * d * F), s), "moe_backward/zero");
+        return MOE_OK;
+    }
+    char* w = (char*)workspace;
+    float* logits = (float*)(w + L.logits);
+    int32_t* idx = (int32_t*)(w + L.idx);
+    float* gate = (float*)(w + L.gate);
+    int32_t* count = (int32_t*)(w + L.count);
+    int32_t* offset = (int32_t*)(w + L.offset);
+    int32_t* row_of = (int32_t*)(w + L.row_of);
+    int32_t* tor = (int32_t*)(w + L.token_of_row);
+    uint16_t* G = (uint16_t*)(w + L.G);
+    uint16_t* U = (uint16_t*)(w + L.U);
+    uint16_t* gH = (uint16_t*)(w + L.gH);
+    float* dHr = (float*)(w + L.dHr);
+    float* dXp = (float*)(w + L.dXp);
+    float* dgrow = (float*)(w + L.dgrow);
+    float* dl = (float*)(w + L.dl);
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* dyb = (const uint16_t*)dy;
+    const int Ei = cfg->E, di = cfg->d, Fi = cfg->d_ff, ki = cfg->k;
+    const long long Rl = max_rows(cfg);
+    const int cus = gemm_grid_cap();
+
+    // forward recompute: routing, dispatch maps, g = x W_gate, u = x W_up
+    BWD(moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T, di, Ei, ki,
+                          cfg->temperature, cfg->renormalize, s), "moe_backward/route");
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, Ei, ki, capacity_eff(cfg), cfg->drop_policy);
+    BWD(moe::launch_dispatch(p, cfg->dtype, idx, x, w + L.x_perm, count, offset, row_of, tor,
+                             w + L.dsp, di, s, !L.gather), "moe_backward/dispatch");
+    const uint16_t* a_src = L.gather ? xb : (const uint16_t*)(w + L.x_perm);
+    const int32_t* a_rows = L.gather ? tor : nullptr;
+    BWD(moe::launch_mfma_grouped(a_src, a_rows, offset, (const uint16_t*)w_gate, G, Ei, di, Fi,
+                                 Rl, cus, s), "moe_backward/gate");
+    BWD(moe::launch_mfma_grouped(a_src, a_rows, offset, (const uint16_t*)w_up, U, Ei, di, Fi,
+                                 Rl, cus, s), "moe_backward/up");
+    // dHr = dy W_down^T per kept row, then the GeGLU backward and dgate
+    BWD(moe::launch_bw_nt(dyb, tor, (const uint16_t*)w_down, dHr, offset, Ei, Fi, di, Rl, false, s),
+        "moe_backward/dh");
+    BWD(moe::launch_geglu_bwd(G, U, dHr, gH, dgrow, offset, tor, row_of, gate, Ei, ki, Fi, Rl, s),
+        "moe_backward/geglu");
+    // G, U now hold dg, du
+    BWD(moe::launch_bw_nt(G, nullptr, (const uint16_t*)w_gate, dXp, offset, Ei, di, Fi, Rl, false, s),
+        "moe_backward/dx_gate");
+    BWD(moe::launch_bw_nt(U, nullptr, (const uint16_t*)w_up, dXp, offset, Ei, di, Fi, Rl, true, s),
+        "moe_backward/dx_up");
+    BWD(moe::launch_bw_tn(xb, tor, G, nullptr, dw_gate, offset, Ei, di, Fi, s), "moe_backward/dw_gate");
+    BWD(moe::launch_bw_tn(xb, tor, U, nullptr, dw_up, offset, Ei, di, Fi, s), "moe_backward/dw_up");
+    BWD(moe::launch_bw_tn(gH, nullptr, dyb, tor, dw_down, offset, Ei, Fi, di, s), "moe_backward/dw_down");
+    // router: dlogit, then dx and the router's weight and bias gradients
+    BWD(moe::launch_router_bwd(logits, idx, gate, row_of, dgrow, cfg->T, Ei, ki, cfg->temperature,
+                               cfg->renormalize, dl, dgate, s), "moe_backward/router");
+    BWD(moe::launch_dx(dl, (const uint16_t*)w_router, dXp, row_of, (uint16_t*)dx, cfg->T, di, Ei,
+                       ki, s), "moe_backward/dx");
+    BWD(moe::launch_dwr(xb, dl, dw_router, dbias, cfg->T, di, Ei, w + L.dwr, s), "moe_backward/dwr");
+#undef BWD
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -11,6 +11,8 @@ independently and large tensors never need a full-size fp32 temporary):
 * W_r ~ N(0, 1/d)                     shape [d, E]      (router, fan_in = d)
 * W_gate, W_up ~ N(0, 1/d)            shape [E, d, d_ff] (fan_in = d)
 * W_down ~ N(0, 1/d_ff)               shape [E, d_ff, d] (fan_in = d_ff)
+* dy ~ N(0, 1)                        shape [T, d]      (upstream gradient of y,
+  for the backward)
 * router bias: none (zero-initialised gate bias, TorchTitan 1K-GPU article
   section 4.2), except for the skewed-routing case, where b_e is the fp32
   rounding of ln p_e with p_e = (e+1)^-s / sum_i i^-s (a Zipf(s) prior over
@@ -30,7 +32,7 @@ import torch
 
 from .configs import MoEConfig
 
-_TENSOR_ID = {"x": 0, "w_router": 1, "w_gate": 2, "w_up": 3, "w_down": 4}
+_TENSOR_ID = {"x": 0, "w_router": 1, "w_gate": 2, "w_up": 3, "w_down": 4, "dy": 5}
 
 
 def torch_dtype(cfg: MoEConfig) -> torch.dtype:
@@ -82,3 +84,8 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, device: str = "cpu",
             w[e] = _normal(shape, 1.0 / math.sqrt(fan_in), dt, device, seed, name, e)
         out[name] = w
     return out
+
+
+def make_dy(cfg: MoEConfig, seed: int = 0, device: str = "cpu") -> torch.Tensor:
+    """Upstream gradient dL/dy [T, d] in the layer's dtype, N(0, 1)."""
+    return _normal((cfg.T, cfg.d), 1.0, torch_dtype(cfg), device, seed, "dy", 0)

@@ -359,9 +359,9 @@ void orc_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t d_ff, int 
     double* dxa = (double*)calloc((size_t)(T * k * d), sizeof(double));   /* per assignment */
     double* dga = (double*)calloc((size_t)(T * k), sizeof(double));
     double* dl = (double*)calloc((size_t)(T * E), sizeof(double));
-    memset(dwg, 0, sizeof(double) * (size_t)(E * d * d_ff));
-    memset(dwu, 0, sizeof(double) * (size_t)(E * d * d_ff));
-    memset(dwd, 0, sizeof(double) * (size_t)(E * d_ff * d));
+    if (dwg) memset(dwg, 0, sizeof(double) * (size_t)(E * d * d_ff));
+    if (dwu) memset(dwu, 0, sizeof(double) * (size_t)(E * d * d_ff));
+    if (dwd) memset(dwd, 0, sizeof(double) * (size_t)(E * d_ff * d));
     #pragma omp parallel
     {
         double* g = (double*)malloc(sizeof(double) * (size_t)d_ff);
@@ -398,7 +398,7 @@ void orc_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t d_ff, int 
                         int64_t wrow = (e * d_ff + n) * d;
                         for (int64_t c = 0; c < d; ++c) {
                             s += dO[c] * load(wd, wrow + c, dtype);
-                            dwd[wrow + c] += h[n] * dO[c];
+                            if (dwd) dwd[wrow + c] += h[n] * dO[c];
                         }
                         dh[n] = s;
                     }
@@ -413,8 +413,8 @@ void orc_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t d_ff, int 
                         int64_t wrow = (e * d + i) * d_ff;
                         for (int64_t n = 0; n < d_ff; ++n) {
                             s += g[n] * load(wg, wrow + n, dtype) + u[n] * load(wu, wrow + n, dtype);
-                            dwg[wrow + n] += xi * g[n];
-                            dwu[wrow + n] += xi * u[n];
+                            if (dwg) dwg[wrow + n] += xi * g[n];
+                            if (dwu) dwu[wrow + n] += xi * u[n];
                         }
                         dxa[a * d + i] = s;
                     }
@@ -459,19 +459,69 @@ void orc_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t d_ff, int 
         }
         free(dp); free(p);
     }
-    #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < d; ++i)
+    if (dwr) {
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < d; ++i)
+            for (int64_t e = 0; e < E; ++e) {
+                double s = 0.0;
+                for (int64_t t = 0; t < T; ++t) s += load(x, t * d + i, dtype) * dl[t * E + e];
+                dwr[i * E + e] = s;
+            }
+    }
+    if (db) {
         for (int64_t e = 0; e < E; ++e) {
             double s = 0.0;
-            for (int64_t t = 0; t < T; ++t) s += load(x, t * d + i, dtype) * dl[t * E + e];
-            dwr[i * E + e] = s;
+            for (int64_t t = 0; t < T; ++t) s += dl[t * E + e];
+            db[e] = s;
         }
-    for (int64_t e = 0; e < E; ++e) {
-        double s = 0.0;
-        for (int64_t t = 0; t < T; ++t) s += dl[t * E + e];
-        db[e] = s;
     }
     free(dxa); free(dga); free(dl);
+}
+
+/* Single entries of the expert weight gradients, each summed straight from
+ * its definition over the kept assignments (t, j) of expert e, tokens
+ * ascending (same quantities as in orc_backward):
+ *   which 0: dWg[e][a][b] = sum x_t[a] dg_t[b]
+ *   which 1: dWu[e][a][b] = sum x_t[a] du_t[b]
+ *   which 2: dWd[e][a][b] = sum gate_tj h_t[a] dy_t[b]
+ * where for column n: g_t[n] = sum_i x_t[i] Wg[e][i][n], u_t[n] likewise,
+ * h = GELU(g) u, dh_t[n] = gate_tj sum_c dy_t[c] Wd[e][n][c],
+ * du = dh GELU(g), dg = dh u GELU'(g).  Costs O(rows of e * d) per entry,
+ * so a few entries can be checked at any layer size. */
+void orc_backward_wentries(int64_t T, int64_t d, int64_t k, int64_t d_ff, int dtype,
+                           const void* x, const int32_t* idx, const double* gate,
+                           const int32_t* row_of, const void* wg, const void* wu, const void* wd,
+                           const double* dy, int64_t n_ent, const int64_t* which,
+                           const int64_t* ent_e, const int64_t* ent_a, const int64_t* ent_b,
+                           double* out) {
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < n_ent; ++q) {
+        const int64_t e = ent_e[q], a = ent_a[q], b = ent_b[q];
+        const int64_t n = which[q] == 2 ? a : b;   /* the d_ff column involved */
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t j = 0; j < k; ++j) {
+                const int64_t s = t * k + j;
+                if (idx[s] != e || row_of[s] < 0) continue;
+                double g = 0.0, u = 0.0;
+                for (int64_t i = 0; i < d; ++i) {
+                    const double xi = load(x, t * d + i, dtype);
+                    g += xi * load(wg, (e * d + i) * d_ff + n, dtype);
+                    u += xi * load(wu, (e * d + i) * d_ff + n, dtype);
+                }
+                const double act = gelu(g);
+                if (which[q] == 2) {
+                    acc += gate[s] * (act * u) * dy[t * d + b];
+                    continue;
+                }
+                double dh = 0.0;
+                for (int64_t c = 0; c < d; ++c) dh += dy[t * d + c] * load(wd, (e * d_ff + n) * d + c, dtype);
+                dh *= gate[s];
+                const double xa = load(x, t * d + a, dtype);
+                acc += which[q] == 0 ? xa * dh * u * gelu_grad(g) : xa * dh * act;
+            }
+        out[q] = acc;
+    }
 }
 
 /* Step 6 -- gate-weighted combine for a list of tokens.

@@ -17,7 +17,7 @@ import ctypes
 import os
 import subprocess
 import threading
-from typing import Dict, Optional, Sequence
+from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -72,6 +72,9 @@ def _declare(lib):
     lib.orc_backward.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_double,
                                  ctypes.c_int] + [_P] * 17
     lib.orc_backward.restype = None
+    lib.orc_backward_wentries.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_int] + [_P] * 8 + \
+        [_I64] + [_P] * 5
+    lib.orc_backward_wentries.restype = None
     lib.orc_ffn_rows.argtypes = [_I64, _P, _P, _I64, _I64, ctypes.c_int,
                                  _P, _P, _P, _P, _P, _P]
     lib.orc_ffn_rows.restype = None
@@ -220,10 +223,16 @@ def mlp_router(x, prev, gamma: float, eps: float, wd, bd, w1, b1, w2, b2, w3, b3
 
 def backward(x, w_router, bias, w_gate, w_up, w_down, dy, *, k: int, tau: float,
              renormalize: bool, cap_num: int, cap_den: int, drop_policy: int = 0,
-             logits_in: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+             logits_in: Optional[np.ndarray] = None,
+             tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Gradients of the layer for an upstream dy [T, d] (fp64 or castable), in
     fp64: dx, dw_router, dbias, dw_gate, dw_up, dw_down, dgate, plus the routing
-    they used.  Routing as in forward(): from logits_in when given."""
+    they used.  Routing as in forward(): from logits_in when given.
+
+    ``tokens`` limits the computation to the listed tokens (routing, capacity
+    and dispatch still cover the whole batch): only dx and dgate are returned,
+    one row per listed token -- they depend on nothing but that token's own
+    routing, inputs and upstream gradient."""
     xr, dt = _raw(x)
     T, d = xr.shape
     wrr, _ = _raw(w_router)
@@ -238,16 +247,58 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, dy, *, k: int, tau: float,
     C = capacity(T, E, k, cap_num, cap_den)
     dsp = dispatch(idx, E, C, drop_policy)
     dyr = np.ascontiguousarray(np.asarray(dy, dtype=np.float64))
+    row_of = dsp["row_of"]
+    if tokens is not None:
+        toks = np.asarray(tokens, dtype=np.int64)
+        n = toks.shape[0]
+        sub = lambda a: np.ascontiguousarray(a[toks])
+        out = dict(dx=np.empty((n, d)), dgate=np.empty((n, k)))
+        _load().orc_backward(n, d, E, k, d_ff, dt, float(tau), int(bool(renormalize)),
+                             _ptr(sub(xr)), _ptr(wrr), _ptr(sub(lg)), _ptr(sub(idx)),
+                             _ptr(sub(gate)), _ptr(sub(row_of)), _ptr(wgr), _ptr(wur), _ptr(wdr),
+                             _ptr(sub(dyr)), _ptr(out["dx"]), None, None, None, None, None,
+                             _ptr(out["dgate"]))
+        out.update(logits=lg, idx=idx, gate=gate, row_of=row_of, C=C, tokens=toks)
+        return out
     out = dict(dx=np.empty((T, d)), dw_router=np.empty((d, E)), dbias=np.empty(E),
                dw_gate=np.empty((E, d, d_ff)), dw_up=np.empty((E, d, d_ff)),
                dw_down=np.empty((E, d_ff, d)), dgate=np.empty((T, k)))
     _load().orc_backward(T, d, E, k, d_ff, dt, float(tau), int(bool(renormalize)), _ptr(xr),
                          _ptr(wrr), _ptr(lg), _ptr(idx), _ptr(np.ascontiguousarray(gate)),
-                         _ptr(dsp["row_of"]), _ptr(wgr), _ptr(wur), _ptr(wdr), _ptr(dyr),
+                         _ptr(row_of), _ptr(wgr), _ptr(wur), _ptr(wdr), _ptr(dyr),
                          _ptr(out["dx"]), _ptr(out["dw_router"]), _ptr(out["dbias"]),
                          _ptr(out["dw_gate"]), _ptr(out["dw_up"]), _ptr(out["dw_down"]),
                          _ptr(out["dgate"]))
-    out.update(logits=lg, idx=idx, gate=gate, row_of=dsp["row_of"], C=C)
+    out.update(logits=lg, idx=idx, gate=gate, row_of=row_of, C=C)
+    return out
+
+
+WGRAD = {"dw_gate": 0, "dw_up": 1, "dw_down": 2}
+
+
+def backward_weight_entries(x, w_gate, w_up, w_down, dy, idx, gate, row_of,
+                            entries: Sequence[Tuple[str, int, int, int]]) -> np.ndarray:
+    """Single entries (name, e, a, b) of dw_gate [E, d, d_ff], dw_up or
+    dw_down [E, d_ff, d], each summed from its definition over the kept rows
+    of expert e (routing idx, gate, row_of as returned by backward/forward)."""
+    xr, dt = _raw(x)
+    T, d = xr.shape
+    wgr, _ = _raw(w_gate)
+    wur, _ = _raw(w_up)
+    wdr, _ = _raw(w_down)
+    d_ff = wgr.shape[2]
+    k = np.asarray(idx).shape[1]
+    which = np.array([WGRAD[n] for n, _, _, _ in entries], dtype=np.int64)
+    ee = np.array([e for _, e, _, _ in entries], dtype=np.int64)
+    aa = np.array([a for _, _, a, _ in entries], dtype=np.int64)
+    bb = np.array([b for _, _, _, b in entries], dtype=np.int64)
+    out = np.empty(len(entries))
+    _load().orc_backward_wentries(
+        T, d, k, d_ff, dt, _ptr(xr), _ptr(np.ascontiguousarray(idx, dtype=np.int32)),
+        _ptr(np.ascontiguousarray(gate, dtype=np.float64)),
+        _ptr(np.ascontiguousarray(row_of, dtype=np.int32)), _ptr(wgr), _ptr(wur), _ptr(wdr),
+        _ptr(np.ascontiguousarray(np.asarray(dy, dtype=np.float64))), len(entries), _ptr(which),
+        _ptr(ee), _ptr(aa), _ptr(bb), _ptr(out))
     return out
 
 

@@ -195,3 +195,42 @@ def test_python_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoe_mi355x.so")
     with pytest.raises(RuntimeError, match="not found"):
         moe.lib()
+
+
+def test_backward_validation_on_host(L):
+    cfg = configs.get("zaya1")
+    c = moe.cconfig(cfg)
+    n = ctypes.c_size_t(0)
+    assert L.moe_backward_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0
+    R, T, d, E, F, k = moe.max_rows(cfg), cfg.T, cfg.d, cfg.E, cfg.d_ff, cfg.k
+    # the recomputed pre-activations, dg/du in place, gate * h, dh (fp32), the
+    # expert input gradients (fp32), the routing maps and the logit gradients
+    assert n.value >= R * F * (3 * 2 + 4) + R * d * 4 + T * E * 4 * 2 + T * k * 4 * 4
+    assert n.value < R * F * 10 + R * d * 4 + T * E * 8 + T * k * 16 + (64 << 20)
+    f32 = moe.cconfig(configs.get("tiny"))
+    assert L.moe_backward_workspace_size(ctypes.byref(f32), ctypes.byref(n)) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_backward_workspace_size(ctypes.byref(c), None) == moe.MOE_ERR_INVALID_ARG
+    ok = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    big = 1 << 40
+
+    def call(**over):
+        a = dict(x=ok, wr=ok, bias=None, wg=ok, wu=ok, wd=ok, dy=ok, dx=ok, dwr=ok, db=None,
+                 dwg=ok, dwu=ok, dwd=ok, dgate=None, ws=ok, nbytes=big)
+        a.update(over)
+        return L.moe_backward(ctypes.byref(c), a["x"], a["wr"], a["bias"], a["wg"], a["wu"],
+                              a["wd"], a["dy"], a["dx"], a["dwr"], a["db"], a["dwg"], a["dwu"],
+                              a["dwd"], a["dgate"], a["ws"], a["nbytes"], None)
+    for name in ("x", "dy", "dx", "dwr", "dwg", "dwu", "dwd", "wd"):
+        assert call(**{name: None}) == moe.MOE_ERR_INVALID_ARG
+        assert b"is NULL" in L.moe_last_error()
+    assert call(dwg=odd) == moe.MOE_ERR_INVALID_ARG
+    assert b"aligned" in L.moe_last_error()
+    assert call(nbytes=n.value - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=None) == moe.MOE_ERR_WORKSPACE
+    c32 = moe.cconfig(configs.get("tiny"))
+    assert L.moe_backward(ctypes.byref(c32), *([ok] * 15), big, None) == moe.MOE_ERR_UNSUPPORTED
+    bad = moe.cconfig(cfg)
+    bad.k = 0
+    assert L.moe_backward(ctypes.byref(bad), *([ok] * 15), big, None) == moe.MOE_ERR_INVALID_ARG

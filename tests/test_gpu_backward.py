@@ -1,0 +1,180 @@
+"""GPU parity of the layer's backward (moe_backward, bf16 layers) against the
+fp64 oracle's analytic gradients (themselves pinned by finite differences),
+through the C ABI.
+
+Routing follows the same-fp32-logits protocol: the oracle ranks the logits
+the GPU router produced (moe_route; moe_backward recomputes them with the same
+kernel, so both see one routing).  Every gradient must lie within 2e-2 of the
+largest oracle magnitude of that gradient, the bar of the bf16 forward: the
+inputs are exact bf16 values, the products accumulate in fp32, and the
+intermediates that feed a further product (g, u, dg, du, gate h) are rounded
+once to bf16, a relative 2^-9 per element; summed with random signs that
+stays near 2^-9 of the result's scale.
+
+Small layers compare every output; the full-size layers compare dx and dgate
+of sampled tokens, sampled entries of the expert weight gradients (each summed
+by the oracle from its definition), and the router gradients through a
+property that holds at any size (the softmax backward sums to zero over the
+experts of each token)."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_15_amd as moe
+from mixture_experts_layer_15_amd import configs, synthetic
+from oracle import oracle as orc
+
+from parity_util import check_route, gpu_inputs, rel_err, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+GRADS = ("dx", "dw_router", "dbias", "dw_gate", "dw_up", "dw_down", "dgate")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+BASE = configs.get("tiny").scaled(dtype="bf16")
+CASES = {
+    # top-2 renormalised, capacity 5/4 (drops), rows span several 128-row tiles
+    "bw_renorm_drops": BASE.scaled(T=512, d=256, E=8, k=2, d_ff=512, temperature=0.7,
+                                   renormalize=True, cap_num=5, cap_den=4),
+    # top-1 raw gate, no capacity limit (the ZAYA1 routing shape)
+    "bw_top1_raw": BASE.scaled(T=384, d=128, E=4, k=1, d_ff=256),
+    # top-3, choice-order drops, E not a multiple of 8, T and d_ff off the tile grid
+    "bw_k3_choice": BASE.scaled(T=300, d=192, E=6, k=3, d_ff=320, temperature=0.5,
+                                cap_num=3, cap_den=4, drop_policy=1),
+    # skewed routing through a Zipf bias, low temperature, capacity 1.0
+    "bw_zipf_bias": BASE.scaled(T=1000, d=128, E=16, k=2, d_ff=128, temperature=0.3,
+                                renormalize=True, cap_num=1, cap_den=1, zipf_bias=1.2),
+    # one expert: the router gets no gradient at all
+    "bw_one_expert": BASE.scaled(T=200, d=64, E=1, k=1, d_ff=64),
+    # capacity 0: every assignment dropped, every gradient zero
+    "bw_all_dropped": BASE.scaled(T=256, d=64, E=4, k=2, d_ff=128, cap_num=0, cap_den=1),
+}
+
+
+def _oracle_kw(cfg):
+    return dict(k=cfg.k, tau=float(np.float32(cfg.temperature)), renormalize=cfg.renormalize,
+                cap_num=cfg.cap_num, cap_den=cfg.cap_den, drop_policy=cfg.drop_policy)
+
+
+def _gpu_backward(cfg, dev, dy):
+    say(f"[{cfg.name}] moe_route + moe_backward T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} "
+        f"d_ff={cfg.d_ff}")
+    logits, idx, gate = moe.route(cfg, dev["x"], dev["w_router"], dev["bias"])
+    g = moe.backward(cfg, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                     dev["w_down"], dy)
+    torch.cuda.synchronize()
+    return logits.cpu(), idx.cpu(), gate.cpu(), g
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_small(name):
+    cfg = CASES[name].scaled(name=name)
+    dev, host = gpu_inputs(cfg, seed=3)
+    dy_h = synthetic.make_dy(cfg, seed=3, device="cpu")
+    lg, idx, gate, g = _gpu_backward(cfg, dev, dy_h.cuda())
+    check_route(cfg, lg, idx, gate)
+    ob = orc.backward(host["x"], host["w_router"], host["bias"], host["w_gate"], host["w_up"],
+                      host["w_down"], dy_h.double().numpy(), logits_in=lg.double().numpy(),
+                      **_oracle_kw(cfg))
+    for n in GRADS:
+        err = rel_err(to_np(g[n]), ob[n])
+        say(f"[{name}] {n} err {err:.3g} (max |oracle| {np.abs(ob[n]).max():.3g})")
+        assert err <= TOL, f"{n}: {err}"
+    if name == "bw_one_expert":   # p = 1 exactly: no router gradient
+        assert (g["dw_router"] == 0).all() and (g["dbias"] == 0).all()
+    if name == "bw_all_dropped":
+        for n in GRADS:
+            assert (g[n].float() == 0).all(), n
+    # no atomics anywhere: a second call is bit-identical
+    g2 = moe.backward(cfg, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                      dev["w_down"], dy_h.cuda())
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(g[n], g2[n]), f"{n} differs between two calls"
+
+
+def test_backward_no_tokens_zeroes_the_weight_gradients():
+    cfg = CASES["bw_renorm_drops"].scaled(name="bw_empty", T=0)
+    dev, _ = gpu_inputs(cfg, seed=1)
+    dy = torch.empty((0, cfg.d), dtype=torch.bfloat16, device="cuda")
+    out = {n: None for n in GRADS}
+    for n, shape in (("dw_router", (cfg.d, cfg.E)), ("dbias", (cfg.E,)),
+                     ("dw_gate", (cfg.E, cfg.d, cfg.d_ff)), ("dw_up", (cfg.E, cfg.d, cfg.d_ff)),
+                     ("dw_down", (cfg.E, cfg.d_ff, cfg.d))):
+        out[n] = torch.full(shape, 7.0, dtype=torch.float32, device="cuda")
+    say("[bw_empty] moe_backward T=0")
+    g = moe.Backward(cfg)(dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                          dev["w_down"], dy, out=out)
+    torch.cuda.synchronize()
+    for n in ("dw_router", "dbias", "dw_gate", "dw_up", "dw_down"):
+        assert (g[n] == 0).all(), n
+
+
+def _sample_tokens(cfg, row_of, rng, n=24):
+    dropped = np.nonzero((row_of < 0).any(1))[0]
+    pick = np.concatenate([[0, cfg.T - 1], dropped[:4], rng.integers(0, cfg.T, size=n)])
+    return np.unique(pick)
+
+
+@pytest.mark.parametrize("name", ["zaya1", "skewed"])
+def test_backward_full_size_sampled(name):
+    cfg = configs.get(name)
+    dev, host = gpu_inputs(cfg, seed=0)
+    dy = synthetic.make_dy(cfg, seed=0, device="cuda")
+    dy_h = dy.cpu()
+    lg, idx, gate, g = _gpu_backward(cfg, dev, dy)
+    rng = np.random.default_rng(11)
+    oidx, _, _ = check_route(cfg, lg, idx, gate)
+    kw = _oracle_kw(cfg)
+    lgn = lg.double().numpy()
+    C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    row_of = orc.dispatch(oidx, cfg.E, C, cfg.drop_policy)["row_of"]
+    toks = _sample_tokens(cfg, row_of, rng)
+    say(f"[{name}] oracle dx, dgate of {toks.size} tokens")
+    ob = orc.backward(host["x"], host["w_router"], host["bias"], host["w_gate"], host["w_up"],
+                      host["w_down"], dy_h.double().numpy(), logits_in=lgn, tokens=toks, **kw)
+    tk = torch.from_numpy(toks).cuda()
+    for n in ("dx", "dgate"):
+        err = rel_err(to_np(g[n].index_select(0, tk)), ob[n])
+        say(f"[{name}] {n} err {err:.3g} over {toks.size} tokens")
+        assert err <= TOL, f"{n}: {err}"
+    # sampled expert weight-gradient entries, the busiest and the idlest expert included
+    count = np.bincount(oidx[row_of >= 0].ravel(), minlength=cfg.E)
+    experts = [int(count.argmax()), int(count.argmin())] + rng.integers(0, cfg.E, 6).tolist()
+    ents = []
+    for n, shape in (("dw_gate", (cfg.d, cfg.d_ff)), ("dw_up", (cfg.d, cfg.d_ff)),
+                     ("dw_down", (cfg.d_ff, cfg.d))):
+        for e in experts:
+            for _ in range(2):
+                ents.append((n, e, int(rng.integers(0, shape[0])), int(rng.integers(0, shape[1]))))
+    say(f"[{name}] oracle: {len(ents)} weight-gradient entries")
+    want = orc.backward_weight_entries(host["x"], host["w_gate"], host["w_up"], host["w_down"],
+                                       dy_h.double().numpy(), ob["idx"], ob["gate"],
+                                       ob["row_of"], ents)
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        sel = [q for q, en in enumerate(ents) if en[0] == n]
+        got = np.array([float(g[n][ents[q][1], ents[q][2], ents[q][3]]) for q in sel])
+        err = rel_err(got, want[sel])
+        say(f"[{name}] {n} err {err:.3g} over {len(sel)} entries")
+        assert err <= TOL, f"{n}: {err}"
+    # router: sum_e dlogit[t][e] = 0 for every token, so the rows of dw_router
+    # and dbias sum to zero up to fp32 rounding (at most about 2 E 2^-24 sqrt(T)
+    # of the entries' scale, 1.4e-3 for the largest layer here); a missing or
+    # misplaced softmax term leaves a sum of the entries' own order
+    dwr = g["dw_router"].double()
+    db = g["dbias"].double()
+    assert torch.isfinite(dwr).all() and torch.isfinite(db).all()
+    scale_r = dwr.abs().max().item()
+    scale_b = db.abs().max().item()
+    assert scale_r > 0 and scale_b > 0
+    rs = (dwr.sum(1).abs().max().item() / scale_r, abs(db.sum().item()) / scale_b)
+    say(f"[{name}] router row sums / scale: dw_router {rs[0]:.3g} dbias {rs[1]:.3g}")
+    assert rs[0] <= 1e-2 and rs[1] <= 1e-2

@@ -115,3 +115,32 @@ def test_linear_in_dy_and_bf16_equals_fp32_of_same_values():
     for _, gname in NAMES:
         np.testing.assert_array_equal(b[gname], 2.0 * a[gname])
         np.testing.assert_array_equal(c[gname], a[gname])
+
+
+def test_token_subset_and_single_entries_match_the_full_backward():
+    # the per-token mode (dx, dgate of listed tokens) and the single-entry
+    # weight gradients, used where the full backward is too large, agree with
+    # the finite-difference-pinned full backward
+    T, d, E, d_ff = 24, 8, 4, 6
+    p = _layer(T, d, E, d_ff, seed=21)
+    dy = torch.randn((T, d), generator=torch.Generator().manual_seed(3)).double().numpy()
+    kw = dict(k=2, tau=0.8, renormalize=True, cap_num=3, cap_den=4)
+    full = orc.backward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"], p["w_down"],
+                        dy, **kw)
+    assert (full["row_of"] < 0).any()
+    toks = [0, 5, 6, 17, 23]
+    sub = orc.backward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"], p["w_down"],
+                       dy, tokens=toks, **kw)
+    np.testing.assert_allclose(sub["dx"], full["dx"][toks], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(sub["dgate"], full["dgate"][toks], rtol=1e-13, atol=1e-15)
+    rng = np.random.default_rng(0)
+    ents = []
+    for name, shape in (("dw_gate", (E, d, d_ff)), ("dw_up", (E, d, d_ff)),
+                        ("dw_down", (E, d_ff, d))):
+        for _ in range(12):
+            ents.append((name,) + tuple(int(rng.integers(0, s)) for s in shape))
+    got = orc.backward_weight_entries(p["x"], p["w_gate"], p["w_up"], p["w_down"], dy,
+                                      full["idx"], full["gate"], full["row_of"], ents)
+    want = np.array([full[n][e, a, b] for n, e, a, b in ents])
+    scale = max(np.abs(full[n]).max() for n in ("dw_gate", "dw_up", "dw_down"))
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13 * scale)
