@@ -116,6 +116,29 @@ def mlp_router_ms(cfg, xs, n_rot, K):
     return round(a.elapsed_time(b) / K, 4)
 
 
+def backward_ms(cfg, dev, xs, n_rot, K):
+    """Mean time of moe_backward (recompute of routing and pre-activations,
+    every gradient) over K calls with preallocated outputs and workspace,
+    HIP events on the stream; dy ~ N(0, 1)."""
+    import torch
+    import mixture_experts_layer_15_amd as moe
+    from mixture_experts_layer_15_amd import synthetic
+    dy = synthetic.make_dy(cfg, seed=1, device="cuda")
+    bw = moe.Backward(cfg)
+    args = (dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"], dy)
+    out = bw(xs[0], *args)
+    for i in range(1, 3):
+        bw(xs[i % n_rot], *args, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(K):
+        bw(xs[i % n_rot], *args, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / K
+
+
 def measured_traffic(cfg):
     """HBM bytes per launch of the gate/up GEMM from the committed FETCH_SIZE /
     WRITE_SIZE counter runs (scaled by a plain copy of known size), or None when
@@ -259,6 +282,7 @@ def main():
     ms_step = wall * 1e3 / K
 
     mlp_ms = mlp_router_ms(cfg, xs, n_rot, K) if cfg.dtype == "bf16" else None
+    bwd_ms = backward_ms(cfg, dev, xs, n_rot, K) if cfg.dtype == "bf16" else None
 
     # the fused entry point: the step time that `value` reports
     fwd = moe.Forward(cfg)
@@ -320,6 +344,14 @@ def main():
                         "dropped": int(ls[6]), "empty_experts": int(ls[7])},
         "variants": {"mlp_router_ms": mlp_ms,
                      "mlp_router_widths": "r=256 m=1024 (ZAYA1 MLP router, random weights)"},
+        "backward": None if bwd_ms is None else {
+            "ms_per_step": round(bwd_ms, 4),
+            "tokens_per_s": round(cfg.T / (bwd_ms * 1e-3), 1),
+            # recomputed g and u (2), dh (1), dx_perm (2), three weight gradients (3):
+            # 8 products of 2 n_kept d d_ff flops each
+            "gemm_tflops": round(16 * n_kept * cfg.d * cfg.d_ff / (bwd_ms * 1e-3) / 1e12, 1),
+            "gemm_frac_of_peak": round(16 * n_kept * cfg.d * cfg.d_ff / (bwd_ms * 1e-3) / 1e12
+                                       / peak, 4)},
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_frac_of_peak": round(gemm_tflops / peak, 4),
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
