@@ -341,6 +341,15 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
     return hipGetLastError();
 }
 
+hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, void* x_perm, long long T,
+                               int row_bytes, int k, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (row_bytes % 16 != 0 || k > 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s,
+                       (const u32x4*)x, row_of, (u32x4*)x_perm, T, row_bytes / 16, k);
+    return hipGetLastError();
+}
+
 // Expert-load telemetry: one workgroup, fp64.  stats as documented in moe.h.
 __global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restrict__ count,
                                                          int E, long long C,

@@ -2,26 +2,33 @@
 //
 // The forward multiplies activations [rows][K] by weights [K][N].  Its
 // backward needs the two other operand layouts:
-//   NT  C[rows][N] (+)= A[rows][K] B^T, B stored [N][K]       dH = dO W_down^T,
-//       dX = dG W_gate^T + dU W_up^T (rows of each expert, K and N fixed)
-//   TN  C[e][M][N] = A^T B, A stored [rows][M], B [rows][N]   dW = X^T dG ...
-//       (K = the rows of expert e: a different reduction length per expert)
-// One kernel, two operand flavours chosen at compile time: an operand stored
-// with K contiguous (A in NT, B in NT) is read into MFMA fragments with
-// ds_read_b128; an operand stored with K as its row index (A in TN, B in TN)
-// with the transposing read ds_read_b64_tr_b16 (a 16-lane group reads a 4 x 16
-// block; lane n receives column n).  Both MFMA operands of
-// v_mfma_f32_16x16x32_bf16 share one register layout (lane l: index l % 16,
-// K values 8 (l / 16) .. + 7), so the same two read paths serve A and B.
+//   NT  C[r][N] (+)= A[r][K] W[e]^T, W[e] stored [N][K]: dh = dy W_down^T and
+//       dx = dg W_gate^T + du W_up^T over the rows r of each expert
+//   TN  C[e][M][N] = sum over the rows r of expert e of A[r][M]^T B[r][N]: the
+//       weight gradients, a different reduction length (its kept rows) per expert
+// In NT both operands are stored with K contiguous, in TN both with K as the
+// row index.  Both MFMA operands of v_mfma_f32_16x16x32_bf16 share one
+// register layout (lane l: index l % 16, K values 8 (l / 16) .. + 7), so one
+// fragment reader per storage order serves A and B: ds_read_b128 for K
+// contiguous, the transposing ds_read_b64_tr_b16 for K rows (a 16-lane group
+// reads a 4 x 16 block; lane n receives column n).
 //
-// Workgroup: 4 waves (2 x 2), tile 128 x 128, K-steps of 32, two LDS buffers
-// filled through registers (loads of step k+1 are in flight while step k
-// multiplies).  Rows past the end (M, N or an expert's K range) load as zero,
-// so the K tail of the ragged reductions adds nothing.  fp32 results; each
-// lane holds four consecutive output columns of one row (weights in the
-// MFMA's first operand slot) and writes them as one 16-byte store.
+// Workgroup: WAVES waves as WMW (M) x WAVES/WMW (N), tile BM x BN, K-steps of
+// 32, a ring of NS LDS stages per operand filled by buffer_load_dwordx4 ...
+// lds (16 bytes per lane straight into LDS, no register round trip): NS - 1
+// stages are in flight while one is multiplied.  A persistent grid walks the
+// tiles in sweeps of one grid; inside a sweep each XCD takes a contiguous
+// run, so tiles of one expert spread over the whole chip.  Every wave fills
+// its share of the 1 KB blocks of each operand stage, each lane picking the
+// global chunk that belongs at its LDS position (XOR swizzles that spread the fragment
+// reads over the banks).  Rows past an expert's end: in NT they are clamped
+// (their results are not stored); in TN, where they are reduction steps,
+// the buffer descriptor's record count ends at the expert's last row, so they
+// read as zeros.  fp32 results written from the accumulators, four
+// consecutive columns per lane (weights in the MFMA's first operand slot).
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 #include "tiles.h"
 
 namespace moe {
@@ -30,227 +37,304 @@ namespace {
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-constexpr int TB = 128;          // tile rows and columns
-constexpr int TK = 32;           // K-step
-constexpr int LD_KC = TK + 8;    // LDS row stride (elements) of a K-contiguous tile [128][32]
-constexpr int LD_KR = TB + 8;    // LDS row stride of a K-row tile [32][128]
-// elements of one LDS tile: [TK][LD_KR] (K-row) or [TB][LD_KC] (K-contiguous)
-constexpr int tile_elems(bool krow) { return krow ? TK * LD_KR : TB * LD_KC; }
+constexpr int TK = 32;   // K-step
 
-// 16 bytes per thread-chunk: tile chunk q (0..511) of an operand tile.
-//  K-contiguous tile (rows x 32 K): row q / 4, K chunk q % 4
-//  K-row tile (32 K x 128 cols):    K row q / 16, col chunk q % 16
-template <bool KROW>
-__device__ __forceinline__ void chunk_pos(int q, int& r, int& c8) {
-    if (KROW) { r = q / 16; c8 = (q % 16) * 8; }
-    else      { r = q / 4;  c8 = (q % 4) * 8; }
-}
+template <int BM, int BN, int WAVES, int WMW, int NS>
+struct BwShape {
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int WNW = WAVES / WMW;
+    static constexpr int MI = BM / WMW / 16;            // 16-row blocks per wave
+    static constexpr int NJ = BN / WNW / 16;            // 16-column blocks per wave
+    static constexpr int A_STAGE = BM * TK * 2;         // bytes of one A stage
+    static constexpr int B_STAGE = BN * TK * 2;
+    static constexpr int A_WL = A_STAGE / 1024 / WAVES; // 1 KB wave-loads per wave and stage
+    static constexpr int B_WL = B_STAGE / 1024 / WAVES;
+    static constexpr int LOADS = A_WL + B_WL;
+    static_assert(A_WL >= 1 && B_WL >= 1 && A_WL * WAVES * 1024 == A_STAGE &&
+                  B_WL * WAVES * 1024 == B_STAGE, "whole wave-loads per wave");
+    static_assert(MI >= 1 && NJ >= 1 && BM % (16 * WMW) == 0 && BN % (16 * WNW) == 0, "waves");
+    static_assert(BM == 128 || BM == 256, "K-row stage rows of 256 or 512 bytes");
+    static_assert(BN == 128 || BN == 256, "K-row stage rows of 256 or 512 bytes");
+    static_assert(NS >= 3 && NS <= 4, "stages");
+    static_assert(NS * (A_STAGE + B_STAGE) + 4096 <= 160 * 1024, "LDS budget");
+};
 
-// Fragment of 16 (rows or columns) x 32 K at tile index base b (0, 16, ...).
-template <bool KROW>
-__device__ __forceinline__ bf16x8 frag(const uint16_t* tile, int b, int lane) {
-    const int c = lane & 15, g = lane >> 4;
-    if (!KROW) {
-        return *(const bf16x8*)(tile + (b + c) * LD_KC + g * 8);
-    } else {
-        const uint16_t* p = tile + (g * 8 + (c >> 2)) * LD_KR + b + (c & 3) * 4;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * LD_KR));
-        return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-}
+// K-contiguous stage [rows][32 K]: row r at 64 r bytes, 16-byte slot s of the
+// row holds K chunk s ^ kc_sw(r).  The 16 rows of a fragment read
+// (r = base + 0..15) then hit four distinct slots per bank group.
+__device__ __forceinline__ int kc_sw(int r) { return (r >> 2) & 3; }
+// K-row stage [32 K rows][columns]: row k at k * (2 columns) bytes, 32-byte
+// pair slot p holds column pair p ^ kr_sw(k) (the pair swizzle of the forward
+// GEMM for rows of 256 or 512 bytes).
+__device__ __forceinline__ int kr_sw(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
-// MODE 0 (NT): tile table over the rows of each expert (ragged M); K, N
-//   fixed; A = act[rows][K] (row off[e] + m), B = W[e] stored [N][K].
-// MODE 1 (TN): tiles (e, M-tile, N-tile), M and N fixed; K = rows of e;
-//   A stored [rows][M] (row off[e] + k), B stored [rows][N].
-// a_rows / b_rows (may be null) replace a row index r of A / B by
-// a_rows[r] / b_rows[r]: the operand is then read from an unpermuted array
-// (x or dy) through the dispatch map token_of_row.
-template <int MODE>
-__global__ __launch_bounds__(256) void gemm_bw_kernel(
+// MODE 0 (NT): tiles from the expert row counts (ragged M), K and N fixed;
+//   A rows row0.. of act (or act[a_rows[row0..]] gathered), B = W[e].
+// MODE 1 (TN): tiles (e, M-tile, N-tile); reduction over the rows off[e] ..
+//   off[e+1]-1 of A [rows][M] and B [rows][N].
+template <int MODE, int BM, int BN, int WAVES, int WMW, int NS>
+__global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
-    const uint16_t* __restrict__ B, const int32_t* __restrict__ b_rows, float* __restrict__ C,
-    const int32_t* __restrict__ off, int E, int M, int N, int K, long long b_stride,
-    int accumulate) {
-    constexpr bool A_KROW = MODE == 1;   // A tile stored with K as its row index
-    constexpr bool B_KROW = MODE == 1;
-    __shared__ __attribute__((aligned(16))) uint16_t sa[2][tile_elems(A_KROW)];
-    __shared__ __attribute__((aligned(16))) uint16_t sb[2][tile_elems(B_KROW)];
+    const uint16_t* __restrict__ B, float* __restrict__ C, const int32_t* __restrict__ off,
+    int E, int M, int N, int K, int accumulate) {
+    using S = BwShape<BM, BN, WAVES, WMW, NS>;
+    constexpr bool KROW = MODE == 1;
+    constexpr int MI = S::MI, NJ = S::NJ;
+    __shared__ __attribute__((aligned(1024))) char sa0[S::A_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sa1[S::A_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sa2[S::A_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sa3[NS > 3 ? S::A_STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char sb0[S::B_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sb1[S::B_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sb2[S::B_STAGE];
+    __shared__ __attribute__((aligned(1024))) char sb3[NS > 3 ? S::B_STAGE : 16];
     __shared__ TileTable tt;
-    __shared__ long long s_wave[4];
+    __shared__ long long s_wave[WAVES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;   // 2 x 2 waves, 64 x 64 each
-
-    int e, row0, rows, n0, m0 = 0, k_begin = 0, k_len = K;
-    if (MODE == 0) {
-        const int ntn = (N + TB - 1) / TB;
-        build_tile_table<TB>(off, E, ntn, tt, s_wave);
-        const long long t = blockIdx.x;
-        if (t >= tt.start[E]) return;   // uniform
-        int mt, nt;
-        decode_tile<1>(tt, E, ntn, t, e, mt, nt);
-        row0 = off[e] + mt * TB;
-        rows = min(TB, off[e + 1] - row0);
-        n0 = nt * TB;
-    } else {
-        const int mtn = (M + TB - 1) / TB, ntn = (N + TB - 1) / TB;
-        const int t = blockIdx.x;
-        e = t / (mtn * ntn);
-        const int r = t % (mtn * ntn);
-        m0 = (r / ntn) * TB;
-        n0 = (r % ntn) * TB;
-        row0 = 0;
-        rows = TB;
-        k_begin = off[e];
-        k_len = off[e + 1] - off[e];
-    }
-    const uint16_t* Bw = B + (MODE == 0 ? (long long)e * b_stride : 0);
-
-    // NT: the A rows of this thread's two chunks are the same for every K-step
-    long long a_src[2] = {0, 0};
-    if (MODE == 0) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            int r, c8;
-            chunk_pos<A_KROW>(tid + 256 * s, r, c8);
-            if (r < rows) a_src[s] = a_rows ? a_rows[row0 + r] : row0 + r;
-        }
-    }
-
-    // global -> register loads of one K-step (two 16-byte chunks per thread and operand)
-    auto load_a = [&](int k0, u32x4 (&v)[2]) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            int r, c8;
-            chunk_pos<A_KROW>(tid + 256 * s, r, c8);
-            bool ok;
-            long long gi = 0;
-            if (MODE == 0) {   // A[row0 + r][k0 + c8]
-                ok = r < rows && k0 + c8 < K;
-                if (ok) gi = a_src[s] * K + k0 + c8;
-            } else {           // A[k_begin + k0 + r][m0 + c8]
-                ok = k0 + r < k_len && m0 + c8 < M;
-                if (ok) {
-                    const int kr = k_begin + k0 + r;
-                    gi = (long long)(a_rows ? a_rows[kr] : kr) * M + m0 + c8;
-                }
-            }
-            v[s] = ok ? *(const u32x4*)(A + gi) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto load_b = [&](int k0, u32x4 (&v)[2]) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            int r, c8;
-            chunk_pos<B_KROW>(tid + 256 * s, r, c8);
-            bool ok;
-            long long gi = 0;
-            if (MODE == 0) {   // W[e][n0 + r][k0 + c8]
-                ok = n0 + r < N && k0 + c8 < K;
-                if (ok) gi = (long long)(n0 + r) * K + k0 + c8;
-            } else {           // B[k_begin + k0 + r][n0 + c8]
-                ok = k0 + r < k_len && n0 + c8 < N;
-                if (ok) {
-                    const int kr = k_begin + k0 + r;
-                    gi = (long long)(b_rows ? b_rows[kr] : kr) * N + n0 + c8;
-                }
-            }
-            v[s] = ok ? *(const u32x4*)(Bw + gi) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store = [&](uint16_t* tile, const u32x4 (&v)[2], bool krow) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            int r, c8;
-            if (krow) chunk_pos<true>(tid + 256 * s, r, c8);
-            else chunk_pos<false>(tid + 256 * s, r, c8);
-            *(u32x4*)(tile + r * (krow ? LD_KR : LD_KC) + c8) = v[s];
-        }
-    };
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = (k_len + TK - 1) / TK;
-    u32x4 va[2], vb[2];
-    if (nk > 0) {
-        load_a(0, va);
-        load_b(0, vb);
-        store(sa[0], va, A_KROW);
-        store(sb[0], vb, B_KROW);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            load_a((kt + 1) * TK, va);
-            load_b((kt + 1) * TK, vb);
-        }
-        bf16x8 fa[4], fb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = frag<A_KROW>(sa[cur], wm * 64 + i * 16, lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = frag<B_KROW>(sb[cur], wn * 64 + j * 16, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-        if (kt + 1 < nk) {
-            store(sa[cur ^ 1], va, A_KROW);
-            store(sb[cur ^ 1], vb, B_KROW);
-        }
-        __syncthreads();
-    }
-
-    // lane (g4, c16) of block (i, j): row i*16 + c16, columns j*16 + 4 g4 .. + 3
+    const int wm = w / S::WNW, wn = w % S::WNW;
     const int c16 = lane & 15, g4 = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + c16;
-        if (MODE == 0 ? r >= rows : m0 + r >= M) continue;
-        float* crow = MODE == 0 ? C + (long long)(row0 + r) * N
-                                : C + ((long long)e * M + m0 + r) * N;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 64 + j * 16 + g4 * 4;
-            if (col >= N) continue;
-            f32x4 v = acc[i][j];
-            if (accumulate) v += *(const f32x4*)(crow + col);
-            *(f32x4*)(crow + col) = v;
+    const int G = gridDim.x;   // a multiple of 8
+
+    // persistent grid: sweeps of G tiles, workgroup b taking slot xcd_slot(b, G)
+    // of each sweep (each XCD a contiguous run of tiles)
+    long long total;
+    int mtn = 1;
+    const int ntn = (N + BN - 1) / BN;
+    if (MODE == 0) {
+        build_tile_table<BM>(off, E, ntn, tt, s_wave);
+        total = tt.start[E];
+    } else {
+        mtn = (M + BM - 1) / BM;
+        total = (long long)E * mtn * ntn;
+    }
+    char* abuf[4] = {sa0, sa1, sa2, sa3};
+    char* bbuf[4] = {sb0, sb1, sb2, sb3};
+    auto lds_base = [](char* p) { return __builtin_amdgcn_readfirstlane(lds_addr(p)); };
+
+    for (long long sweep = 0; sweep < total; sweep += G) {
+        const long long t = sweep + xcd_slot(blockIdx.x, G);
+        if (t >= total) continue;   // uniform across the workgroup
+        int e, row0, rows = BM, m0 = 0, n0, k_len;
+        if (MODE == 0) {
+            int mt, nt;
+            decode_tile<4>(tt, E, ntn, t, e, mt, nt);
+            row0 = off[e] + mt * BM;
+            rows = min(BM, off[e + 1] - row0);
+            n0 = nt * BN;
+            k_len = K;
+        } else {
+            e = (int)(t / (mtn * ntn));
+            const int r = (int)(t % (mtn * ntn));
+            m0 = (r / ntn) * BM;
+            n0 = (r % ntn) * BN;
+            row0 = off[e];
+            k_len = off[e + 1] - row0;
         }
+        const int nk = (k_len + TK - 1) / TK;
+
+        // this lane's byte offset for each of its wave-loads (q < A_WL: A, else B)
+        uint32_t l_off[S::LOADS];
+#pragma unroll
+        for (int q = 0; q < S::LOADS; ++q) {
+            const bool is_a = q < S::A_WL;
+            const int blk = is_a ? w * S::A_WL + q : w * S::B_WL + (q - S::A_WL);
+            if (!KROW) {   // [rows][32 K]: rows 16 blk .. + 15, four slots each
+                const int r = blk * 16 + lane / 4;
+                const int c = (lane % 4) ^ kc_sw(r);
+                int src;
+                if (is_a) {
+                    const int rr = min(r, rows - 1);
+                    src = a_rows ? a_rows[row0 + rr] : rr;
+                } else {
+                    src = min(r, N - 1 - n0);
+                }
+                l_off[q] = ((uint32_t)src * (uint32_t)K + c * 8) * 2u;
+            } else {       // [32 K rows][columns]: (1024 / row bytes) rows per block
+                const int cols = is_a ? BM : BN;
+                const int spr = cols / 8;                     // 16-byte slots per row
+                const int k = blk * (1024 / (cols * 2)) + lane / spr;
+                const int sl = lane % spr;
+                const int col = ((sl >> 1) ^ kr_sw(k)) * 16 + (sl & 1) * 8;
+                const int ld = is_a ? M : N;
+                const int c0 = is_a ? m0 : n0;
+                l_off[q] = ((uint32_t)k * (uint32_t)ld + min(col, ld - c0 - 8)) * 2u;
+            }
+        }
+        // NT: fixed descriptors, the K step in the scalar offset.  A without a
+        // gather starts at its tile's first row (offsets stay tile-local).
+        const uint16_t* a_base = MODE == 0 ? (a_rows ? A : A + (long long)row0 * K)
+                                           : A + (long long)row0 * M + m0;
+        const uint16_t* b_base = MODE == 0 ? B + ((long long)e * N + n0) * K
+                                           : B + (long long)row0 * N + n0;
+        const i32x4 rs_a0 = buffer_rsrc(a_base);
+        const i32x4 rs_b0 = buffer_rsrc(b_base);
+
+        // all loads of K-step kt into stage buffers (la, lb)
+        auto issue = [&](int kt, uint32_t la, uint32_t lb) {
+            const int k0 = kt * TK;
+            i32x4 ra = rs_a0, rb = rs_b0;
+            uint32_t so = (uint32_t)k0 * 2u;
+            if (MODE == 1) {
+                // descriptors that start at row k0 and end at the expert's last
+                // row: the rows past it read as zeros (no scalar offset, so the
+                // range check sees the whole per-lane offset)
+                const uint32_t left = (uint32_t)min(k_len - k0, TK);   // valid rows
+                ra = buffer_rsrc(a_base + (long long)k0 * M,
+                                 left * (uint32_t)M * 2u - (uint32_t)m0 * 2u);
+                rb = buffer_rsrc(b_base + (long long)k0 * N,
+                                 left * (uint32_t)N * 2u - (uint32_t)n0 * 2u);
+                so = 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < S::A_WL; ++q)
+                load_to_lds(ra, l_off[q], so, la + (w * S::A_WL + q) * 1024);
+#pragma unroll
+            for (int q = 0; q < S::B_WL; ++q)
+                load_to_lds(rb, l_off[S::A_WL + q], so, lb + (w * S::B_WL + q) * 1024);
+        };
+
+        // per-lane fragment read offsets (lane constants)
+        const int kc_rd = c16 * 64 + ((g4 ^ kc_sw(c16)) << 4);
+        const int kr_row = g4 * 8 + (c16 >> 2);
+        const int kr_h = kr_sw(kr_row);
+        const int kr_in = ((c16 >> 1) & 1) * 16 + (c16 & 1) * 8;
+        // 16 rows (K contiguous) or 16 columns (K rows of rb bytes) from index b
+        auto frag = [&](const char* st, int b, int rb) -> bf16x8 {
+            if (!KROW) {
+                return *(const bf16x8*)(st + b * 64 + kc_rd);
+            } else {
+                const char* p = st + kr_row * rb + kr_in + (((b >> 4) ^ kr_h) << 5);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * rb));
+                return __builtin_bit_cast(
+                    bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        };
+
+        f32x4 acc[MI][NJ];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+        for (int s = 0; s + 1 < NS; ++s)
+            if (s < nk) issue(s, lds_base(abuf[s]), lds_base(bbuf[s]));
+
+        for (int kt = 0; kt < nk; kt += NS) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int k = kt + s;
+                if (k >= nk) break;
+                // stage k has landed (up to NS-2 later stages may still be in
+                // flight) and every wave is done with the buffer refilled below
+                switch (min(nk - 1 - k, NS - 2)) {
+                    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
+                    case 1:
+                        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(S::LOADS) : "memory");
+                        break;
+                    default:
+                        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * S::LOADS)
+                                     : "memory");
+                        break;
+                }
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (k + NS - 1 < nk)
+                    issue(k + NS - 1, lds_base(abuf[(s + NS - 1) % NS]),
+                          lds_base(bbuf[(s + NS - 1) % NS]));
+                const char* sa = abuf[s];
+                const char* sb = bbuf[s];
+                bf16x8 fb[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) fb[j] = frag(sb, (wn * NJ + j) * 16, BN * 2);
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    const bf16x8 fa = frag(sa, (wm * MI + i) * 16, BM * 2);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa, acc[i][j],
+                                                                            0, 0, 0);
+                }
+            }
+        }
+
+        // lane (g4, c16) of block (i, j): row i*16 + c16, columns j*16 + 4 g4 .. + 3
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int r = (wm * MI + i) * 16 + c16;
+            if (MODE == 0 ? r >= rows : m0 + r >= M) continue;
+            float* crow = MODE == 0 ? C + (long long)(row0 + r) * N
+                                    : C + ((long long)e * M + m0 + r) * N;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int col = n0 + (wn * NJ + j) * 16 + g4 * 4;
+                if (col >= N) continue;
+                f32x4 v = acc[i][j];
+                if (accumulate) v += *(const f32x4*)(crow + col);
+                *(f32x4*)(crow + col) = v;
+            }
+        }
+        // every wave is done reading this tile's stages before the next tile's
+        // loads refill them
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
 }
 
-}  // namespace
+// Persistent grid of at most `cap` workgroups (a multiple of 8).
+unsigned grid_of(long long tiles, int cap) {
+    long long g = std::min<long long>(cap, (tiles + 7) / 8 * 8);
+    return (unsigned)std::max<long long>(8, g / 8 * 8);
+}
 
-hipError_t launch_bw_nt(const uint16_t* act, const int32_t* act_rows, const uint16_t* W,
-                        float* C, const int32_t* off, int E, int N, int K, long long max_rows,
-                        bool accumulate, hipStream_t s) {
-    if (max_rows == 0) return hipSuccess;
-    if (N % 8 != 0 || K % TK != 0) return hipErrorInvalidValue;
-    const long long tiles = ((max_rows + TB - 1) / TB + E) * ((N + TB - 1) / TB);
-    hipLaunchKernelGGL(gemm_bw_kernel<0>, dim3((unsigned)tiles), dim3(256), 0, s, act, act_rows,
-                       W, (const int32_t*)nullptr, C, off, E, 0, N, K, (long long)N * K,
+template <int BM, int BN, int WAVES, int WMW, int NS>
+hipError_t launch_nt(const uint16_t* act, const int32_t* act_rows, const uint16_t* W, float* C,
+                     const int32_t* off, int E, int N, int K, long long max_rows, bool accumulate,
+                     int cap, hipStream_t s) {
+    const long long tiles = ((max_rows + BM - 1) / BM + E) * ((N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_bw_kernel<0, BM, BN, WAVES, WMW, NS>), dim3(grid_of(tiles, cap)),
+                       dim3(64 * WAVES), 0, s, act, act_rows, W, C, off, E, 0, N, K,
                        accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
-hipError_t launch_bw_tn(const uint16_t* A, const int32_t* a_rows, const uint16_t* B,
-                        const int32_t* b_rows, float* C, const int32_t* off, int E, int M, int N,
-                        hipStream_t s) {
-    const long long tiles = (long long)E * ((M + TB - 1) / TB) * ((N + TB - 1) / TB);
-    if (tiles == 0) return hipSuccess;
-    if (M % 8 != 0 || N % 8 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gemm_bw_kernel<1>, dim3((unsigned)tiles), dim3(256), 0, s, A, a_rows, B,
-                       b_rows, C, off, E, M, N, 0, 0LL, 0);
+template <int BM, int BN, int WAVES, int WMW, int NS>
+hipError_t launch_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off, int E,
+                     int M, int N, int cap, hipStream_t s) {
+    const long long tiles = (long long)E * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_bw_kernel<1, BM, BN, WAVES, WMW, NS>), dim3(grid_of(tiles, cap)),
+                       dim3(64 * WAVES), 0, s, A, (const int32_t*)nullptr, B, C, off, E, M, N, 0,
+                       0);
     return hipGetLastError();
+}
+
+}  // namespace
+
+// One shape for both: 256 x 256 tiles, 8 waves as 2 (M) x 4 (N), three
+// stages (one workgroup per CU; cus counts two per CU).  Measured on the
+// four large layers against 128 x 128 tiles with 4 waves (two workgroups per
+// CU) and 256 x 128: 256 x 256 is the fastest on every one (the backward of
+// the ZAYA1-like layer 2.38 ms against 2.95 and 2.72); a 4 x 2 wave layout and
+// a fourth stage measure within 1.5%.
+hipError_t launch_bw_nt(const uint16_t* act, const int32_t* act_rows, const uint16_t* W,
+                        float* C, const int32_t* off, int E, int N, int K, long long max_rows,
+                        bool accumulate, int cus, hipStream_t s) {
+    if (max_rows == 0) return hipSuccess;
+    if (N % 8 != 0 || N < 8 || K % TK != 0) return hipErrorInvalidValue;
+    return launch_nt<256, 256, 8, 2, 3>(act, act_rows, W, C, off, E, N, K, max_rows, accumulate,
+                                        cus / 2, s);
+}
+
+hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off,
+                        int E, int M, int N, int cus, hipStream_t s) {
+    if (E == 0) return hipSuccess;
+    if (M % 8 != 0 || N % 8 != 0 || M < 8 || N < 8) return hipErrorInvalidValue;
+    return launch_tn<256, 256, 8, 2, 3>(A, B, C, off, E, M, N, cus / 2, s);
 }
 
 }  // namespace moe

@@ -42,6 +42,10 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
                            int32_t* token_of_row, void* workspace, int d, hipStream_t s,
                            bool scatter = true);
 
+// x_perm[row_of[t][j]] = x[t] for every kept (t, j) (rows of row_bytes bytes).
+hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, void* x_perm, long long T,
+                               int row_bytes, int k, hipStream_t s);
+
 // Expert-load telemetry (8 fp64 values, see moe_load_stats).
 hipError_t launch_load_stats(const int32_t* count, int E, long long C, double* stats,
                              hipStream_t s);
@@ -98,18 +102,19 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
                           const float* gate, void* y, long long T, int d, int k,
                           hipStream_t s);
 
-// Backward GEMMs (gemm_bw.hip), fp32 results.
+// Backward GEMMs (gemm_bw.hip), fp32 results; cus = workgroups of the
+// persistent grid (a multiple of 8).
 // NT: C[r][N] (+)= A[r'][K] W[e]^T over the rows r of each expert, W[e] stored
-// [N][K]; r' = act_rows[r] when act_rows is given.
+// [N][K]; r' = act_rows[r] when act_rows is given (byte offsets into act then
+// span the whole array: the caller keeps them below 2^32).
 hipError_t launch_bw_nt(const uint16_t* act, const int32_t* act_rows, const uint16_t* W,
                         float* C, const int32_t* off, int E, int N, int K, long long max_rows,
-                        bool accumulate, hipStream_t s);
-// TN: C[e][M][N] = sum over the rows r of expert e of A[a(r)][m] B[b(r)][n]
-// (a(r) = a_rows[r] or r, likewise b): the weight gradients, a ragged
-// reduction length per expert; experts with no rows get zeros.
-hipError_t launch_bw_tn(const uint16_t* A, const int32_t* a_rows, const uint16_t* B,
-                        const int32_t* b_rows, float* C, const int32_t* off, int E, int M, int N,
-                        hipStream_t s);
+                        bool accumulate, int cus, hipStream_t s);
+// TN: C[e][M][N] = sum over the rows r of expert e of A[r][m] B[r][n]: the
+// weight gradients, a ragged reduction length per expert; experts with no
+// rows get zeros.
+hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off,
+                        int E, int M, int N, int cus, hipStream_t s);
 
 // Backward elementwise and router kernels (backward.hip).
 hipError_t launch_geglu_bwd(uint16_t* G, uint16_t* U, const float* dHr, uint16_t* gH,

@@ -435,13 +435,11 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
 
 namespace {
 
-// bf16 backward: the forward's maps, then the recomputed pre-activations and
-// the gradients of every product.  x_perm only when x is too large to be
-// gathered through 32-bit offsets.
+// bf16 backward: the forward's maps, x and dy in expert-grouped row order,
+// the recomputed pre-activations and the gradients of every product.
 struct BwdLayout {
-    size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, G, U, gH, dHr,
-        dXp, dgrow, dl, dwr, total;
-    bool gather;
+    size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, dy_perm, G, U,
+        gH, dHr, dXp, dgrow, dl, dwr, total;
 };
 
 BwdLayout bwd_layout(const moe_config* c) {
@@ -449,7 +447,6 @@ BwdLayout bwd_layout(const moe_config* c) {
     const size_t F = (size_t)c->d_ff, R = (size_t)max_rows(c);
     const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy);
     BwdLayout L;
-    L.gather = T * d * 2 < ((size_t)1 << 32);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.logits = take(T * E * 4);
@@ -460,7 +457,8 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.row_of = take(T * k * 4);
     L.token_of_row = take(T * k * 4);
     L.dsp = take(moe::dispatch_workspace_bytes(p));
-    L.x_perm = take(L.gather ? 0 : R * d * 2);
+    L.x_perm = take(R * d * 2);
+    L.dy_perm = take(R * d * 2);
     L.G = take(R * F * 2);
     L.U = take(R * F * 2);
     L.gH = take(R * F * 2);
@@ -542,36 +540,37 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     float* dgrow = (float*)(w + L.dgrow);
     float* dl = (float*)(w + L.dl);
     const uint16_t* xb = (const uint16_t*)x;
-    const uint16_t* dyb = (const uint16_t*)dy;
     const int Ei = cfg->E, di = cfg->d, Fi = cfg->d_ff, ki = cfg->k;
     const long long Rl = max_rows(cfg);
     const int cus = gemm_grid_cap();
 
-    // forward recompute: routing, dispatch maps, g = x W_gate, u = x W_up
+    // forward recompute: routing, dispatch maps and x_perm, g = x W_gate, u = x W_up
     BWD(moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T, di, Ei, ki,
                           cfg->temperature, cfg->renormalize, s), "moe_backward/route");
     const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, Ei, ki, capacity_eff(cfg), cfg->drop_policy);
-    BWD(moe::launch_dispatch(p, cfg->dtype, idx, x, w + L.x_perm, count, offset, row_of, tor,
-                             w + L.dsp, di, s, !L.gather), "moe_backward/dispatch");
-    const uint16_t* a_src = L.gather ? xb : (const uint16_t*)(w + L.x_perm);
-    const int32_t* a_rows = L.gather ? tor : nullptr;
-    BWD(moe::launch_mfma_grouped(a_src, a_rows, offset, (const uint16_t*)w_gate, G, Ei, di, Fi,
+    uint16_t* x_perm = (uint16_t*)(w + L.x_perm);
+    uint16_t* dy_perm = (uint16_t*)(w + L.dy_perm);
+    BWD(moe::launch_dispatch(p, cfg->dtype, idx, x, x_perm, count, offset, row_of, tor,
+                             w + L.dsp, di, s, true), "moe_backward/dispatch");
+    BWD(moe::launch_scatter_rows(dy, row_of, dy_perm, cfg->T, di * 2, ki, s),
+        "moe_backward/scatter_dy");
+    BWD(moe::launch_mfma_grouped(x_perm, nullptr, offset, (const uint16_t*)w_gate, G, Ei, di, Fi,
                                  Rl, cus, s), "moe_backward/gate");
-    BWD(moe::launch_mfma_grouped(a_src, a_rows, offset, (const uint16_t*)w_up, U, Ei, di, Fi,
+    BWD(moe::launch_mfma_grouped(x_perm, nullptr, offset, (const uint16_t*)w_up, U, Ei, di, Fi,
                                  Rl, cus, s), "moe_backward/up");
     // dHr = dy W_down^T per kept row, then the GeGLU backward and dgate
-    BWD(moe::launch_bw_nt(dyb, tor, (const uint16_t*)w_down, dHr, offset, Ei, Fi, di, Rl, false, s),
-        "moe_backward/dh");
+    BWD(moe::launch_bw_nt(dy_perm, nullptr, (const uint16_t*)w_down, dHr, offset, Ei, Fi, di, Rl,
+                          false, cus, s), "moe_backward/dh");
     BWD(moe::launch_geglu_bwd(G, U, dHr, gH, dgrow, offset, tor, row_of, gate, Ei, ki, Fi, Rl, s),
         "moe_backward/geglu");
     // G, U now hold dg, du
-    BWD(moe::launch_bw_nt(G, nullptr, (const uint16_t*)w_gate, dXp, offset, Ei, di, Fi, Rl, false, s),
+    BWD(moe::launch_bw_nt(G, nullptr, (const uint16_t*)w_gate, dXp, offset, Ei, di, Fi, Rl, false, cus, s),
         "moe_backward/dx_gate");
-    BWD(moe::launch_bw_nt(U, nullptr, (const uint16_t*)w_up, dXp, offset, Ei, di, Fi, Rl, true, s),
+    BWD(moe::launch_bw_nt(U, nullptr, (const uint16_t*)w_up, dXp, offset, Ei, di, Fi, Rl, true, cus, s),
         "moe_backward/dx_up");
-    BWD(moe::launch_bw_tn(xb, tor, G, nullptr, dw_gate, offset, Ei, di, Fi, s), "moe_backward/dw_gate");
-    BWD(moe::launch_bw_tn(xb, tor, U, nullptr, dw_up, offset, Ei, di, Fi, s), "moe_backward/dw_up");
-    BWD(moe::launch_bw_tn(gH, nullptr, dyb, tor, dw_down, offset, Ei, Fi, di, s), "moe_backward/dw_down");
+    BWD(moe::launch_bw_tn(x_perm, G, dw_gate, offset, Ei, di, Fi, cus, s), "moe_backward/dw_gate");
+    BWD(moe::launch_bw_tn(x_perm, U, dw_up, offset, Ei, di, Fi, cus, s), "moe_backward/dw_up");
+    BWD(moe::launch_bw_tn(gH, dy_perm, dw_down, offset, Ei, Fi, di, cus, s), "moe_backward/dw_down");
     // router: dlogit, then dx and the router's weight and bias gradients
     BWD(moe::launch_router_bwd(logits, idx, gate, row_of, dgrow, cfg->T, Ei, ki, cfg->temperature,
                                cfg->renormalize, dl, dgate, s), "moe_backward/router");
