@@ -187,7 +187,7 @@ __device__ __forceinline__ void stage_sync(int later) {
 template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB, int WM>
 __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
+    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, uint16_t* __restrict__ C2,
     const int32_t* __restrict__ off, const int32_t* __restrict__ a_rows, int E, int K, int N,
     int dense_rows, const float* __restrict__ bias, int act) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB, WM>;
@@ -364,7 +364,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         // epilogue straight from the accumulators: lane (g4, c16) of block
         // (i, j) holds output columns 4 g4 .. 4 g4 + 3 of row c16, one 8-byte
         // store per block.  Plain GEMMs may add a per-column fp32 bias and
-        // apply GELU (act == 1).
+        // apply GELU (act == 1).  gate/up with act == 2 stores the two
+        // products themselves (x W_gate to C, x W_up to C2) instead of GeGLU.
         float bv[S::OUTW / 16][4];
 #pragma unroll
         for (int jj = 0; jj < S::OUTW / 16; ++jj)
@@ -381,6 +382,20 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
 #pragma unroll
                 for (int jj = 0; jj < S::OUTW / 16; ++jj) {
                     const int col = wn * S::OUTW + jj * 16 + g4 * 4;
+                    if (GATEUP && act == 2) {
+                        bf16x4 vg, vu;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            vg[q] = (__bf16)acc[i][jj][q];
+                            vu[q] = (__bf16)acc[i][jj + NJ / 2][q];
+                        }
+                        if (n0 + col < N) {
+                            *(u32x2*)(crow + col) = __builtin_bit_cast(u32x2, vg);
+                            *(u32x2*)(C2 + (long long)(row0 + r) * N + n0 + col) =
+                                __builtin_bit_cast(u32x2, vu);
+                        }
+                        continue;
+                    }
                     bf16x4 v;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -410,15 +425,15 @@ template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB, int WM = 2>
 hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                         const int32_t* off, const int32_t* a_rows, int dense_rows,
                         const float* bias, int act, int E, int K, int N, long long max_rows, int cus,
-                        hipStream_t s) {
+                        hipStream_t s, uint16_t* C2 = nullptr) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB, WM>;
     const long long mt = (max_rows + S::BM - 1) / S::BM + E;   // >= sum_e ceil(rows_e / BM)
     const long long tiles = mt * ((N + S::OUTC - 1) / S::OUTC);
     long long g = std::min<long long>(cus, (tiles + 7) / 8 * 8);
     g = std::max<long long>(8, g / 8 * 8);
     hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NA, NB, WM>), dim3((unsigned)g),
-                       dim3(S::THREADS), 0, s, A, B0, B1, C, off, a_rows, E, K, N, dense_rows,
-                       bias, act);
+                       dim3(S::THREADS), 0, s, A, B0, B1, C, C2, off, a_rows, E, K, N,
+                       dense_rows, bias, act);
     return hipGetLastError();
 }
 
@@ -444,6 +459,19 @@ hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const i
                                                 max_rows, cus, s);
     return launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0, E, d, d_ff, max_rows,
                                            cus, s);
+}
+
+// Both products of the gate/up GEMM, unfused: g = X W_gate, u = X W_up (bf16),
+// same tiles and schedule as the GeGLU-fused launch.
+hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, const int32_t* off,
+                                   const uint16_t* w_gate, const uint16_t* w_up, uint16_t* g,
+                                   uint16_t* u, int E, int d, int d_ff, long long max_rows,
+                                   int cus, hipStream_t s) {
+    if (small_experts(max_rows, E))
+        return launch_shape<true, 10, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2,
+                                                   E, d, d_ff, max_rows, cus, s, u);
+    return launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2, E,
+                                              d, d_ff, max_rows, cus, s, u);
 }
 
 hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const int32_t* off,

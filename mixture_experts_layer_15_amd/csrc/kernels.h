@@ -75,6 +75,13 @@ hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
                             int cus, hipStream_t s);
 
+// The gate/up GEMM's two products stored separately (bf16): g = X W_gate,
+// u = X W_up (rows of X as in launch_mfma_gate_up).
+hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, const int32_t* off,
+                                   const uint16_t* w_gate, const uint16_t* w_up, uint16_t* g,
+                                   uint16_t* u, int E, int d, int d_ff, long long max_rows,
+                                   int cus, hipStream_t s);
+
 // Plain grouped GEMM C[rows][N] = A[rows][K] B[e] (bf16 out), A's rows read
 // directly (a_rows == nullptr) or gathered through a_rows (gemm_mfma.hip).
 hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const int32_t* off,

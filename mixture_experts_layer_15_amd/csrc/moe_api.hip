@@ -554,10 +554,9 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                              w + L.dsp, di, s, true), "moe_backward/dispatch");
     BWD(moe::launch_scatter_rows(dy, row_of, dy_perm, cfg->T, di * 2, ki, s),
         "moe_backward/scatter_dy");
-    BWD(moe::launch_mfma_grouped(x_perm, nullptr, offset, (const uint16_t*)w_gate, G, Ei, di, Fi,
-                                 Rl, cus, s), "moe_backward/gate");
-    BWD(moe::launch_mfma_grouped(x_perm, nullptr, offset, (const uint16_t*)w_up, U, Ei, di, Fi,
-                                 Rl, cus, s), "moe_backward/up");
+    BWD(moe::launch_mfma_gate_up_pre(x_perm, nullptr, offset, (const uint16_t*)w_gate,
+                                     (const uint16_t*)w_up, G, U, Ei, di, Fi, Rl, cus, s),
+        "moe_backward/gate_up");
     // dHr = dy W_down^T per kept row, then the GeGLU backward and dgate
     BWD(moe::launch_bw_nt(dy_perm, nullptr, (const uint16_t*)w_down, dHr, offset, Ei, Fi, di, Rl,
                           false, cus, s), "moe_backward/dh");
