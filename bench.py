@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="zaya1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the moe_backward timing (e.g. for counter runs of the forward)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -282,7 +284,8 @@ def main():
     ms_step = wall * 1e3 / K
 
     mlp_ms = mlp_router_ms(cfg, xs, n_rot, K) if cfg.dtype == "bf16" else None
-    bwd_ms = backward_ms(cfg, dev, xs, n_rot, K) if cfg.dtype == "bf16" else None
+    bwd_ms = backward_ms(cfg, dev, xs, n_rot, K) \
+        if cfg.dtype == "bf16" and not args.no_backward else None
 
     # the fused entry point: the step time that `value` reports
     fwd = moe.Forward(cfg)
