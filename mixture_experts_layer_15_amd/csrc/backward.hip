@@ -187,12 +187,14 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     }
 }
 
-// dx[t][i] = sum_j dXp[row_of[t, j]][i] + sum_e dl[t][e] Wr[i][e]  (bf16 out).
+// dx[t][i] = sum_j sum_p dXp_p[row_of[t, j]][i] + sum_e dl[t][e] Wr[i][e]
+// (bf16 out; the parts p of the expert input gradient in part order).
 // Tile 64 tokens x 64 columns, 4 x 4 per thread, e in chunks of 16 via LDS.
 __global__ __launch_bounds__(256) void dx_kernel(
     const float* __restrict__ dl, const uint16_t* __restrict__ wr,
-    const float* __restrict__ dXp, const int32_t* __restrict__ row_of, uint16_t* __restrict__ dx,
-    long long T, int d, int E, int k) {
+    const float* __restrict__ dXp, int nparts, long long part_stride,
+    const int32_t* __restrict__ row_of, uint16_t* __restrict__ dx, long long T, int d, int E,
+    int k) {
     __shared__ float s_l[16][64 + 4];
     __shared__ float s_w[16][64 + 4];
     const int tid = threadIdx.x, tt = tid >> 4, ti = tid & 15;
@@ -228,7 +230,9 @@ __global__ __launch_bounds__(256) void dx_kernel(
         f32x4 v = {acc[x][0], acc[x][1], acc[x][2], acc[x][3]};
         for (int j = 0; j < k; ++j) {
             const int rr = row_of[t * k + j];
-            if (rr >= 0) v += *(const f32x4*)(dXp + (long long)rr * d + i);
+            if (rr < 0) continue;
+            for (int p = 0; p < nparts; ++p)
+                v += *(const f32x4*)(dXp + p * part_stride + (long long)rr * d + i);
         }
         *(u32x2*)(dx + t * d + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
@@ -338,13 +342,13 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const floa
     return hipGetLastError();
 }
 
-hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp,
-                     const int32_t* row_of, uint16_t* dx, long long T, int d, int E, int k,
-                     hipStream_t s) {
+hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp, int nparts,
+                     long long part_stride, const int32_t* row_of, uint16_t* dx, long long T,
+                     int d, int E, int k, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if (d % 64 != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(dx_kernel, dim3((unsigned)((T + 63) / 64), d / 64), dim3(256), 0, s, dl,
-                       wr, dXp, row_of, dx, T, d, E, k);
+                       wr, dXp, nparts, part_stride, row_of, dx, T, d, E, k);
     return hipGetLastError();
 }
 

@@ -68,15 +68,26 @@ __device__ __forceinline__ int kc_sw(int r) { return (r >> 2) & 3; }
 // GEMM for rows of 256 or 512 bytes).
 __device__ __forceinline__ int kr_sw(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
-// MODE 0 (NT): tiles from the expert row counts (ragged M), K and N fixed;
-//   A rows row0.. of act (or act[a_rows[row0..]] gathered), B = W[e].
+// Operands of one launch.  NT runs nsrc x ksplit independent parts: part p
+// multiplies source s = p / ksplit (A[s] [rows][K] by W = B[s] [E][N][K]) over
+// the K slice p % ksplit of K / ksplit, into its own fp32 buffer
+// C + p * c_stride ([rows][N]); the parts are summed by their consumer, in
+// part order.  TN uses A[0], B[0] and C.
+struct BwOperands {
+    const uint16_t* A[2];
+    const uint16_t* B[2];
+    float* C;
+    long long c_stride;
+    int nsrc, ksplit;
+};
+
+// MODE 0 (NT): tiles from the expert row counts (ragged M) for every part;
+//   A rows row0.. of A[s], B = W[e] of source s, one K slice.
 // MODE 1 (TN): tiles (e, M-tile, N-tile); reduction over the rows off[e] ..
 //   off[e+1]-1 of A [rows][M] and B [rows][N].
 template <int MODE, int BM, int BN, int WAVES, int WMW, int NS>
 __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
-    const uint16_t* __restrict__ B, float* __restrict__ C, const int32_t* __restrict__ off,
-    int E, int M, int N, int K, int accumulate) {
+    const BwOperands ops, const int32_t* __restrict__ off, int E, int M, int N, int K) {
     using S = BwShape<BM, BN, WAVES, WMW, NS>;
     constexpr bool KROW = MODE == 1;
     constexpr int MI = S::MI, NJ = S::NJ;
@@ -102,9 +113,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     long long total;
     int mtn = 1;
     const int ntn = (N + BN - 1) / BN;
+    long long per_part = 0;
     if (MODE == 0) {
         build_tile_table<BM>(off, E, ntn, tt, s_wave);
-        total = tt.start[E];
+        per_part = tt.start[E];
+        total = per_part * ops.nsrc * ops.ksplit;
     } else {
         mtn = (M + BM - 1) / BM;
         total = (long long)E * mtn * ntn;
@@ -116,14 +129,21 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     for (long long sweep = 0; sweep < total; sweep += G) {
         const long long t = sweep + xcd_slot(blockIdx.x, G);
         if (t >= total) continue;   // uniform across the workgroup
-        int e, row0, rows = BM, m0 = 0, n0, k_len;
+        int e, row0, rows = BM, m0 = 0, n0, k_len, k_beg = 0, part = 0;
+        const uint16_t* A = ops.A[0];
+        const uint16_t* B = ops.B[0];
         if (MODE == 0) {
+            part = (int)(t / per_part);
+            const int src = part / ops.ksplit;
+            A = src ? ops.A[1] : ops.A[0];
+            B = src ? ops.B[1] : ops.B[0];
+            k_len = K / ops.ksplit;
+            k_beg = (part % ops.ksplit) * k_len;
             int mt, nt;
-            decode_tile<4>(tt, E, ntn, t, e, mt, nt);
+            decode_tile<4>(tt, E, ntn, t - (long long)part * per_part, e, mt, nt);
             row0 = off[e] + mt * BM;
             rows = min(BM, off[e + 1] - row0);
             n0 = nt * BN;
-            k_len = K;
         } else {
             e = (int)(t / (mtn * ntn));
             const int r = (int)(t % (mtn * ntn));
@@ -143,13 +163,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
             if (!KROW) {   // [rows][32 K]: rows 16 blk .. + 15, four slots each
                 const int r = blk * 16 + lane / 4;
                 const int c = (lane % 4) ^ kc_sw(r);
-                int src;
-                if (is_a) {
-                    const int rr = min(r, rows - 1);
-                    src = a_rows ? a_rows[row0 + rr] : rr;
-                } else {
-                    src = min(r, N - 1 - n0);
-                }
+                const int src = is_a ? min(r, rows - 1) : min(r, N - 1 - n0);
                 l_off[q] = ((uint32_t)src * (uint32_t)K + c * 8) * 2u;
             } else {       // [32 K rows][columns]: (1024 / row bytes) rows per block
                 const int cols = is_a ? BM : BN;
@@ -162,11 +176,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
                 l_off[q] = ((uint32_t)k * (uint32_t)ld + min(col, ld - c0 - 8)) * 2u;
             }
         }
-        // NT: fixed descriptors, the K step in the scalar offset.  A without a
-        // gather starts at its tile's first row (offsets stay tile-local).
-        const uint16_t* a_base = MODE == 0 ? (a_rows ? A : A + (long long)row0 * K)
+        // NT: fixed descriptors from the tile's first row and the K slice, the
+        // K step in the scalar offset (offsets stay tile-local)
+        const uint16_t* a_base = MODE == 0 ? A + (long long)row0 * K + k_beg
                                            : A + (long long)row0 * M + m0;
-        const uint16_t* b_base = MODE == 0 ? B + ((long long)e * N + n0) * K
+        const uint16_t* b_base = MODE == 0 ? B + ((long long)e * N + n0) * K + k_beg
                                            : B + (long long)row0 * N + n0;
         const i32x4 rs_a0 = buffer_rsrc(a_base);
         const i32x4 rs_b0 = buffer_rsrc(b_base);
@@ -267,15 +281,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
         for (int i = 0; i < MI; ++i) {
             const int r = (wm * MI + i) * 16 + c16;
             if (MODE == 0 ? r >= rows : m0 + r >= M) continue;
-            float* crow = MODE == 0 ? C + (long long)(row0 + r) * N
-                                    : C + ((long long)e * M + m0 + r) * N;
+            float* crow = MODE == 0 ? ops.C + part * ops.c_stride + (long long)(row0 + r) * N
+                                    : ops.C + ((long long)e * M + m0 + r) * N;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int col = n0 + (wn * NJ + j) * 16 + g4 * 4;
                 if (col >= N) continue;
-                f32x4 v = acc[i][j];
-                if (accumulate) v += *(const f32x4*)(crow + col);
-                *(f32x4*)(crow + col) = v;
+                *(f32x4*)(crow + col) = acc[i][j];
             }
         }
         // every wave is done reading this tile's stages before the next tile's
@@ -293,25 +305,25 @@ unsigned grid_of(long long tiles, int cap) {
 }
 
 template <int BM, int BN, int WAVES, int WMW, int NS>
-hipError_t launch_nt(const uint16_t* act, const int32_t* act_rows, const uint16_t* W, float* C,
-                     const int32_t* off, int E, int N, int K, long long max_rows, bool accumulate,
-                     int cap, hipStream_t s) {
-    const long long tiles = ((max_rows + BM - 1) / BM + E) * ((N + BN - 1) / BN);
+hipError_t launch_nt(const BwOperands& ops, const int32_t* off, int E, int N, int K,
+                     long long max_rows, int cap, hipStream_t s) {
+    const long long tiles =
+        ((max_rows + BM - 1) / BM + E) * ((N + BN - 1) / BN) * ops.nsrc * ops.ksplit;
     hipLaunchKernelGGL((gemm_bw_kernel<0, BM, BN, WAVES, WMW, NS>), dim3(grid_of(tiles, cap)),
-                       dim3(64 * WAVES), 0, s, act, act_rows, W, C, off, E, 0, N, K,
-                       accumulate ? 1 : 0);
+                       dim3(64 * WAVES), 0, s, ops, off, E, 0, N, K);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int WAVES, int WMW, int NS>
-hipError_t launch_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off, int E,
-                     int M, int N, int cap, hipStream_t s) {
+hipError_t launch_tn(const BwOperands& ops, const int32_t* off, int E, int M, int N, int cap,
+                     hipStream_t s) {
     const long long tiles = (long long)E * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL((gemm_bw_kernel<1, BM, BN, WAVES, WMW, NS>), dim3(grid_of(tiles, cap)),
-                       dim3(64 * WAVES), 0, s, A, (const int32_t*)nullptr, B, C, off, E, M, N, 0,
-                       0);
+                       dim3(64 * WAVES), 0, s, ops, off, E, M, N, 0);
     return hipGetLastError();
 }
+
+constexpr int BW_BM = 256;   // NT rows per tile
 
 }  // namespace
 
@@ -321,20 +333,31 @@ hipError_t launch_tn(const uint16_t* A, const uint16_t* B, float* C, const int32
 // CU) and 256 x 128: 256 x 256 is the fastest on every one (the backward of
 // the ZAYA1-like layer 2.38 ms against 2.95 and 2.72); a 4 x 2 wave layout and
 // a fourth stage measure within 1.5%.
-hipError_t launch_bw_nt(const uint16_t* act, const int32_t* act_rows, const uint16_t* W,
-                        float* C, const int32_t* off, int E, int N, int K, long long max_rows,
-                        bool accumulate, int cus, hipStream_t s) {
+int bw_nt_ksplit(long long max_rows, int E, int N, int K, int nsrc, int cus) {
+    const long long tiles = ((max_rows + BW_BM - 1) / BW_BM + E) * ((N + 255) / 256) * nsrc;
+    const long long want = 3LL * (cus / 2);   // three sweeps of one workgroup per CU
+    int ks = 1;
+    while (ks < 4 && tiles * ks < want && (K / (2 * ks)) % TK == 0 && K % (2 * ks) == 0) ks *= 2;
+    return ks;
+}
+
+hipError_t launch_bw_nt(const uint16_t* A0, const uint16_t* W0, const uint16_t* A1,
+                        const uint16_t* W1, float* C, long long part_stride, int ksplit,
+                        const int32_t* off, int E, int N, int K, long long max_rows, int cus,
+                        hipStream_t s) {
     if (max_rows == 0) return hipSuccess;
-    if (N % 8 != 0 || N < 8 || K % TK != 0) return hipErrorInvalidValue;
-    return launch_nt<256, 256, 8, 2, 3>(act, act_rows, W, C, off, E, N, K, max_rows, accumulate,
-                                        cus / 2, s);
+    if (N % 8 != 0 || N < 8 || ksplit < 1 || K % ksplit != 0 || (K / ksplit) % TK != 0)
+        return hipErrorInvalidValue;
+    BwOperands ops{{A0, A1}, {W0, W1}, C, part_stride, A1 ? 2 : 1, ksplit};
+    return launch_nt<BW_BM, 256, 8, 2, 3>(ops, off, E, N, K, max_rows, cus / 2, s);
 }
 
 hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off,
                         int E, int M, int N, int cus, hipStream_t s) {
     if (E == 0) return hipSuccess;
     if (M % 8 != 0 || N % 8 != 0 || M < 8 || N < 8) return hipErrorInvalidValue;
-    return launch_tn<256, 256, 8, 2, 3>(A, B, C, off, E, M, N, cus / 2, s);
+    BwOperands ops{{A, nullptr}, {B, nullptr}, C, 0, 1, 1};
+    return launch_tn<256, 256, 8, 2, 3>(ops, off, E, M, N, cus / 2, s);
 }
 
 }  // namespace moe

@@ -111,12 +111,16 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
 
 // Backward GEMMs (gemm_bw.hip), fp32 results; cus = workgroups of the
 // persistent grid (a multiple of 8).
-// NT: C[r][N] (+)= A[r'][K] W[e]^T over the rows r of each expert, W[e] stored
-// [N][K]; r' = act_rows[r] when act_rows is given (byte offsets into act then
-// span the whole array: the caller keeps them below 2^32).
-hipError_t launch_bw_nt(const uint16_t* act, const int32_t* act_rows, const uint16_t* W,
-                        float* C, const int32_t* off, int E, int N, int K, long long max_rows,
-                        bool accumulate, int cus, hipStream_t s);
+// NT: nsrc (1 or 2: A1 == nullptr or not) sources times ksplit K slices,
+// each an independent part p writing C + p * part_stride ([rows][N] fp32):
+// part p = C_p[r][N] = A_s[r][slice] W_s[e][N][slice]^T over the rows r of
+// each expert (s = p / ksplit); the sum over the parts is the product.
+// bw_nt_ksplit picks ksplit so that the parts fill the chip.
+int bw_nt_ksplit(long long max_rows, int E, int N, int K, int nsrc, int cus);
+hipError_t launch_bw_nt(const uint16_t* A0, const uint16_t* W0, const uint16_t* A1,
+                        const uint16_t* W1, float* C, long long part_stride, int ksplit,
+                        const int32_t* off, int E, int N, int K, long long max_rows, int cus,
+                        hipStream_t s);
 // TN: C[e][M][N] = sum over the rows r of expert e of A[r][m] B[r][n]: the
 // weight gradients, a ragged reduction length per expert; experts with no
 // rows get zeros.
@@ -132,9 +136,11 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const floa
                              const int32_t* row_of, const float* dgate_row, long long T, int E,
                              int k, float tau, int renorm, float* dl, float* dgate,
                              hipStream_t s);
-hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp,
-                     const int32_t* row_of, uint16_t* dx, long long T, int d, int E, int k,
-                     hipStream_t s);
+// dx = sum over the nparts buffers dXp + p * part_stride of the kept rows of
+// each token, plus dl W_r^T.
+hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp, int nparts,
+                     long long part_stride, const int32_t* row_of, uint16_t* dx, long long T,
+                     int d, int E, int k, hipStream_t s);
 size_t dwr_workspace_bytes(long long T, int d, int E);
 hipError_t launch_dwr(const uint16_t* x, const float* dl, float* dwr, float* dbias, long long T,
                       int d, int E, void* ws, hipStream_t s);

@@ -440,6 +440,7 @@ namespace {
 struct BwdLayout {
     size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, dy_perm, G, U,
         gH, dHr, dXp, dgrow, dl, dwr, total;
+    int dx_parts;   // parts of dx_perm (gate and up, each in K slices)
 };
 
 BwdLayout bwd_layout(const moe_config* c) {
@@ -463,7 +464,8 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.U = take(R * F * 2);
     L.gH = take(R * F * 2);
     L.dHr = take(R * F * 4);
-    L.dXp = take(R * d * 4);
+    L.dx_parts = 2 * moe::bw_nt_ksplit((long long)R, c->E, c->d, c->d_ff, 2, gemm_grid_cap());
+    L.dXp = take((size_t)L.dx_parts * R * d * 4);
     L.dgrow = take(R * 4);
     L.dl = take(T * E * 4);
     L.dwr = take(moe::dwr_workspace_bytes(c->T, c->d, c->E));
@@ -558,23 +560,23 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                                      (const uint16_t*)w_up, G, U, Ei, di, Fi, Rl, cus, s),
         "moe_backward/gate_up");
     // dHr = dy W_down^T per kept row, then the GeGLU backward and dgate
-    BWD(moe::launch_bw_nt(dy_perm, nullptr, (const uint16_t*)w_down, dHr, offset, Ei, Fi, di, Rl,
-                          false, cus, s), "moe_backward/dh");
+    BWD(moe::launch_bw_nt(dy_perm, (const uint16_t*)w_down, nullptr, nullptr, dHr, 0, 1, offset,
+                          Ei, Fi, di, Rl, cus, s), "moe_backward/dh");
     BWD(moe::launch_geglu_bwd(G, U, dHr, gH, dgrow, offset, tor, row_of, gate, Ei, ki, Fi, Rl, s),
         "moe_backward/geglu");
     // G, U now hold dg, du
-    BWD(moe::launch_bw_nt(G, nullptr, (const uint16_t*)w_gate, dXp, offset, Ei, di, Fi, Rl, false, cus, s),
-        "moe_backward/dx_gate");
-    BWD(moe::launch_bw_nt(U, nullptr, (const uint16_t*)w_up, dXp, offset, Ei, di, Fi, Rl, true, cus, s),
-        "moe_backward/dx_up");
+    // dx_perm in parts: (dg W_gate^T, du W_up^T) x K slices, summed by launch_dx
+    const long long part = Rl * (long long)di;
+    BWD(moe::launch_bw_nt(G, (const uint16_t*)w_gate, U, (const uint16_t*)w_up, dXp, part,
+                          L.dx_parts / 2, offset, Ei, di, Fi, Rl, cus, s), "moe_backward/dx_perm");
     BWD(moe::launch_bw_tn(x_perm, G, dw_gate, offset, Ei, di, Fi, cus, s), "moe_backward/dw_gate");
     BWD(moe::launch_bw_tn(x_perm, U, dw_up, offset, Ei, di, Fi, cus, s), "moe_backward/dw_up");
     BWD(moe::launch_bw_tn(gH, dy_perm, dw_down, offset, Ei, Fi, di, cus, s), "moe_backward/dw_down");
     // router: dlogit, then dx and the router's weight and bias gradients
     BWD(moe::launch_router_bwd(logits, idx, gate, row_of, dgrow, cfg->T, Ei, ki, cfg->temperature,
                                cfg->renormalize, dl, dgate, s), "moe_backward/router");
-    BWD(moe::launch_dx(dl, (const uint16_t*)w_router, dXp, row_of, (uint16_t*)dx, cfg->T, di, Ei,
-                       ki, s), "moe_backward/dx");
+    BWD(moe::launch_dx(dl, (const uint16_t*)w_router, dXp, L.dx_parts, part, row_of,
+                       (uint16_t*)dx, cfg->T, di, Ei, ki, s), "moe_backward/dx");
     BWD(moe::launch_dwr(xb, dl, dw_router, dbias, cfg->T, di, Ei, w + L.dwr, s), "moe_backward/dwr");
 #undef BWD
     return MOE_OK;
