@@ -141,18 +141,28 @@ def backward_ms(cfg, dev, xs, n_rot, K):
     return a.elapsed_time(b) / K
 
 
+GEMM_SOURCES = ("gemm_mfma.hip", "tiles.h", "lds_dma.h", "common.h")
+
+
+def gemm_source_hash() -> str:
+    """First 16 hex digits of the SHA-256 over the gate/up kernel's sources (the
+    kernel file and the headers it includes, in this order)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "mixture_experts_layer_15_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(cfg):
     """HBM bytes per launch of the gate/up GEMM from the committed FETCH_SIZE /
     WRITE_SIZE counter runs (scaled by a plain copy of known size), or None when
-    they were taken on another workload or the GEMM source has changed since."""
-    import hashlib
+    they were taken on another workload or the GEMM sources have changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_gemm_gate_up_{cfg.name}.json")
     if not os.path.exists(path):
         return None, None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "mixture_experts_layer_15_amd", "csrc", "gemm_mfma.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if rec.get("gemm_source_sha256_16") != sha:
+    if rec.get("gemm_source_sha256_16") != gemm_source_hash():
         return None, None
     return rec["traffic_bytes_per_launch"], rec["kernel"]
 
