@@ -206,12 +206,17 @@ int64_t orc_capacity(int64_t T, int64_t E, int64_t k, int64_t cap_num, int64_t c
  *    first when j' < j, or j' == j and t' < t.
  * pos[t][j] = number of assignments to the same expert before (t, j) in that
  * order.  count = assignments per expert before drops, kept_e = min(count_e,
- * C), offset = exclusive prefix sum of kept (E + 1 entries, offset[E] = rows
- * kept in total).  Rows are grouped by expert in priority order:
- * row = offset[e] + pos, or -1 if dropped; token_of_row[row] = t. */
+ * C).  Rows are grouped by expert in priority order, row = offset[e] + pos
+ * (-1 if dropped), token_of_row[row] = t, in one of two layouts:
+ *  - layout 0, compact: offset = exclusive prefix sum of kept (E + 1 entries,
+ *    offset[E] = rows kept in total), no empty rows;
+ *  - layout 1, padded to capacity (the fixed per-expert buffer that a
+ *    capacity factor implies, a variant): offset[e] = e C, offset[E] = E C;
+ *    the C - kept_e rows after an expert's kept rows are empty
+ *    (token_of_row = -1, which the caller pre-fills). */
 void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C, const int32_t* idx,
                   int32_t* count, int32_t* kept, int32_t* offset, int32_t* pos,
-                  int32_t* row_of, int32_t* token_of_row, int policy) {
+                  int32_t* row_of, int32_t* token_of_row, int policy, int layout) {
     for (int64_t e = 0; e < E; ++e) count[e] = 0;
     if (policy == 0) {
         for (int64_t t = 0; t < T; ++t)
@@ -231,7 +236,7 @@ void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C, const int32_t* idx
     offset[0] = 0;
     for (int64_t e = 0; e < E; ++e) {
         kept[e] = count[e] < C ? count[e] : (int32_t)C;
-        offset[e + 1] = offset[e] + kept[e];
+        offset[e + 1] = layout == 1 ? (int32_t)((e + 1) * C) : offset[e] + kept[e];
     }
     for (int64_t t = 0; t < T; ++t)
         for (int64_t j = 0; j < k; ++j) {

@@ -62,7 +62,8 @@ def _declare(lib):
     lib.orc_route.restype = None
     lib.orc_capacity.argtypes = [_I64, _I64, _I64, _I64, _I64]
     lib.orc_capacity.restype = _I64
-    lib.orc_dispatch.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int]
+    lib.orc_dispatch.argtypes = [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int,
+                                 ctypes.c_int]
     lib.orc_dispatch.restype = None
     lib.orc_load_stats.argtypes = [_I64, _P, _I64, _P]
     lib.orc_load_stats.restype = None
@@ -136,9 +137,12 @@ def capacity(T: int, E: int, k: int, cap_num: int, cap_den: int) -> int:
     return int(_load().orc_capacity(T, E, k, cap_num, cap_den))
 
 
-def dispatch(idx: np.ndarray, E: int, C: int, policy: int = 0) -> Dict[str, np.ndarray]:
+def dispatch(idx: np.ndarray, E: int, C: int, policy: int = 0,
+             layout: int = 0) -> Dict[str, np.ndarray]:
     """Positions in priority order (0: token order, 1: choice order), drops,
-    counts, offsets and the permutation maps."""
+    counts, offsets and the permutation maps, in the compact layout (0) or
+    padded to C rows per expert (1, empty rows marked -1 in token_of_row).
+    n_kept = rows holding a token, n_rows = rows of the layout (offset[E])."""
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     T, k = idx.shape
     count = np.empty(E, dtype=np.int32)
@@ -146,12 +150,13 @@ def dispatch(idx: np.ndarray, E: int, C: int, policy: int = 0) -> Dict[str, np.n
     offset = np.empty(E + 1, dtype=np.int32)
     pos = np.empty((T, k), dtype=np.int32)
     row_of = np.empty((T, k), dtype=np.int32)
-    token_of_row = np.full(T * k, -1, dtype=np.int32)
+    token_of_row = np.full(max(T * k, E * C if layout == 1 else 0), -1, dtype=np.int32)
     _load().orc_dispatch(T, E, k, C, _ptr(idx), _ptr(count), _ptr(kept), _ptr(offset),
-                         _ptr(pos), _ptr(row_of), _ptr(token_of_row), int(policy))
-    n_kept = int(offset[E])
+                         _ptr(pos), _ptr(row_of), _ptr(token_of_row), int(policy), int(layout))
+    n_rows = int(offset[E])
     return dict(count=count, kept=kept, offset=offset, pos=pos, row_of=row_of,
-                token_of_row=token_of_row[:n_kept].copy(), n_kept=n_kept)
+                token_of_row=token_of_row[:n_rows].copy(), n_kept=int(kept.sum()),
+                n_rows=n_rows)
 
 
 def ffn_rows(tokens: Sequence[int], experts: Sequence[int], x, w_gate, w_up, w_down,

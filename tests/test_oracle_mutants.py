@@ -68,6 +68,9 @@ MUTANTS = {
     "expert index ignored": ("int64_t t = tok[r], e = ex[r];", "int64_t t = tok[r], e = 0;"),
     "second expert dropped in combine": ("for (int64_t j = 0; j < k; ++j)\n                if (row_of",
                                          "for (int64_t j = 0; j < 1; ++j)\n                if (row_of"),
+    "padded layout one expert short": (
+        "offset[e + 1] = layout == 1 ? (int32_t)((e + 1) * C)",
+        "offset[e + 1] = layout == 1 ? (int32_t)(e * C)"),
     "single-entry down gradient without the gate": (
         "acc += gate[s] * (act * u) * dy[t * d + b];", "acc += (act * u) * dy[t * d + b];"),
     "single-entry gate gradient with GELU for its derivative": (

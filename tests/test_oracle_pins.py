@@ -476,3 +476,33 @@ def test_token_sample_and_logits_override_agree_with_full_forward():
     np.testing.assert_array_equal(part["y"], full["y"][toks])
     over = orc.forward(x, wr, None, wg, wu, wd, logits_in=full["logits"], **kw)
     np.testing.assert_array_equal(over["y"], full["y"])
+
+
+@pytest.mark.parametrize("C", [0, 1, 3, 7, 40])
+@pytest.mark.parametrize("policy", [0, 1])
+@pytest.mark.parametrize("E,k", [(5, 2), (4, 1), (6, 3)])
+def test_padded_layout_matches_bruteforce(C, policy, E, k):
+    # each expert owns rows e*C .. e*C + C - 1; its kept assignments fill the
+    # first rows in priority order, the rest are empty (-1)
+    T = 40
+    idx = _random_choices(T, E, k, seed=C * 29 + E * 7 + k + 100 * policy)
+    got = orc.dispatch(idx, E, C, policy=policy, layout=1)
+    order = [(t, j) for t in range(T) for j in range(k)] if policy == 0 else \
+        [(t, j) for j in range(k) for t in range(T)]
+    seen = np.zeros(E, dtype=np.int64)
+    row_of = np.full((T, k), -1)
+    tor = np.full(E * C, -1)
+    for t, j in order:
+        e = idx[t, j]
+        if seen[e] < C:
+            row_of[t, j] = e * C + seen[e]
+            tor[e * C + seen[e]] = t
+        seen[e] += 1
+    np.testing.assert_array_equal(got["row_of"], row_of)
+    np.testing.assert_array_equal(got["token_of_row"], tor)
+    np.testing.assert_array_equal(got["offset"], np.arange(E + 1) * C)
+    assert got["n_rows"] == E * C and got["n_kept"] == int((row_of >= 0).sum())
+    # the same assignments are kept as in the compact layout
+    compact = orc.dispatch(idx, E, C, policy=policy)
+    np.testing.assert_array_equal(compact["row_of"] >= 0, row_of >= 0)
+    np.testing.assert_array_equal(got["count"], compact["count"])
