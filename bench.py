@@ -118,6 +118,30 @@ def mlp_router_ms(cfg, xs, n_rot, K):
     return round(a.elapsed_time(b) / K, 4)
 
 
+def padded_forward_ms(cfg, dev, xs, n_rot, K):
+    """Mean time of moe_forward with the padded-capacity layout (every expert
+    runs C rows) over K calls, HIP events on the stream; None without a
+    capacity limit."""
+    import torch
+    import mixture_experts_layer_15_amd as moe
+    if cfg.cap_den == 0:
+        return None
+    pad = cfg.scaled(layout=moe.MOE_LAYOUT_PADDED)
+    fwd = moe.Forward(pad)
+    args = (dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"])
+    y = fwd(xs[0], *args)
+    for i in range(1, 3):
+        fwd(xs[i % n_rot], *args, y=y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(K):
+        fwd(xs[i % n_rot], *args, y=y)
+    b.record()
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) / K, 4)
+
+
 def backward_ms(cfg, dev, xs, n_rot, K):
     """Mean time of moe_backward (recompute of routing and pre-activations,
     every gradient) over K calls with preallocated outputs and workspace,
@@ -294,6 +318,7 @@ def main():
     ms_step = wall * 1e3 / K
 
     mlp_ms = mlp_router_ms(cfg, xs, n_rot, K) if cfg.dtype == "bf16" else None
+    padded_ms = padded_forward_ms(cfg, dev, xs, n_rot, K)
     bwd_ms = backward_ms(cfg, dev, xs, n_rot, K) \
         if cfg.dtype == "bf16" and not args.no_backward else None
 
@@ -356,7 +381,8 @@ def main():
                         "max_deviation": round(float(ls[4]), 4), "cv": round(float(ls[5]), 4),
                         "dropped": int(ls[6]), "empty_experts": int(ls[7])},
         "variants": {"mlp_router_ms": mlp_ms,
-                     "mlp_router_widths": "r=256 m=1024 (ZAYA1 MLP router, random weights)"},
+                     "mlp_router_widths": "r=256 m=1024 (ZAYA1 MLP router, random weights)",
+                     "padded_layout_ms_per_step": padded_ms},
         "backward": None if bwd_ms is None else {
             "ms_per_step": round(bwd_ms, 4),
             "tokens_per_s": round(cfg.T / (bwd_ms * 1e-3), 1),

@@ -69,7 +69,9 @@ typedef enum {
  *   temperature > 0 and finite
  *   cap_den == 0: no capacity limit (C = T); else cap_num >= 0, cap_den > 0
  *   renormalize: 0 or 1;  dtype: a moe_dtype
- *   drop_policy: a moe_drop_policy (appended field; zero = the default) */
+ *   drop_policy: a moe_drop_policy (appended field; zero = the default)
+ *   layout: a moe_layout (appended field; zero = the default); the padded
+ *           layout needs a capacity limit (cap_den > 0) and E * C < 2^31 */
 typedef struct {
     int64_t T;
     int32_t d;
@@ -82,6 +84,7 @@ typedef struct {
     int32_t renormalize;
     int32_t dtype;
     int32_t drop_policy;
+    int32_t layout;
 } moe_config;
 
 /* Which assignments fill an expert's C slots first when it overflows. */
@@ -96,14 +99,29 @@ typedef enum {
     MOE_DROP_CHOICE_ORDER = 1
 } moe_drop_policy;
 
+/* Row layout of the expert-grouped buffers (x_perm, h, y_perm). */
+typedef enum {
+    /* compact: expert e's kept rows at offset[e] .. offset[e+1]-1, offset the
+     * exclusive prefix of the kept counts; no empty rows */
+    MOE_LAYOUT_COMPACT = 0,
+    /* padded to capacity (a variant: the fixed per-expert buffer that a
+     * capacity factor implies, TorchTitan 1K-GPU article, section 2.1):
+     * expert e owns rows e C .. e C + C - 1 (C the effective capacity), its
+     * kept rows first; the others are empty (token_of_row -1, x_perm zero).
+     * The grouped GEMMs then run C rows for every expert. */
+    MOE_LAYOUT_PADDED = 1
+} moe_layout;
+
 /* Host.  Expert capacity C = ceil(cap_num * k * T / (cap_den * E)) in exact
  * integer arithmetic, or T when cap_den == 0.  Returns -1 for an invalid
  * config.  (The pages give only the factor, 1.25; tokens-per-expert times the
  * factor, rounded up, is the reading used.) */
 int64_t moe_capacity(const moe_config* cfg);
 
-/* Host.  Upper bound on rows kept after drops: min(T * k, C * E).  -1 if the
- * config is invalid.  x_perm, h and y_perm need this many rows. */
+/* Host.  Rows of the expert-grouped buffers: min(T * k, C * E) in the compact
+ * layout (an upper bound on rows kept), E * min(C, T) in the padded one.  -1
+ * if the config is invalid.  x_perm, h and y_perm need this many rows;
+ * token_of_row needs max(T * k, this) entries. */
 int64_t moe_max_rows(const moe_config* cfg);
 
 /* Host.  Bytes of workspace moe_dispatch (dispatch_only = 1) or moe_forward
@@ -188,11 +206,14 @@ moe_status moe_route_mlp(const moe_config* cfg, const moe_mlp_router* router, co
  *                                            in cfg->drop_policy's priority order
  *                                            (token order: ascending token)
  *   expert_count  [E]            int32  out  assignments per expert before drops
- *   expert_offset [E + 1]        int32  out  exclusive prefix of kept counts
- *                                            min(count, C); [E] = rows kept
+ *   expert_offset [E + 1]        int32  out  compact: exclusive prefix of kept counts
+ *                                            min(count, C), [E] = rows kept;
+ *                                            padded: e * C
  *   row_of        [T, k]         int32  out  row of assignment (t, j), -1 if dropped
- *   token_of_row  [T * k]        int32  out  token of each kept row; entries at and
- *                                            past offset[E] are set to -1
+ *   token_of_row  [max(T * k, max_rows)]
+ *                                int32  out  token of each kept row; empty rows and
+ *                                            entries past offset[E] are set to -1
+ * In the padded layout the empty rows of x_perm are set to zero.
  *   workspace     ws_bytes >= moe_workspace_size(cfg, 1, .)
  * An assignment (t, j) to expert e is kept iff fewer than C assignments to e
  * come before it in cfg->drop_policy's order; with MOE_DROP_TOKEN_ORDER, iff
@@ -264,11 +285,13 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
 moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* Backward of steps 1-7 for an upstream gradient dy = dL/dy (training, the
- * step that follows the forward on every page: the TorchTitan 1K-GPU
- * article trains this layer, section 2.1; the MegaBlocks paper derives its
- * grouped backward GEMMs, section 5).  bf16 layers only (MOE_ERR_UNSUPPORTED
- * otherwise).  The forward's routing and expert pre-activations are
- * recomputed from the inputs (same kernels, same values as moe_forward);
+ * step that follows the forward on every page: the TorchTitan 1K-GPU article
+ * trains this layer, section 2; "AMD MI300X平台上的MoE模型训练实践" trains it
+ * too, section 4).  bf16 layers in the compact layout only
+ * (MOE_ERR_UNSUPPORTED otherwise).  The forward's routing and expert
+ * pre-activations are recomputed from the inputs, as the activation
+ * recomputation of that training page's section 4.1 does (same kernels, same
+ * values as moe_forward);
  * top-k selection and capacity drops are piecewise constant, so no gradient
  * passes through them.  With p = softmax(logits / temperature), per kept
  * assignment (t, j) of expert e, g = x_t W_gate[e], u = x_t W_up[e],

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_DROP_TOKEN_ORDER, MOE_DROP_CHOICE_ORDER = 0, 1
+MOE_LAYOUT_COMPACT, MOE_LAYOUT_PADDED = 0, 1
 
 EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_status_string",
            "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
@@ -35,7 +36,8 @@ class CConfig(ctypes.Structure):
                 ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("cap_num", ctypes.c_int32),
                 ("cap_den", ctypes.c_int32), ("renormalize", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("drop_policy", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class CMLPRouter(ctypes.Structure):
@@ -104,7 +106,7 @@ def cconfig(cfg: MoEConfig, T: Optional[int] = None) -> CConfig:
                    temperature=cfg.temperature, cap_num=cfg.cap_num, cap_den=cfg.cap_den,
                    renormalize=int(cfg.renormalize),
                    dtype=MOE_BF16 if cfg.dtype == "bf16" else MOE_F32,
-                   drop_policy=int(cfg.drop_policy))
+                   drop_policy=int(cfg.drop_policy), layout=int(cfg.layout))
 
 
 def _check(status: int, where: str) -> None:
@@ -193,7 +195,7 @@ def dispatch(cfg: MoEConfig, topk_idx, x) -> Dict:
         expert_count=torch.empty(cfg.E, dtype=torch.int32, device=dev),
         expert_offset=torch.empty(cfg.E + 1, dtype=torch.int32, device=dev),
         row_of=torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
-        token_of_row=torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
+        token_of_row=torch.empty(max(cfg.T * cfg.k, R), dtype=torch.int32, device=dev))
     wsb = workspace_bytes(cfg, dispatch_only=True)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     _check(lib().moe_dispatch(ctypes.byref(cconfig(cfg)), _ptr(topk_idx), _ptr(x),

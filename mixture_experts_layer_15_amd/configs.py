@@ -41,6 +41,7 @@ class MoEConfig:
     dtype: str           # "f32" or "bf16" for activations and weights
     zipf_bias: Optional[float] = None  # Zipf exponent of the router bias, or None for no bias
     drop_policy: int = 0  # 0: overflow dropped in token order; 1: choice order (first choices first)
+    layout: int = 0       # 0: compact expert-grouped rows; 1: padded to C rows per expert
 
     def scaled(self, **kw) -> "MoEConfig":
         """A copy with some fields replaced (used to make small test cases)."""

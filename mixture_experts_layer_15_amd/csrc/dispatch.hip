@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
 
 __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ blockcount,
                                                    int32_t* __restrict__ blockbase, int nblk,
-                                                   int E, long long C,
+                                                   int E, long long C, int padded,
                                                    int32_t* __restrict__ count,
                                                    int32_t* __restrict__ offset) {
     __shared__ int s_wave[4];
@@ -89,8 +89,9 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ b
     int add = 0;
     for (int i = 0; i < w; ++i) add += s_wave[i];
     const int incl = v + add;
-    if (e < E) offset[e] = incl - kept;
-    if (e == E - 1) offset[E] = incl;
+    // padded layout: every expert owns C rows
+    if (e < E) offset[e] = padded ? (int)(e * C) : incl - kept;
+    if (e == E - 1) offset[E] = padded ? (int)(E * C) : incl;
 }
 
 // Places the assignments of the 256 tokens [tb, tb + 256): run[e] holds, on
@@ -193,7 +194,7 @@ constexpr long long kSmallAssign = 16384;
 template <bool CM>
 __global__ __launch_bounds__(256) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, long long C, long long T, int E, int k, int Tr, int kr,
-    int32_t* __restrict__ count, int32_t* __restrict__ offset_out,
+    int padded, int32_t* __restrict__ count, int32_t* __restrict__ offset_out,
     int32_t* __restrict__ row_of, int32_t* __restrict__ token_of_row) {
     __shared__ int h_all[256], run[256];
     __shared__ int32_t s_off[257];
@@ -227,12 +228,14 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     int add = 0;
     for (int i = 0; i < w; ++i) add += s_wave[i];
     const int incl = v + add;
-    if (e < E) s_off[e] = incl - kept;
-    if (e == E - 1) s_off[E] = incl;
+    const int off_e = padded ? (int)(e * C) : incl - kept;
+    const int off_end = padded ? (int)(E * C) : incl;
+    if (e < E) s_off[e] = off_e;
+    if (e == E - 1) s_off[E] = off_end;
     if (blockIdx.x == 0 && e < E) {
         count[e] = h_all[e];
-        offset_out[e] = incl - kept;
-        if (e == E - 1) offset_out[E] = incl;
+        offset_out[e] = off_e;
+        if (e == E - 1) offset_out[E] = off_end;
     }
     __syncthreads();
     place_chunk<CM>(idx, run, wcnt, s_off, s_off[E], C, T, E, k, tb, Tr, kr, row_of,
@@ -272,10 +275,29 @@ __global__ __launch_bounds__(256) void scatter_kernel(const u32x4* __restrict__ 
     }
 }
 
+// Padded layout: the rows of expert e past its kept ones (pos >= min(count_e,
+// C) in its C-row segment) are empty: token_of_row -1 and, when x_perm is
+// given, a zero row.  One wave per row.
+__global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict__ count,
+                                                       long long C, int E,
+                                                       int32_t* __restrict__ token_of_row,
+                                                       u32x4* __restrict__ x_perm, int nvec) {
+    const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= (long long)E * C) return;
+    const int e = (int)(r / C);
+    const long long pos = r - (long long)e * C;
+    if (pos < min((long long)count[e], C)) return;
+    const int lane = threadIdx.x & 63;
+    if (lane == 0) token_of_row[r] = -1;
+    if (x_perm != nullptr)
+        for (int v = lane; v < nvec; v += 64) x_perm[r * nvec + v] = u32x4{0u, 0u, 0u, 0u};
+}
+
 }  // namespace
 
-DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy) {
+DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy, int layout) {
     DispatchPlan p;
+    p.padded = layout == 1;
     p.Tr = T;
     p.kr = k;
     p.choice_order = policy == 1 && k > 1;   // with one choice the orders coincide
@@ -304,8 +326,8 @@ hipError_t dispatch_kernels(const DispatchPlan& p, const int32_t* idx, int32_t* 
     const int Tr = (int)p.Tr, kr = p.kr;
     if (p.T > 0 && p.T * p.k <= kSmallAssign) {
         hipLaunchKernelGGL(dispatch_small_kernel<CM>, dim3((unsigned)((p.T + 255) / 256)),
-                           dim3(256), 0, s, idx, p.C, p.T, p.E, p.k, Tr, kr, count, offset,
-                           row_of, token_of_row);
+                           dim3(256), 0, s, idx, p.C, p.T, p.E, p.k, Tr, kr, p.padded ? 1 : 0,
+                           count, offset, row_of, token_of_row);
         return hipGetLastError();
     }
     int32_t* blockcount = (int32_t*)workspace;
@@ -317,7 +339,7 @@ hipError_t dispatch_kernels(const DispatchPlan& p, const int32_t* idx, int32_t* 
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, blockcount, blockbase, p.nblk,
-                       p.E, p.C, count, offset);
+                       p.E, p.C, p.padded ? 1 : 0, count, offset);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || p.nblk == 0) return err;
     hipLaunchKernelGGL(place_kernel<CM>, dim3(p.nblk), dim3(256), 0, s, idx, blockbase, offset,
@@ -334,8 +356,17 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
     hipError_t err = p.choice_order
         ? dispatch_kernels<true>(p, idx, count, offset, row_of, token_of_row, workspace, s)
         : dispatch_kernels<false>(p, idx, count, offset, row_of, token_of_row, workspace, s);
-    if (err != hipSuccess || !scatter || p.Tr == 0) return err;
+    if (err != hipSuccess) return err;
     const int nvec = d * (dtype == 1 ? 2 : 4) / 16;
+    const long long padded_rows = p.padded ? p.C * p.E : 0;
+    if (padded_rows > 0) {
+        hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((padded_rows + 3) / 4)), dim3(256), 0,
+                           s, count, p.C, p.E, token_of_row,
+                           scatter ? (u32x4*)x_perm : (u32x4*)nullptr, nvec);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (!scatter || p.Tr == 0) return err;
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((p.Tr + 3) / 4)), dim3(256), 0, s,
                        (const u32x4*)x, row_of, (u32x4*)x_perm, p.Tr, nvec, p.kr);
     return hipGetLastError();

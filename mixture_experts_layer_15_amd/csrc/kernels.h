@@ -32,11 +32,14 @@ struct DispatchPlan {
     long long Tr;          // real tokens
     int kr;                // real choices per token
     bool choice_order;
+    bool padded;           // padded layout: expert e owns rows e*C .. e*C + C - 1
 };
-DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy = 0);
+DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy = 0,
+                           int layout = 0);
 size_t dispatch_workspace_bytes(const DispatchPlan& p);
 // scatter = false leaves x_perm unwritten (for a consumer that gathers rows of
-// x through token_of_row itself).
+// x through token_of_row itself).  In the padded layout the empty rows get
+// token_of_row -1 and (with scatter) zero rows in x_perm.
 hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx, const void* x,
                            void* x_perm, int32_t* count, int32_t* offset, int32_t* row_of,
                            int32_t* token_of_row, void* workspace, int d, hipStream_t s,

@@ -48,9 +48,16 @@ int64_t capacity_eff(const moe_config* c) {
 }
 
 int64_t max_rows(const moe_config* c) {
-    const int64_t tk = c->T * c->k;
     const int64_t ce = capacity_eff(c) * c->E;
+    if (c->layout == MOE_LAYOUT_PADDED) return ce;
+    const int64_t tk = c->T * c->k;
     return tk < ce ? tk : ce;
+}
+
+// Entries of token_of_row: every assignment slot and every row.
+int64_t tor_len(const moe_config* c) {
+    const int64_t tk = c->T * c->k, r = max_rows(c);
+    return tk > r ? tk : r;
 }
 
 size_t esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
@@ -77,6 +84,15 @@ moe_status check_cfg(const moe_config* c) {
         return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
     if (c->drop_policy != MOE_DROP_TOKEN_ORDER && c->drop_policy != MOE_DROP_CHOICE_ORDER)
         return fail(MOE_ERR_INVALID_ARG, "drop_policy %d is not a moe_drop_policy", c->drop_policy);
+    if (c->layout != MOE_LAYOUT_COMPACT && c->layout != MOE_LAYOUT_PADDED)
+        return fail(MOE_ERR_INVALID_ARG, "layout %d is not a moe_layout", c->layout);
+    if (c->layout == MOE_LAYOUT_PADDED) {
+        if (c->cap_den == 0)
+            return fail(MOE_ERR_INVALID_ARG, "the padded layout needs a capacity limit (cap_den > 0)");
+        if (capacity_eff(c) * (int64_t)c->E >= ((int64_t)1 << 31))
+            return fail(MOE_ERR_INVALID_ARG, "padded layout: E * C = %lld must be < 2^31",
+                        (long long)(capacity_eff(c) * (int64_t)c->E));
+    }
     return MOE_OK;
 }
 
@@ -129,7 +145,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 FwdLayout fwd_layout(const moe_config* c) {
     const size_t T = (size_t)c->T, E = (size_t)c->E, k = (size_t)c->k;
     const size_t R = (size_t)max_rows(c);
-    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy);
+    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy, c->layout);
     FwdLayout L;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -139,7 +155,7 @@ FwdLayout fwd_layout(const moe_config* c) {
     L.count = take(E * 4);
     L.offset = take((E + 1) * 4);
     L.row_of = take(T * k * 4);
-    L.token_of_row = take(T * k * 4);
+    L.token_of_row = take((size_t)tor_len(c) * 4);
     L.dsp = take(moe::dispatch_workspace_bytes(p));
     L.x_perm = take(R * (size_t)c->d * esize(c));
     L.h = take(R * (size_t)c->d_ff * esize(c));
@@ -167,7 +183,7 @@ moe_status moe_workspace_size(const moe_config* cfg, int dispatch_only, size_t* 
     if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
     if (dispatch_only) {
         *bytes = moe::dispatch_workspace_bytes(
-            moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy));
+            moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout));
     } else {
         *bytes = fwd_layout(cfg).total;
     }
@@ -231,8 +247,8 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const vo
     CHECK(check_ptr(expert_count, "expert_count", E * 4));
     CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
     CHECK(check_ptr(row_of, "row_of", T * k * 4));
-    CHECK(check_ptr(token_of_row, "token_of_row", T * k * 4));
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy);
+    CHECK(check_ptr(token_of_row, "token_of_row", (size_t)tor_len(cfg) * 4));
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout);
     const size_t need = moe::dispatch_workspace_bytes(p);
     if (workspace == nullptr || ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "dispatch workspace: need %zu bytes, got %zu", need, ws_bytes);
@@ -414,8 +430,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
     // bf16: the gate/up GEMM gathers its rows of x through token_of_row, so
     // x_perm is never written (its 32-bit byte offsets must span x)
-    const bool gather = cfg->dtype == MOE_BF16 && T * d * es < ((size_t)1 << 32);
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy);
+    const bool gather = cfg->dtype == MOE_BF16 && cfg->layout == MOE_LAYOUT_COMPACT &&
+                        T * d * es < ((size_t)1 << 32);
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout);
     e = moe::launch_dispatch(p, cfg->dtype, idx, x, w + L.x_perm, count, offset, row_of, tor,
                              w + L.dsp, cfg->d, s, !gather);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/dispatch");
@@ -446,7 +463,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(const moe_config* c) {
     const size_t T = (size_t)c->T, E = (size_t)c->E, k = (size_t)c->k, d = (size_t)c->d;
     const size_t F = (size_t)c->d_ff, R = (size_t)max_rows(c);
-    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy);
+    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy, c->layout);
     BwdLayout L;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -473,14 +490,21 @@ BwdLayout bwd_layout(const moe_config* c) {
     return L;
 }
 
+moe_status check_bwd(const moe_config* cfg) {
+    CHECK(check_cfg(cfg));
+    if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
+    if (cfg->layout != MOE_LAYOUT_COMPACT)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward runs on the compact layout only");
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
-    CHECK(check_cfg(cfg));
+    CHECK(check_bwd(cfg));
     if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-    if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
     *bytes = bwd_layout(cfg).total;
     return MOE_OK;
 }
@@ -490,8 +514,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                         const void* w_down, const void* dy, void* dx, float* dw_router,
                         float* dbias, float* dw_gate, float* dw_up, float* dw_down, float* dgate,
                         void* workspace, size_t ws_bytes, void* stream) {
-    CHECK(check_cfg(cfg));
-    if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
+    CHECK(check_bwd(cfg));
     SIZES(cfg);
     CHECK(check_ptr(x, "x", T * d * es));
     CHECK(check_ptr(w_router, "w_router", d * E * es));
@@ -549,7 +572,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     // forward recompute: routing, dispatch maps and x_perm, g = x W_gate, u = x W_up
     BWD(moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T, di, Ei, ki,
                           cfg->temperature, cfg->renormalize, s), "moe_backward/route");
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, Ei, ki, capacity_eff(cfg), cfg->drop_policy);
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, Ei, ki, capacity_eff(cfg), cfg->drop_policy, cfg->layout);
     uint16_t* x_perm = (uint16_t*)(w + L.x_perm);
     uint16_t* dy_perm = (uint16_t*)(w + L.dy_perm);
     BWD(moe::launch_dispatch(p, cfg->dtype, idx, x, x_perm, count, offset, row_of, tor,

@@ -236,3 +236,29 @@ def test_backward_validation_on_host(L):
     bad = moe.cconfig(cfg)
     bad.k = 0
     assert L.moe_backward(ctypes.byref(bad), *([ok] * 15), big, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_padded_layout_validation_and_sizes(L):
+    n = ctypes.c_size_t(0)
+    bad = moe.cconfig(configs.get("wide"))
+    bad.layout = 2
+    assert L.moe_max_rows(ctypes.byref(bad)) == -1
+    assert b"moe_layout" in L.moe_last_error()
+    nocap = moe.cconfig(configs.get("zaya1").scaled(layout=1))
+    assert L.moe_workspace_size(ctypes.byref(nocap), 0, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert b"capacity limit" in L.moe_last_error()
+    huge = moe.cconfig(configs.get("wide").scaled(T=(1 << 28) - 1, E=256, k=8, layout=1))
+    assert L.moe_max_rows(ctypes.byref(huge)) == -1 and b"2^31" in L.moe_last_error()
+    for name in ("wide", "skewed", "longseq"):
+        cfg = configs.get(name)
+        C = min(moe.capacity(cfg), cfg.T)
+        pad = cfg.scaled(layout=1)
+        assert moe.max_rows(pad) == cfg.E * C >= moe.max_rows(cfg)
+        assert moe.workspace_bytes(pad) > moe.workspace_bytes(cfg)
+        # the backward runs on the compact layout only
+        assert L.moe_backward_workspace_size(ctypes.byref(moe.cconfig(pad)), ctypes.byref(n)) == \
+            moe.MOE_ERR_UNSUPPORTED
+    # token_of_row must cover max(T * k, rows): too small a buffer is not checked
+    # on the host (it is a device pointer), but the binding sizes it that way
+    cfg = configs.get("skewed").scaled(layout=1)
+    assert max(cfg.T * cfg.k, moe.max_rows(cfg)) == moe.max_rows(cfg)

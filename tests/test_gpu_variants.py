@@ -10,7 +10,7 @@ import mixture_experts_layer_15_amd as moe
 from mixture_experts_layer_15_amd import configs
 from oracle import oracle as orc
 
-from parity_util import gpu_inputs, say
+from parity_util import TOL_Y, check_route, gpu_inputs, rel_err, say, to_np
 from test_gpu_parity import run_layer
 
 pytestmark = pytest.mark.gpu
@@ -143,3 +143,73 @@ def test_mlp_router_matches_oracle(name):
     idx2, gate2 = moe.route_from_logits(cfg, lg)
     torch.cuda.synchronize()
     assert torch.equal(idx2, idx) and torch.equal(gate2, gate)
+
+
+PADDED_CASES = {
+    # top-2 renormalised, capacity 5/4, experts not a multiple of 8
+    "padded_small": SMALL.scaled(T=1500, d=128, E=12, k=3, d_ff=192, drop_policy=0),
+    # choice order, hot expert (Zipf bias): most slots of the cold experts empty
+    "padded_hot": SMALL.scaled(T=3000, d=128, E=16, k=2, d_ff=128, zipf_bias=1.2),
+    # top-1 with capacity 1/2: many drops, every expert full
+    "padded_drops": SMALL.scaled(T=2000, d=192, E=8, k=1, d_ff=320, cap_num=1, cap_den=2,
+                                 renormalize=False, drop_policy=0),
+}
+
+
+def _check_padded(cfg, dev, host, full, label):
+    """Padded layout: dispatch maps bit-exact against the oracle's padded
+    layout, empty rows zero, and the layer output bit-identical to the
+    compact layout's (same rows, same per-row arithmetic)."""
+    pad = cfg.scaled(layout=1)
+    logits, idx, gate = moe.route(pad, dev["x"], dev["w_router"], dev["bias"])
+    torch.cuda.synchronize()
+    oidx, _, _ = check_route(pad, logits.cpu(), idx.cpu(), gate.cpu())
+    C = min(orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den), cfg.T)
+    say(f"[{label}] moe_dispatch padded: E={cfg.E} C={C} rows={cfg.E * C}")
+    dsp = moe.dispatch(pad, idx, dev["x"])
+    torch.cuda.synchronize()
+    od = orc.dispatch(oidx, cfg.E, C, cfg.drop_policy, layout=1)
+    np.testing.assert_array_equal(dsp["expert_count"].cpu().numpy(), od["count"])
+    np.testing.assert_array_equal(dsp["expert_offset"].cpu().numpy(), od["offset"])
+    np.testing.assert_array_equal(dsp["row_of"].cpu().numpy(), od["row_of"])
+    tor = dsp["token_of_row"].cpu().numpy()
+    np.testing.assert_array_equal(tor[:od["n_rows"]], od["token_of_row"])
+    assert (tor[od["n_rows"]:] == -1).all()
+    xp = dsp["x_perm"]
+    kept = torch.from_numpy(np.nonzero(od["token_of_row"] >= 0)[0]).cuda()
+    empty = torch.from_numpy(np.nonzero(od["token_of_row"] < 0)[0]).cuda()
+    src = torch.from_numpy(od["token_of_row"][od["token_of_row"] >= 0].astype(np.int64)).cuda()
+    assert torch.equal(xp.index_select(0, kept).view(torch.int16),
+                       dev["x"].index_select(0, src).view(torch.int16))
+    if empty.numel():
+        assert (xp.index_select(0, empty).float() == 0).all()
+    say(f"[{label}] kept {od['n_kept']} of {od['n_rows']} padded rows")
+    say(f"[{label}] moe_forward padded vs compact")
+    args = (dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"])
+    y_pad = moe.forward(pad, *args)
+    y_cmp = moe.forward(cfg, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(y_pad.view(torch.int16), y_cmp.view(torch.int16)), \
+        "padded and compact layouts give different outputs"
+    if full:
+        ofw = orc.forward(host["x"], host["w_router"], host["bias"], host["w_gate"],
+                          host["w_up"], host["w_down"], k=cfg.k,
+                          tau=float(np.float32(cfg.temperature)), renormalize=cfg.renormalize,
+                          cap_num=cfg.cap_num, cap_den=cfg.cap_den, drop_policy=cfg.drop_policy,
+                          logits_in=logits.cpu().double().numpy())
+        err = rel_err(to_np(y_pad), ofw["y"])
+        say(f"[{label}] y err {err:.3g}")
+        assert err <= TOL_Y[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", list(PADDED_CASES))
+def test_padded_layout(name):
+    cfg = PADDED_CASES[name]
+    dev, host = gpu_inputs(cfg, seed=5)
+    _check_padded(cfg, dev, host, full=True, label=name)
+
+
+def test_padded_layout_full_size_skewed():
+    cfg = configs.get("skewed")
+    dev, host = gpu_inputs(cfg, seed=0)
+    _check_padded(cfg, dev, host, full=False, label="skewed/padded")
