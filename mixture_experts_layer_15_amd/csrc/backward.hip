@@ -189,105 +189,188 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
 
 // dx[t][i] = sum_j sum_p dXp_p[row_of[t, j]][i] + sum_e dl[t][e] Wr[i][e]
 // (bf16 out; the parts p of the expert input gradient in part order).
-// Tile 64 tokens x 64 columns, 4 x 4 per thread, e in chunks of 16 via LDS.
+// dl W_r^T on v_mfma_f32_16x16x32_bf16 with dl split into two bf16 terms
+// (hi = bf16(dl), lo = bf16(dl - hi): about 16 bits of dl, W_r exact), both
+// operands read from global memory straight into the fragment layout (lane
+// (c16, g4): index c16, K values 8 g4 .. + 7).  Workgroup: 64 tokens x 256
+// columns, each wave 64 x 64 (4 x 4 blocks of 16 x 16).  VEC: E % 8 == 0, so
+// eight K values are one aligned vector.
+template <bool VEC>
 __global__ __launch_bounds__(256) void dx_kernel(
     const float* __restrict__ dl, const uint16_t* __restrict__ wr,
     const float* __restrict__ dXp, int nparts, long long part_stride,
     const int32_t* __restrict__ row_of, uint16_t* __restrict__ dx, long long T, int d, int E,
     int k) {
-    __shared__ float s_l[16][64 + 4];
-    __shared__ float s_w[16][64 + 4];
-    const int tid = threadIdx.x, tt = tid >> 4, ti = tid & 15;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c16 = lane & 15, g4 = lane >> 4;
     const long long t0 = (long long)blockIdx.x * 64;
-    const int i0 = blockIdx.y * 64;
-    float acc[4][4] = {};
-    for (int e0 = 0; e0 < E; e0 += 16) {
+    const int i0 = blockIdx.y * 256 + w * 64;
+    f32x4 acc[4][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int q = tid + 256 * s, mm = q >> 4, kk = q & 15;
-            const long long t = t0 + mm;
-            const int e = e0 + kk;
-            s_l[kk][mm] = (t < T && e < E) ? dl[t * E + e] : 0.f;
-            s_w[kk][mm] = e < E ? bf16_bits_to_f32(wr[(long long)(i0 + mm) * E + e]) : 0.f;
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e0 = 0; e0 < E; e0 += 32) {
+        const int ek = e0 + 8 * g4;   // this lane's first K value
+        bf16x8 fb[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const int i = i0 + jb * 16 + c16;
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (i < d) {
+                const uint16_t* src = wr + (long long)i * E + ek;
+                if (VEC) {
+                    if (ek < E) raw = *(const u32x4*)src;
+                } else {
+                    uint32_t h[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) h[u] = ek + u < E ? src[u] : 0u;
+                    raw = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                h[6] | (h[7] << 16)};
+                }
+            }
+            fb[jb] = __builtin_bit_cast(bf16x8, raw);
         }
-        __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            const f32x4 a = *(const f32x4*)&s_l[kk][tt * 4];
-            const f32x4 b = *(const f32x4*)&s_w[kk][ti * 4];
+        for (int ib = 0; ib < 4; ++ib) {
+            const long long t = t0 + ib * 16 + c16;
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (t < T) {
+                const float* src = dl + t * E + ek;
+                if (VEC) {
+                    if (ek < E) {
+                        const f32x4 v0 = *(const f32x4*)src, v1 = *(const f32x4*)(src + 4);
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+                        for (int u = 0; u < 4; ++u) {
+                            v[u] = v0[u];
+                            v[4 + u] = v1[u];
+                        }
+                    }
+                } else {
 #pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+                    for (int u = 0; u < 8; ++u) v[u] = ek + u < E ? src[u] : 0.f;
+                }
+            }
+            bf16x8 hi, lo;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                hi[u] = (__bf16)v[u];
+                lo[u] = (__bf16)(v[u] - (float)hi[u]);
+            }
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                acc[ib][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[jb], hi, acc[ib][jb], 0, 0, 0);
+                acc[ib][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[jb], lo, acc[ib][jb], 0, 0, 0);
+            }
         }
-        __syncthreads();
     }
-    const int i = i0 + ti * 4;
+    // router part through LDS (lane (g4, c16) of block (ib, jb): token
+    // ib*16 + c16, columns jb*16 + 4 g4 .. + 3), then one wave per token row:
+    // its 256 columns of each expert part are one contiguous 1 KB read
+    __shared__ __attribute__((aligned(16))) float s_acc[64][256 + 4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const long long t = t0 + tt * 4 + x;
-        if (t >= T) continue;
-        f32x4 v = {acc[x][0], acc[x][1], acc[x][2], acc[x][3]};
-        for (int j = 0; j < k; ++j) {
-            const int rr = row_of[t * k + j];
-            if (rr < 0) continue;
-            for (int p = 0; p < nparts; ++p)
-                v += *(const f32x4*)(dXp + p * part_stride + (long long)rr * d + i);
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            *(f32x4*)&s_acc[ib * 16 + c16][w * 64 + jb * 16 + 4 * g4] = acc[ib][jb];
+    __syncthreads();
+    const int col = blockIdx.y * 256 + 4 * lane;
+    if (col >= d) return;   // d is a multiple of 64: whole 4-column groups
+    for (int r0 = 0; r0 < 16; r0 += 4) {   // four rows at a time: their loads in flight together
+        f32x4 v[4];
+        long long t[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            t[q] = t0 + w * 16 + r0 + q;
+            v[q] = *(const f32x4*)&s_acc[w * 16 + r0 + q][4 * lane];
         }
-        *(u32x2*)(dx + t * d + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        for (int j = 0; j < k; ++j) {
+            int rr[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rr[q] = t[q] < T ? row_of[t[q] * k + j] : -1;
+            for (int p = 0; p < nparts; ++p) {
+                const float* base = dXp + p * part_stride + col;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (rr[q] >= 0) v[q] += *(const f32x4*)(base + (long long)rr[q] * d);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (t[q] < T)
+                *(u32x2*)(dx + t[q] * d + col) =
+                    u32x2{pack_bf16x2(v[q][0], v[q][1]), pack_bf16x2(v[q][2], v[q][3])};
     }
 }
 
 // Partial router weight gradients over one split of the tokens:
 // part[s][i][e] = sum_{t in split s} x[t][i] dl[t][e]; the first column tile
-// also writes bpart[s][e] = sum_t dl[t][e].  Tile 64 (i) x 64 (e).
-__global__ __launch_bounds__(256) void dwr_part_kernel(
+// also writes bpart[s][e] = sum_t dl[t][e].  Tile 256 (i) x 64 (e), 8 x 8 per
+// thread, t in chunks of 16 through LDS.
+__global__ __launch_bounds__(256, 2) void dwr_part_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ dl, float* __restrict__ part,
     float* __restrict__ bpart, long long T, int d, int E, long long split) {
-    __shared__ float s_x[16][64 + 4];
-    __shared__ float s_l[16][64 + 4];
-    const int tid = threadIdx.x, ti = tid >> 4, te = tid & 15;
-    const int i0 = blockIdx.x * 64, e0 = blockIdx.y * 64, s = blockIdx.z;
+    __shared__ __attribute__((aligned(16))) float s_x[16][256];
+    __shared__ __attribute__((aligned(16))) float s_l[16][64];
+    const int tid = threadIdx.x, ti = tid >> 3, te = tid & 7;
+    const int i0 = blockIdx.x * 256, e0 = blockIdx.y * 64, s = blockIdx.z;
     const long long ta = (long long)s * split, tb = min(T, ta + split);
-    float acc[4][4] = {};
-    float bacc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[8][8] = {};
+    float bacc[8] = {};
     const bool do_b = blockIdx.x == 0 && ti == 0;
     for (long long tc = ta; tc < tb; tc += 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 2; ++r) {   // x: 16 tokens x 256 columns, 8 per thread
+            const int q = tid + 256 * r, kk = q >> 5, c8 = (q & 31) * 8;
+            const long long t = tc + kk;
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (t < tb && i0 + c8 < d) {
+                const u32x4 raw = *(const u32x4*)(x + t * d + i0 + c8);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = Elem<uint16_t>::to_f32(raw, u);
+            }
+            *(f32x4*)&s_x[kk][c8] = f32x4{v[0], v[1], v[2], v[3]};
+            *(f32x4*)&s_x[kk][c8 + 4] = f32x4{v[4], v[5], v[6], v[7]};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {   // dl: 16 tokens x 64 e
             const int q = tid + 256 * r, kk = q >> 6, c = q & 63;
             const long long t = tc + kk;
-            s_x[kk][c] = t < tb ? bf16_bits_to_f32(x[t * d + i0 + c]) : 0.f;
             s_l[kk][c] = (t < tb && e0 + c < E) ? dl[t * E + e0 + c] : 0.f;
         }
         __syncthreads();
-#pragma unroll
+#pragma unroll 2
         for (int kk = 0; kk < 16; ++kk) {
-            const f32x4 a = *(const f32x4*)&s_x[kk][ti * 4];
-            const f32x4 b = *(const f32x4*)&s_l[kk][te * 4];
+            const f32x4 a0 = *(const f32x4*)&s_x[kk][ti * 8];
+            const f32x4 a1 = *(const f32x4*)&s_x[kk][ti * 8 + 4];
+            const f32x4 b0 = *(const f32x4*)&s_l[kk][te * 8];
+            const f32x4 b1 = *(const f32x4*)&s_l[kk][te * 8 + 4];
+            const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
 #pragma unroll
-            for (int xx = 0; xx < 4; ++xx)
+            for (int xx = 0; xx < 8; ++xx)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) acc[xx][y] = fmaf(a[xx], b[y], acc[xx][y]);
+                for (int y = 0; y < 8; ++y) acc[xx][y] = fmaf(a[xx], b[y], acc[xx][y]);
             if (do_b)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) bacc[y] += b[y];
+                for (int y = 0; y < 8; ++y) bacc[y] += b[y];
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int xx = 0; xx < 4; ++xx) {
-        const int i = i0 + ti * 4 + xx;
+    for (int xx = 0; xx < 8; ++xx) {
+        const int i = i0 + ti * 8 + xx;
+        if (i >= d) continue;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int e = e0 + te * 4 + y;
+        for (int y = 0; y < 8; ++y) {
+            const int e = e0 + te * 8 + y;
             if (e < E) part[((long long)s * d + i) * E + e] = acc[xx][y];
         }
     }
     if (do_b)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int e = e0 + te * 4 + y;
+        for (int y = 0; y < 8; ++y) {
+            const int e = e0 + te * 8 + y;
             if (e < E) bpart[(long long)s * E + e] = bacc[y];
         }
 }
@@ -347,14 +430,19 @@ hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp, int 
                      int d, int E, int k, hipStream_t s) {
     if (T == 0) return hipSuccess;
     if (d % 64 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(dx_kernel, dim3((unsigned)((T + 63) / 64), d / 64), dim3(256), 0, s, dl,
-                       wr, dXp, nparts, part_stride, row_of, dx, T, d, E, k);
+    const dim3 grid((unsigned)((T + 63) / 64), (d + 255) / 256);
+    if (E % 8 == 0)
+        hipLaunchKernelGGL(dx_kernel<true>, grid, dim3(256), 0, s, dl, wr, dXp, nparts,
+                           part_stride, row_of, dx, T, d, E, k);
+    else
+        hipLaunchKernelGGL(dx_kernel<false>, grid, dim3(256), 0, s, dl, wr, dXp, nparts,
+                           part_stride, row_of, dx, T, d, E, k);
     return hipGetLastError();
 }
 
 int dwr_splits(long long T, int d, int E) {
-    const long long tiles = (long long)(d / 64) * ((E + 63) / 64);
-    long long ns = (1024 + tiles - 1) / tiles;
+    const long long tiles = (long long)((d + 255) / 256) * ((E + 63) / 64);
+    long long ns = (512 + tiles - 1) / tiles;   // about two workgroups per CU
     ns = std::min<long long>(ns, std::max<long long>(1, (T + 63) / 64));
     return (int)std::max<long long>(1, std::min<long long>(ns, 4096));
 }
@@ -371,7 +459,7 @@ hipError_t launch_dwr(const uint16_t* x, const float* dl, float* dwr, float* dbi
     const long long split = T == 0 ? 1 : ((T + ns - 1) / ns + 15) / 16 * 16;
     float* part = (float*)ws;
     float* bpart = part + (size_t)ns * d * E;
-    hipLaunchKernelGGL(dwr_part_kernel, dim3(d / 64, (E + 63) / 64, ns), dim3(256), 0, s, x, dl,
+    hipLaunchKernelGGL(dwr_part_kernel, dim3((d + 255) / 256, (E + 63) / 64, ns), dim3(256), 0, s, x, dl,
                        part, bpart, T, d, E, split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
