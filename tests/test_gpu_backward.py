@@ -56,6 +56,9 @@ CASES = {
     "bw_one_expert": BASE.scaled(T=200, d=64, E=1, k=1, d_ff=64),
     # capacity 0: every assignment dropped, every gradient zero
     "bw_all_dropped": BASE.scaled(T=256, d=64, E=4, k=2, d_ff=128, cap_num=0, cap_den=1),
+    # the widest routing: 256 experts, 8 choices per token, ragged token count
+    "bw_e256_k8": BASE.scaled(T=130, d=64, E=256, k=8, d_ff=64, temperature=0.5,
+                              renormalize=True, cap_num=3, cap_den=2),
 }
 
 
@@ -99,6 +102,22 @@ def test_backward_small(name):
     torch.cuda.synchronize()
     for n in GRADS:
         assert torch.equal(g[n], g2[n]), f"{n} differs between two calls"
+
+
+def test_backward_optional_outputs_left_out():
+    # dgate and dbias may be NULL; the other gradients are the same bits
+    cfg = CASES["bw_renorm_drops"].scaled(name="bw_optional")
+    dev, _ = gpu_inputs(cfg, seed=4)
+    dy = synthetic.make_dy(cfg, seed=4, device="cuda")
+    args = (dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"], dy)
+    say("[bw_optional] moe_backward with and without dgate / dbias")
+    bw = moe.Backward(cfg)
+    full = bw(*args)
+    part = bw(*args, want_dgate=False, want_dbias=False)
+    torch.cuda.synchronize()
+    assert part["dgate"] is None and part["dbias"] is None
+    for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(full[n], part[n]), n
 
 
 def test_backward_no_tokens_zeroes_the_weight_gradients():
