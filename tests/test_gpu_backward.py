@@ -143,7 +143,7 @@ def _sample_tokens(cfg, row_of, rng, n=24):
     return np.unique(pick)
 
 
-@pytest.mark.parametrize("name", ["zaya1", "skewed"])
+@pytest.mark.parametrize("name", ["zaya1", "skewed", "wide", "longseq"])
 def test_backward_full_size_sampled(name):
     cfg = configs.get(name)
     dev, host = gpu_inputs(cfg, seed=0)
