@@ -37,9 +37,7 @@ namespace {
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-constexpr int TK = 32;   // K-step
-
-template <int BM, int BN, int WAVES, int WMW, int NS>
+template <int BM, int BN, int WAVES, int WMW, int NS, int TK>
 struct BwShape {
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int WNW = WAVES / WMW;
@@ -50,19 +48,24 @@ struct BwShape {
     static constexpr int A_WL = A_STAGE / 1024 / WAVES; // 1 KB wave-loads per wave and stage
     static constexpr int B_WL = B_STAGE / 1024 / WAVES;
     static constexpr int LOADS = A_WL + B_WL;
+    static constexpr int KS = TK / 32;                  // MFMA steps per stage
+    static constexpr int CR = TK / 8;                   // 16-byte chunks per K-contiguous row
+    static_assert(TK == 32 || TK == 64, "K-step");
     static_assert(A_WL >= 1 && B_WL >= 1 && A_WL * WAVES * 1024 == A_STAGE &&
                   B_WL * WAVES * 1024 == B_STAGE, "whole wave-loads per wave");
     static_assert(MI >= 1 && NJ >= 1 && BM % (16 * WMW) == 0 && BN % (16 * WNW) == 0, "waves");
     static_assert(BM == 128 || BM == 256, "K-row stage rows of 256 or 512 bytes");
     static_assert(BN == 128 || BN == 256, "K-row stage rows of 256 or 512 bytes");
-    static_assert(NS >= 3 && NS <= 4, "stages");
+    static_assert(NS >= 2 && NS <= 4, "stages");
     static_assert(NS * (A_STAGE + B_STAGE) + 4096 <= 160 * 1024, "LDS budget");
 };
 
-// K-contiguous stage [rows][32 K]: row r at 64 r bytes, 16-byte slot s of the
+// K-contiguous stage [rows][TK]: row r at 2 TK r bytes, 16-byte slot s of the
 // row holds K chunk s ^ kc_sw(r).  The 16 rows of a fragment read
-// (r = base + 0..15) then hit four distinct slots per bank group.
-__device__ __forceinline__ int kc_sw(int r) { return (r >> 2) & 3; }
+// (r = base + 0..15) then spread over the banks: rows of 64 bytes (TK = 32)
+// take four slots per bank group, rows of 128 bytes eight.
+template <int TK>
+__device__ __forceinline__ int kc_sw(int r) { return TK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
 // K-row stage [32 K rows][columns]: row k at k * (2 columns) bytes, 32-byte
 // pair slot p holds column pair p ^ kr_sw(k) (the pair swizzle of the forward
 // GEMM for rows of 256 or 512 bytes).
@@ -85,10 +88,10 @@ struct BwOperands {
 //   A rows row0.. of A[s], B = W[e] of source s, one K slice.
 // MODE 1 (TN): tiles (e, M-tile, N-tile); reduction over the rows off[e] ..
 //   off[e+1]-1 of A [rows][M] and B [rows][N].
-template <int MODE, int BM, int BN, int WAVES, int WMW, int NS>
+template <int MODE, int BM, int BN, int WAVES, int WMW, int NS, int TK>
 __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     const BwOperands ops, const int32_t* __restrict__ off, int E, int M, int N, int K) {
-    using S = BwShape<BM, BN, WAVES, WMW, NS>;
+    using S = BwShape<BM, BN, WAVES, WMW, NS, TK>;
     constexpr bool KROW = MODE == 1;
     constexpr int MI = S::MI, NJ = S::NJ;
     __shared__ __attribute__((aligned(1024))) char sa0[S::A_STAGE];
@@ -160,9 +163,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
         for (int q = 0; q < S::LOADS; ++q) {
             const bool is_a = q < S::A_WL;
             const int blk = is_a ? w * S::A_WL + q : w * S::B_WL + (q - S::A_WL);
-            if (!KROW) {   // [rows][32 K]: rows 16 blk .. + 15, four slots each
-                const int r = blk * 16 + lane / 4;
-                const int c = (lane % 4) ^ kc_sw(r);
+            if (!KROW) {   // [rows][TK]: 64 / CR rows per block, CR slots each
+                const int r = blk * (64 / S::CR) + lane / S::CR;
+                const int c = (lane % S::CR) ^ kc_sw<TK>(r);
                 const int src = is_a ? min(r, rows - 1) : min(r, N - 1 - n0);
                 l_off[q] = ((uint32_t)src * (uint32_t)K + c * 8) * 2u;
             } else {       // [32 K rows][columns]: (1024 / row bytes) rows per block
@@ -210,16 +213,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
         };
 
         // per-lane fragment read offsets (lane constants)
-        const int kc_rd = c16 * 64 + ((g4 ^ kc_sw(c16)) << 4);
+        const int kc_rd = c16 * (2 * TK);
+        const int kc_s = kc_sw<TK>(c16);
         const int kr_row = g4 * 8 + (c16 >> 2);
         const int kr_h = kr_sw(kr_row);
         const int kr_in = ((c16 >> 1) & 1) * 16 + (c16 & 1) * 8;
-        // 16 rows (K contiguous) or 16 columns (K rows of rb bytes) from index b
-        auto frag = [&](const char* st, int b, int rb) -> bf16x8 {
+        // 16 rows (K contiguous) or 16 columns (K rows of rb bytes) from index
+        // b, K values 32 ks .. + 31 of the stage
+        auto frag = [&](const char* st, int b, int rb, int ks) -> bf16x8 {
             if (!KROW) {
-                return *(const bf16x8*)(st + b * 64 + kc_rd);
+                return *(const bf16x8*)(st + b * (2 * TK) + kc_rd + (((ks * 4 + g4) ^ kc_s) << 4));
             } else {
-                const char* p = st + kr_row * rb + kr_in + (((b >> 4) ^ kr_h) << 5);
+                const char* p = st + (ks * 32 + kr_row) * rb + kr_in + (((b >> 4) ^ kr_h) << 5);
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
                 const s16x4 hi =
                     __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * rb));
@@ -262,16 +267,19 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
                           lds_base(bbuf[(s + NS - 1) % NS]));
                 const char* sa = abuf[s];
                 const char* sb = bbuf[s];
-                bf16x8 fb[NJ];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) fb[j] = frag(sb, (wn * NJ + j) * 16, BN * 2);
+                for (int ks = 0; ks < S::KS; ++ks) {
+                    bf16x8 fb[NJ];
 #pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const bf16x8 fa = frag(sa, (wm * MI + i) * 16, BM * 2);
+                    for (int j = 0; j < NJ; ++j) fb[j] = frag(sb, (wn * NJ + j) * 16, BN * 2, ks);
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa, acc[i][j],
-                                                                            0, 0, 0);
+                    for (int i = 0; i < MI; ++i) {
+                        const bf16x8 fa = frag(sa, (wm * MI + i) * 16, BM * 2, ks);
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa,
+                                                                                acc[i][j], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -304,31 +312,37 @@ unsigned grid_of(long long tiles, int cap) {
     return (unsigned)std::max<long long>(8, g / 8 * 8);
 }
 
-template <int BM, int BN, int WAVES, int WMW, int NS>
+template <int BM, int BN, int WAVES, int WMW, int NS, int TK>
 hipError_t launch_nt(const BwOperands& ops, const int32_t* off, int E, int N, int K,
                      long long max_rows, int cap, hipStream_t s) {
     const long long tiles =
         ((max_rows + BM - 1) / BM + E) * ((N + BN - 1) / BN) * ops.nsrc * ops.ksplit;
-    hipLaunchKernelGGL((gemm_bw_kernel<0, BM, BN, WAVES, WMW, NS>), dim3(grid_of(tiles, cap)),
+    hipLaunchKernelGGL((gemm_bw_kernel<0, BM, BN, WAVES, WMW, NS, TK>), dim3(grid_of(tiles, cap)),
                        dim3(64 * WAVES), 0, s, ops, off, E, 0, N, K);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WAVES, int WMW, int NS>
+template <int BM, int BN, int WAVES, int WMW, int NS, int TK>
 hipError_t launch_tn(const BwOperands& ops, const int32_t* off, int E, int M, int N, int cap,
                      hipStream_t s) {
     const long long tiles = (long long)E * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_bw_kernel<1, BM, BN, WAVES, WMW, NS>), dim3(grid_of(tiles, cap)),
+    hipLaunchKernelGGL((gemm_bw_kernel<1, BM, BN, WAVES, WMW, NS, TK>), dim3(grid_of(tiles, cap)),
                        dim3(64 * WAVES), 0, s, ops, off, E, M, N, 0);
     return hipGetLastError();
 }
 
 constexpr int BW_BM = 256;   // NT rows per tile
+// K-step and ring depth: the NT products read their weight operand in 128-byte
+// row pieces (64 K values) through a two-stage ring; the TN products, whose K
+// runs over an expert's ragged rows, keep 32-deep steps and three stages
+// (64-deep steps measured 2-3 % faster for NT, slower for TN)
+constexpr int BW_NT_TK = 64, BW_NT_NS = 2;
+constexpr int BW_TN_TK = 32, BW_TN_NS = 3;
 
 }  // namespace
 
-// One shape for both: 256 x 256 tiles, 8 waves as 2 (M) x 4 (N), three
-// stages (one workgroup per CU; cus counts two per CU).  Measured on the
+// One tile shape for both: 256 x 256 tiles, 8 waves as 2 (M) x 4 (N) (one
+// workgroup per CU; cus counts two per CU); K-step and stages as above.  Measured on the
 // four large layers against 128 x 128 tiles with 4 waves (two workgroups per
 // CU) and 256 x 128: 256 x 256 is the fastest on every one (the backward of
 // the ZAYA1-like layer 2.38 ms against 2.95 and 2.72); a 4 x 2 wave layout and
@@ -337,7 +351,8 @@ int bw_nt_ksplit(long long max_rows, int E, int N, int K, int nsrc, int cus) {
     const long long tiles = ((max_rows + BW_BM - 1) / BW_BM + E) * ((N + 255) / 256) * nsrc;
     const long long want = 3LL * (cus / 2);   // three sweeps of one workgroup per CU
     int ks = 1;
-    while (ks < 4 && tiles * ks < want && (K / (2 * ks)) % TK == 0 && K % (2 * ks) == 0) ks *= 2;
+    while (ks < 4 && tiles * ks < want && (K / (2 * ks)) % BW_NT_TK == 0 && K % (2 * ks) == 0)
+        ks *= 2;
     return ks;
 }
 
@@ -346,10 +361,10 @@ hipError_t launch_bw_nt(const uint16_t* A0, const uint16_t* W0, const uint16_t* 
                         const int32_t* off, int E, int N, int K, long long max_rows, int cus,
                         hipStream_t s) {
     if (max_rows == 0) return hipSuccess;
-    if (N % 8 != 0 || N < 8 || ksplit < 1 || K % ksplit != 0 || (K / ksplit) % TK != 0)
+    if (N % 8 != 0 || N < 8 || ksplit < 1 || K % ksplit != 0 || (K / ksplit) % BW_NT_TK != 0)
         return hipErrorInvalidValue;
     BwOperands ops{{A0, A1}, {W0, W1}, C, part_stride, A1 ? 2 : 1, ksplit};
-    return launch_nt<BW_BM, 256, 8, 2, 3>(ops, off, E, N, K, max_rows, cus / 2, s);
+    return launch_nt<BW_BM, 256, 8, 2, BW_NT_NS, BW_NT_TK>(ops, off, E, N, K, max_rows, cus / 2, s);
 }
 
 hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off,
@@ -357,7 +372,7 @@ hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const in
     if (E == 0) return hipSuccess;
     if (M % 8 != 0 || N % 8 != 0 || M < 8 || N < 8) return hipErrorInvalidValue;
     BwOperands ops{{A, nullptr}, {B, nullptr}, C, 0, 1, 1};
-    return launch_tn<256, 256, 8, 2, 3>(ops, off, E, M, N, cus / 2, s);
+    return launch_tn<256, 256, 8, 2, BW_TN_NS, BW_TN_TK>(ops, off, E, M, N, cus / 2, s);
 }
 
 }  // namespace moe
