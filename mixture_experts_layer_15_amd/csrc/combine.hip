@@ -12,7 +12,10 @@
 namespace moe {
 namespace {
 
-template <typename T>
+// KMAX >= k choices per token; U vectors per lane in flight at once (the
+// loads of all U are issued before any is used: one memory round trip per U
+// vectors of each row).
+template <typename T, int KMAX, int U>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y_perm,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
@@ -22,31 +25,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     const int lane = threadIdx.x & 63;
     const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= ntok) return;
-    int rows[8];
-    float g[8];
+    // row and gate of each choice, loaded together (the gate of a dropped
+    // choice is read but never used)
+    int rows[KMAX];
+    float g[KMAX];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < KMAX; ++j) {
         rows[j] = (j < k) ? row_of[t * k + j] : -1;
-        g[j] = (rows[j] >= 0) ? gate[t * k + j] : 0.f;
+        g[j] = (j < k) ? gate[t * k + j] : 0.f;
     }
     u32x4* dst = y + t * nvec;
-    for (int v0 = lane; v0 < nvec; v0 += 2 * 64) {
-        float acc[2][PV];
-        u32x4 in[2][8];
+    for (int v0 = lane; v0 < nvec; v0 += U * 64) {
+        float acc[U][PV];
+        u32x4 in[U][KMAX];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int i = 0; i < PV; ++i) acc[u][i] = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < KMAX; ++j)
                 if (rows[j] >= 0 && v0 + u * 64 < nvec)
                     in[u][j] = y_perm[(long long)rows[j] * nvec + v0 + u * 64];
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < U; ++u) {
             if (v0 + u * 64 >= nvec) continue;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < KMAX; ++j) {
                 if (rows[j] < 0) continue;
 #pragma unroll
                 for (int i = 0; i < PV; ++i)
@@ -73,11 +78,15 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
     if (T == 0) return hipSuccess;
     const dim3 grid((unsigned)((T + 3) / 4));
     if (dtype == 1) {
-        hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, (const u32x4*)y_perm,
-                           row_of, gate, (u32x4*)y, T, d / 8, k);
+        if (k <= 2)
+            hipLaunchKernelGGL((combine_kernel<uint16_t, 2, 4>), grid, dim3(256), 0, s,
+                               (const u32x4*)y_perm, row_of, gate, (u32x4*)y, T, d / 8, k);
+        else
+            hipLaunchKernelGGL((combine_kernel<uint16_t, 8, 2>), grid, dim3(256), 0, s,
+                               (const u32x4*)y_perm, row_of, gate, (u32x4*)y, T, d / 8, k);
     } else {
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, (const u32x4*)y_perm,
-                           row_of, gate, (u32x4*)y, T, d / 4, k);
+        hipLaunchKernelGGL((combine_kernel<float, 8, 2>), grid, dim3(256), 0, s,
+                           (const u32x4*)y_perm, row_of, gate, (u32x4*)y, T, d / 4, k);
     }
     return hipGetLastError();
 }
