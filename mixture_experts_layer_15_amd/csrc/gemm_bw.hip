@@ -111,8 +111,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     const int c16 = lane & 15, g4 = lane >> 4;
     const int G = gridDim.x;   // a multiple of 8
 
-    // persistent grid: sweeps of G tiles, workgroup b taking slot xcd_slot(b, G)
-    // of each sweep (each XCD a contiguous run of tiles)
+    // persistent grid: sweeps of G tiles, workgroup b taking tile
+    // sweep_tile(b, ...) of each sweep (each XCD a contiguous run of tiles)
     long long total;
     int mtn = 1;
     const int ntn = (N + BN - 1) / BN;
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     auto lds_base = [](char* p) { return __builtin_amdgcn_readfirstlane(lds_addr(p)); };
 
     for (long long sweep = 0; sweep < total; sweep += G) {
-        const long long t = sweep + xcd_slot(blockIdx.x, G);
-        if (t >= total) continue;   // uniform across the workgroup
+        const long long t = sweep_tile(blockIdx.x, G, sweep, total);
+        if (t < 0) continue;   // uniform across the workgroup
         int e, row0, rows = BM, m0 = 0, n0, k_len, k_beg = 0, part = 0;
         const uint16_t* A = ops.A[0];
         const uint16_t* B = ops.B[0];

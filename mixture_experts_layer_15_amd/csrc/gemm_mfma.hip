@@ -245,8 +245,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     }
 
     for (long long base = 0; base < total; base += G) {
-        const long long t = base + xcd_slot(blockIdx.x, G);
-        if (t >= total) continue;   // uniform across the workgroup
+        const long long t = sweep_tile(blockIdx.x, G, base, total);
+        if (t < 0) continue;   // uniform across the workgroup
         int e, mtile, ntile;
         decode_tile<GM>(tt, E, ntn, t, e, mtile, ntile);
         const int row0 = (off ? off[e] : 0) + mtile * S::BM;

@@ -120,7 +120,10 @@ moe_status check_ptr(const void* p, const char* name, size_t bytes, bool optiona
         if (_s != MOE_OK) return _s;         \
     } while (0)
 
-// Persistent-grid size of the grouped GEMM: two workgroups per CU.
+// Persistent-grid cap of the grouped GEMMs: twice the CU count.  The fp32
+// GEMMs (256-thread workgroups, two resident per CU) launch up to this many;
+// the bf16 MFMA GEMMs, whose LDS stages hold one workgroup per CU, launch
+// half (one per CU).
 int gemm_grid_cap() {
     static std::atomic<int> cached[64];
     int dev = 0;

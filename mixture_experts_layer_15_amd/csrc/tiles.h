@@ -5,9 +5,9 @@
 // the M-tiles that share one weight tile are adjacent, and consecutive
 // N-tiles of one expert reuse that expert's rows.  A persistent grid walks
 // the list in sweeps of gridDim.x tiles; within a sweep workgroup b takes
-// slot xcd_slot(b), which hands each XCD (workgroups b, b+8, ... run on XCD
-// b % 8) a contiguous run of tile ids, so tiles that share data meet in the
-// same L2.
+// tile sweep_tile(b, ...), which hands each XCD (workgroups b, b+8, ... run
+// on XCD b % 8) a contiguous run of tile ids, so tiles that share data meet
+// in the same L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -77,9 +77,19 @@ __device__ __forceinline__ void decode_tile(const TileTable& tt, int E, int ntn,
     m = g * GM + r % gs;
 }
 
-// Slot of workgroup b in a sweep of G (G a multiple of 8).
-__device__ __forceinline__ long long xcd_slot(int b, int G) {
-    return (long long)(b & 7) * (G >> 3) + (b >> 3);
+// Tile of workgroup b in the sweep that starts at tile `base`, or -1.  The
+// sweep holds n = min(G, total - base) tiles (G a multiple of 8, the grid),
+// cut into 8 contiguous runs of ceil(n / 8); run x goes to XCD x, tile i of
+// the run to the XCD's i-th workgroup (b = 8 i + x).  Sizing the runs by n
+// rather than by G matters when a sweep is not full: the grid is sized on the
+// host from an upper bound on the tiles, and runs of G / 8 would put the
+// whole of a short sweep on the first few XCDs, leaving the others idle.
+__device__ __forceinline__ long long sweep_tile(int b, int G, long long base, long long total) {
+    const long long n = min((long long)G, total - base);
+    const long long per = (n + 7) >> 3;
+    const long long i = b >> 3;
+    const long long t = base + (long long)(b & 7) * per + i;
+    return (i < per && t < base + n) ? t : -1;
 }
 
 }  // namespace moe
