@@ -14,8 +14,9 @@ namespace {
 
 // KMAX >= k choices per token; U vectors per lane in flight at once (the
 // loads of all U are issued before any is used: one memory round trip per U
-// vectors of each row).
-template <typename T, int KMAX, int U>
+// vectors of each row).  NT: non-temporal loads and stores, for layers whose
+// data are several times the 256 MB last-level cache.
+template <typename T, int KMAX, int U, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y_perm,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate,
@@ -45,7 +46,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 #pragma unroll
             for (int j = 0; j < KMAX; ++j)
                 if (rows[j] >= 0 && v0 + u * 64 < nvec)
-                    in[u][j] = y_perm[(long long)rows[j] * nvec + v0 + u * 64];
+                    in[u][j] = NT ? __builtin_nontemporal_load(y_perm + (long long)rows[j] * nvec +
+                                                               v0 + u * 64)
+                                  : y_perm[(long long)rows[j] * nvec + v0 + u * 64];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -65,7 +68,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 #pragma unroll
                 for (int p = 0; p < 4; ++p) out[p] = __float_as_uint(acc[u][p]);
             }
-            dst[v0 + u * 64] = out;
+            if (NT) __builtin_nontemporal_store(out, dst + v0 + u * 64);
+            else dst[v0 + u * 64] = out;
         }
     }
 }
@@ -77,15 +81,25 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
                           hipStream_t s) {
     if (T == 0) return hipSuccess;
     const dim3 grid((unsigned)((T + 3) / 4));
+    // Stream past the caches only when the output alone is at least twice
+    // the 256 MB last-level cache: smaller layers still find the down GEMM's
+    // y_perm there, and non-temporal loads then measured 3-12% slower (wide
+    // and skewed layers) against 7% faster on the long-sequence layer.
+    const bool nt = (double)T * d * (dtype == 1 ? 2 : 4) >= 512.0 * (1 << 20);
     if (dtype == 1) {
-        if (k <= 2)
-            hipLaunchKernelGGL((combine_kernel<uint16_t, 2, 4>), grid, dim3(256), 0, s,
+        if (k <= 2) {
+            if (nt)
+                hipLaunchKernelGGL((combine_kernel<uint16_t, 2, 4, true>), grid, dim3(256), 0, s,
+                                   (const u32x4*)y_perm, row_of, gate, (u32x4*)y, T, d / 8, k);
+            else
+                hipLaunchKernelGGL((combine_kernel<uint16_t, 2, 4, false>), grid, dim3(256), 0, s,
+                                   (const u32x4*)y_perm, row_of, gate, (u32x4*)y, T, d / 8, k);
+        } else {
+            hipLaunchKernelGGL((combine_kernel<uint16_t, 8, 2, false>), grid, dim3(256), 0, s,
                                (const u32x4*)y_perm, row_of, gate, (u32x4*)y, T, d / 8, k);
-        else
-            hipLaunchKernelGGL((combine_kernel<uint16_t, 8, 2>), grid, dim3(256), 0, s,
-                               (const u32x4*)y_perm, row_of, gate, (u32x4*)y, T, d / 8, k);
+        }
     } else {
-        hipLaunchKernelGGL((combine_kernel<float, 8, 2>), grid, dim3(256), 0, s,
+        hipLaunchKernelGGL((combine_kernel<float, 8, 2, false>), grid, dim3(256), 0, s,
                            (const u32x4*)y_perm, row_of, gate, (u32x4*)y, T, d / 4, k);
     }
     return hipGetLastError();

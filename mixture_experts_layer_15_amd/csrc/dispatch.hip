@@ -18,7 +18,9 @@
 //           bits), plus the counts of earlier waves and chunks -> row_of,
 //           token_of_row
 //   scatter one wave per token: the x row is read once and written to each
-//           of its kept rows with 16-byte vector stores (HBM-bound)
+//           of its kept rows with 16-byte vector stores (HBM-bound; both
+//           sides non-temporal: every byte is touched once, and streaming
+//           past the caches measured 2-9% faster on the four bf16 layers)
 #include "common.h"
 #include "kernels.h"
 
@@ -275,14 +277,14 @@ __global__ __launch_bounds__(256) void scatter_kernel(const u32x4* __restrict__ 
         u32x4 val[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if (v0 + u * 64 < nvec) val[u] = src[v0 + u * 64];
+            if (v0 + u * 64 < nvec) val[u] = __builtin_nontemporal_load(src + v0 + u * 64);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if (rows[j] < 0) continue;
             u32x4* dst = x_perm + (long long)rows[j] * nvec;
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                if (v0 + u * 64 < nvec) dst[v0 + u * 64] = val[u];
+                if (v0 + u * 64 < nvec) __builtin_nontemporal_store(val[u], dst + v0 + u * 64);
         }
     }
 }
