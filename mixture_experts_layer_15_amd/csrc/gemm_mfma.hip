@@ -189,7 +189,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, uint16_t* __restrict__ C2,
     const int32_t* __restrict__ off, const int32_t* __restrict__ a_rows, int E, int K, int N,
-    int dense_rows, const float* __restrict__ bias, int act) {
+    int dense_rows, const float* __restrict__ bias, int act, int rlo, int rhi) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB, WM>;
     // one distinct __shared__ array per stage buffer, so that the compiler can
     // tell the reads of one stage from the fills of the others
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     __shared__ long long s_wave[S::WAVES];
 
     const int ntn = (N + S::OUTC - 1) / S::OUTC;
-    build_tile_table<S::BM>(off, E, ntn, tt, s_wave, dense_rows);
+    build_tile_table<S::BM>(off, E, ntn, tt, s_wave, dense_rows, rlo, rhi);
     const long long total = tt.start[E];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -425,7 +425,8 @@ template <bool GATEUP, int MI, int NJ, int BKT, int NA, int NB, int WM = 2>
 hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                         const int32_t* off, const int32_t* a_rows, int dense_rows,
                         const float* bias, int act, int E, int K, int N, long long max_rows, int cus,
-                        hipStream_t s, uint16_t* C2 = nullptr) {
+                        hipStream_t s, uint16_t* C2 = nullptr, int rlo = 0,
+                        int rhi = 0x7fffffff) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB, WM>;
     const long long mt = (max_rows + S::BM - 1) / S::BM + E;   // >= sum_e ceil(rows_e / BM)
     const long long tiles = mt * ((N + S::OUTC - 1) / S::OUTC);
@@ -433,7 +434,7 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
     g = std::max<long long>(8, g / 8 * 8);
     hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NA, NB, WM>), dim3((unsigned)g),
                        dim3(S::THREADS), 0, s, A, B0, B1, C, C2, off, a_rows, E, K, N,
-                       dense_rows, bias, act);
+                       dense_rows, bias, act, rlo, rhi);
     return hipGetLastError();
 }
 
@@ -450,6 +451,17 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
 // faster); for the 320 x 256 gate/up tile the two layouts measure the same.
 static bool small_experts(long long max_rows, int E) { return max_rows <= 320LL * E; }
 
+// Layers on 256 x 256 tiles can still hold experts with only a few rows (the
+// skewed layer: 45 of 64 experts under 64 rows).  Those experts go to a second
+// launch of 128 x 256 tiles with 32-deep K-steps and four stages per operand
+// (more weight bytes in flight per CU for tiles that are all weight
+// streaming); each launch skips the other's experts.  The per-row arithmetic
+// is the same in both shapes (K ascending in steps of 32), so the result is
+// bit-identical to one launch.  Measured on the skewed layer: down 442 -> 399
+// us, gate/up 761 -> 740 us; no change on the long-sequence layer, whose
+// second launch finds no tiles.
+constexpr int kFewRows = 64;
+
 hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const int32_t* off,
                                const uint16_t* w_gate,
                                const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
@@ -457,8 +469,12 @@ hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const i
     if (small_experts(max_rows, E))
         return launch_shape<true, 10, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0, E, d, d_ff,
                                                 max_rows, cus, s);
-    return launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0, E, d, d_ff, max_rows,
-                                           cus, s);
+    const hipError_t e = launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0,
+                                                            nullptr, 0, E, d, d_ff, max_rows, cus,
+                                                            s, nullptr, kFewRows);
+    if (e != hipSuccess) return e;
+    return launch_shape<true, 4, 4, 32, 4, 4>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0, E,
+                                              d, d_ff, max_rows, cus, s, nullptr, 0, kFewRows);
 }
 
 // Both products of the gate/up GEMM, unfused: g = X W_gate, u = X W_up (bf16),
@@ -470,8 +486,12 @@ hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, con
     if (small_experts(max_rows, E))
         return launch_shape<true, 10, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2,
                                                    E, d, d_ff, max_rows, cus, s, u);
-    return launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2, E,
-                                              d, d_ff, max_rows, cus, s, u);
+    const hipError_t e = launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0,
+                                                            nullptr, 2, E, d, d_ff, max_rows, cus,
+                                                            s, u, kFewRows);
+    if (e != hipSuccess) return e;
+    return launch_shape<true, 4, 4, 32, 4, 4>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2, E,
+                                              d, d_ff, max_rows, cus, s, u, 0, kFewRows);
 }
 
 hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const int32_t* off,
@@ -480,8 +500,12 @@ hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const i
     if (small_experts(max_rows, E))
         return launch_shape<false, 5, 4, 64, 2, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0,
                                                       E, K, N, max_rows, cus, s);
-    return launch_shape<false, 8, 4, 64, 2, 2>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E, K,
-                                               N, max_rows, cus, s);
+    const hipError_t e = launch_shape<false, 8, 4, 64, 2, 2>(A, B, nullptr, C, off, a_rows, 0,
+                                                             nullptr, 0, E, K, N, max_rows, cus, s,
+                                                             nullptr, kFewRows);
+    if (e != hipSuccess) return e;
+    return launch_shape<false, 4, 4, 32, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E, K,
+                                               N, max_rows, cus, s, nullptr, 0, kFewRows);
 }
 
 hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_t* w_down,

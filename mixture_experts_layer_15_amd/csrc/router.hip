@@ -375,13 +375,12 @@ hipError_t route_ks(const uint16_t* x, const uint16_t* w, const float* bias, flo
                     int32_t* idx, float* gate, long long T, int d, int E, int k, float tau,
                     int renorm, hipStream_t s) {
     // E > 64: W_r chunks take 64 registers per K-step in flight, so two steps
-    // and at most two token tiles per wave
-    constexpr int MT4 = NT <= 4 ? 4 : 2, D4 = 2;
+    // in flight.  At most two token tiles per wave: four (fewer re-reads of
+    // W_r per token) need more than 256 registers, which leaves one wave per
+    // SIMD, and measured slower on the skewed (E = 64: 69.5 against 55.7 us)
+    // and long-sequence (E = 8: 165 against 151 us) layers.
     constexpr int D2 = NT <= 4 ? 3 : 2, D1 = NT <= 4 ? 4 : 2;
-    if (T >= 16LL * MT4 * 512)
-        hipLaunchKernelGGL((router_ks_kernel<NT, MT4, D4>), dim3((unsigned)((T + 16 * MT4 - 1) / (16 * MT4))),
-                           dim3(256), 0, s, x, w, bias, logits, idx, gate, T, d, E, k, tau, renorm);
-    else if (T >= 16LL * 2 * 512)
+    if (T >= 16LL * 2 * 512)
         hipLaunchKernelGGL((router_ks_kernel<NT, 2, D2>), dim3((unsigned)((T + 31) / 32)), dim3(256),
                            0, s, x, w, bias, logits, idx, gate, T, d, E, k, tau, renorm);
     else

@@ -23,17 +23,20 @@ struct TileTable {
 // Every thread of the block (a multiple of 64, at least 256) calls this; the
 // first 256 own one expert each.  ntn = N-tiles per expert.  s_wave holds one
 // entry per wave.  Without an offset table (off == nullptr, E == 1) the single
-// group has dense_rows rows.
+// group has dense_rows rows.  Experts whose row count lies outside
+// [rlo, rhi) get no tiles (they are left to another launch).
 template <int TBM>
 __device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ off, int E, int ntn,
                                                  TileTable& tt, long long* s_wave,
-                                                 int dense_rows = 0) {
+                                                 int dense_rows = 0, int rlo = 0,
+                                                 int rhi = 0x7fffffff) {
     const int e = threadIdx.x;
     long long cnt = 0;
     int mt = 0;
     if (e < E) {
         // off == nullptr: one group (E == 1) of dense_rows rows
-        const int kept = off ? off[e + 1] - off[e] : dense_rows;
+        int kept = off ? off[e + 1] - off[e] : dense_rows;
+        if (kept < rlo || kept >= rhi) kept = 0;
         mt = (kept + TBM - 1) / TBM;
         cnt = (long long)mt * ntn;
     }
