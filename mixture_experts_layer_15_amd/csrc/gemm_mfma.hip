@@ -445,7 +445,11 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
 // whose experts hold up to ~320 rows (weight-streaming bound: every weight
 // byte is used by that few rows) take 320-row tiles so that one M-tile covers
 // an expert and each weight tile is streamed once; larger experts take
-// 256 x 256 tiles (the most flops per byte moved into a CU).  The down GEMM's
+// 256 x 256 tiles (the most flops per byte moved into a CU).  The 320 x 256
+// gate/up tile runs 32-deep K-steps in a ring of four stages per operand
+// (three in flight while one is multiplied): 321 against 334 us with 64-deep
+// steps in two stages on the ZAYA1-like layer, the same on the wide layer;
+// the down GEMM's 320 x 128 tile measured 34% slower that way.  The down GEMM's
 // 320 x 128 tile arranges its waves 4 (M) x 2 (N): 80 x 64 per wave instead of
 // 160 x 32 reads 27% fewer fragment bytes from LDS per stage (measured 4%
 // faster); for the 320 x 256 gate/up tile the two layouts measure the same.
@@ -467,8 +471,8 @@ hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const i
                                const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
                                long long max_rows, int cus, hipStream_t s) {
     if (small_experts(max_rows, E))
-        return launch_shape<true, 10, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0, E, d, d_ff,
-                                                max_rows, cus, s);
+        return launch_shape<true, 10, 4, 32, 4, 4>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0,
+                                                   E, d, d_ff, max_rows, cus, s);
     const hipError_t e = launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0,
                                                             nullptr, 0, E, d, d_ff, max_rows, cus,
                                                             s, nullptr, kFewRows);
@@ -484,7 +488,7 @@ hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, con
                                    uint16_t* u, int E, int d, int d_ff, long long max_rows,
                                    int cus, hipStream_t s) {
     if (small_experts(max_rows, E))
-        return launch_shape<true, 10, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2,
+        return launch_shape<true, 10, 4, 32, 4, 4>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2,
                                                    E, d, d_ff, max_rows, cus, s, u);
     const hipError_t e = launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0,
                                                             nullptr, 2, E, d, d_ff, max_rows, cus,
