@@ -103,11 +103,13 @@ hipError_t launch_gate_up(int dtype, const void* x_perm, const int32_t* off, con
 
 hipError_t launch_down(int dtype, const void* h, const int32_t* off, const void* w_down,
                        void* y_perm, int E, int d, int d_ff, long long max_rows, int grid_cap,
-                       hipStream_t s) {
+                       hipStream_t s, const float* gate, const int32_t* token_of_row, void* y) {
     if (max_rows == 0) return hipSuccess;
+    if (y != nullptr && dtype != 1) return hipErrorInvalidValue;   // bf16 only
     if (dtype == 1)
         return launch_mfma_down((const uint16_t*)h, off, (const uint16_t*)w_down,
-                                (uint16_t*)y_perm, E, d, d_ff, max_rows, grid_cap / 2, s);
+                                (uint16_t*)y_perm, E, d, d_ff, max_rows, grid_cap / 2, s, gate,
+                                token_of_row, (uint16_t*)y);
     {
         const long long mt = (max_rows + FBM - 1) / FBM + E;
         hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3(grid_for(mt * ((d + FBN - 1) / FBN), grid_cap)),

@@ -189,7 +189,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, uint16_t* __restrict__ C2,
     const int32_t* __restrict__ off, const int32_t* __restrict__ a_rows, int E, int K, int N,
-    int dense_rows, const float* __restrict__ bias, int act, int rlo, int rhi) {
+    int dense_rows, const float* __restrict__ bias, int act, int rlo, int rhi,
+    const float* __restrict__ gate, const int32_t* __restrict__ tor, uint16_t* __restrict__ Y) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB, WM>;
     // one distinct __shared__ array per stage buffer, so that the compiler can
     // tell the reads of one stage from the fills of the others
@@ -366,6 +367,11 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         // store per block.  Plain GEMMs may add a per-column fp32 bias and
         // apply GELU (act == 1).  gate/up with act == 2 stores the two
         // products themselves (x W_gate to C, x W_up to C2) instead of GeGLU.
+        // The down GEMM with Y != nullptr (a top-1 layer that keeps every
+        // token) writes the layer output itself: row r of expert order is
+        // token t = tor[r], and y[t] = gate[t] * O[r], with O rounded to bf16
+        // first and the product rounded like the combine rounds it, so the
+        // result is bit-identical to writing O and combining.
         float bv[S::OUTW / 16][4];
 #pragma unroll
         for (int jj = 0; jj < S::OUTW / 16; ++jj)
@@ -379,6 +385,12 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
             const int r = wm * MI * 16 + i * 16 + c16;
             if (i < nvm && r < rows) {
                 uint16_t* crow = C + (long long)(row0 + r) * N + n0;
+                float gr = 0.f;
+                if (!GATEUP && Y != nullptr) {
+                    const int t = tor[row0 + r];
+                    crow = Y + (long long)t * N + n0;
+                    gr = gate[t];
+                }
 #pragma unroll
                 for (int jj = 0; jj < S::OUTW / 16; ++jj) {
                     const int col = wn * S::OUTW + jj * 16 + g4 * 4;
@@ -408,6 +420,9 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
                             if (act == 1) o = gelu_erf_bf16(o);
                         }
                         v[q] = (__bf16)o;
+                        if (!GATEUP && Y != nullptr)
+                            v[q] = __builtin_bit_cast(
+                                __bf16, (uint16_t)f32_to_bf16_bits(fmaf(gr, (float)v[q], 0.f)));
                     }
                     if (n0 + col < N) *(u32x2*)(crow + col) = __builtin_bit_cast(u32x2, v);
                 }
@@ -426,7 +441,8 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
                         const int32_t* off, const int32_t* a_rows, int dense_rows,
                         const float* bias, int act, int E, int K, int N, long long max_rows, int cus,
                         hipStream_t s, uint16_t* C2 = nullptr, int rlo = 0,
-                        int rhi = 0x7fffffff) {
+                        int rhi = 0x7fffffff, const float* gate = nullptr,
+                        const int32_t* tor = nullptr, uint16_t* Y = nullptr) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB, WM>;
     const long long mt = (max_rows + S::BM - 1) / S::BM + E;   // >= sum_e ceil(rows_e / BM)
     const long long tiles = mt * ((N + S::OUTC - 1) / S::OUTC);
@@ -434,7 +450,7 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
     g = std::max<long long>(8, g / 8 * 8);
     hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NA, NB, WM>), dim3((unsigned)g),
                        dim3(S::THREADS), 0, s, A, B0, B1, C, C2, off, a_rows, E, K, N,
-                       dense_rows, bias, act, rlo, rhi);
+                       dense_rows, bias, act, rlo, rhi, gate, tor, Y);
     return hipGetLastError();
 }
 
@@ -500,22 +516,28 @@ hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, con
 
 hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const int32_t* off,
                                const uint16_t* B, uint16_t* C, int E, int K, int N,
-                               long long max_rows, int cus, hipStream_t s) {
+                               long long max_rows, int cus, hipStream_t s, const float* gate,
+                               const int32_t* tor, uint16_t* y) {
     if (small_experts(max_rows, E))
         return launch_shape<false, 5, 4, 64, 2, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0,
-                                                      E, K, N, max_rows, cus, s);
+                                                      E, K, N, max_rows, cus, s, nullptr, 0,
+                                                      0x7fffffff, gate, tor, y);
     const hipError_t e = launch_shape<false, 8, 4, 64, 2, 2>(A, B, nullptr, C, off, a_rows, 0,
                                                              nullptr, 0, E, K, N, max_rows, cus, s,
-                                                             nullptr, kFewRows);
+                                                             nullptr, kFewRows, 0x7fffffff, gate,
+                                                             tor, y);
     if (e != hipSuccess) return e;
     return launch_shape<false, 4, 4, 32, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E, K,
-                                               N, max_rows, cus, s, nullptr, 0, kFewRows);
+                                               N, max_rows, cus, s, nullptr, 0, kFewRows, gate,
+                                               tor, y);
 }
 
 hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_t* w_down,
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
-                            int cus, hipStream_t s) {
-    return launch_mfma_grouped(h, nullptr, off, w_down, y_perm, E, d_ff, d, max_rows, cus, s);
+                            int cus, hipStream_t s, const float* gate, const int32_t* tor,
+                            uint16_t* y) {
+    return launch_mfma_grouped(h, nullptr, off, w_down, y_perm, E, d_ff, d, max_rows, cus, s,
+                               gate, tor, y);
 }
 
 // Dense bf16 GEMM C [M][N] = A [M][K] B [K][N] (+ bias[N]) (GELU when act ==

@@ -63,9 +63,13 @@ hipError_t launch_expert_ffn(int dtype, const void* x_perm, const int32_t* off,
 hipError_t launch_gate_up(int dtype, const void* x_perm, const int32_t* off, const void* w_gate,
                           const void* w_up, void* h, int E, int d, int d_ff, long long max_rows,
                           int grid_cap, hipStream_t s, const int32_t* gather_rows = nullptr);
+// With y != nullptr (bf16, top-1, every token kept) the down GEMM writes the
+// layer output y[token_of_row[r]] = gate * O[r] itself instead of y_perm,
+// bit-identical to launch_combine over y_perm.
 hipError_t launch_down(int dtype, const void* h, const int32_t* off, const void* w_down,
                        void* y_perm, int E, int d, int d_ff, long long max_rows, int grid_cap,
-                       hipStream_t s);
+                       hipStream_t s, const float* gate = nullptr,
+                       const int32_t* token_of_row = nullptr, void* y = nullptr);
 
 // bf16 MFMA kernels (gemm_mfma.hip); cus = workgroups of the persistent grid.
 // gate/up reads its rows from a: x_perm (a_rows == nullptr), or x gathered
@@ -76,7 +80,8 @@ hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const i
                                long long max_rows, int cus, hipStream_t s);
 hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_t* w_down,
                             uint16_t* y_perm, int E, int d, int d_ff, long long max_rows,
-                            int cus, hipStream_t s);
+                            int cus, hipStream_t s, const float* gate = nullptr,
+                            const int32_t* tor = nullptr, uint16_t* y = nullptr);
 
 // The gate/up GEMM's two products stored separately (bf16): g = X W_gate,
 // u = X W_up (rows of X as in launch_mfma_gate_up).
@@ -89,7 +94,9 @@ hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, con
 // directly (a_rows == nullptr) or gathered through a_rows (gemm_mfma.hip).
 hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const int32_t* off,
                                const uint16_t* B, uint16_t* C, int E, int K, int N,
-                               long long max_rows, int cus, hipStream_t s);
+                               long long max_rows, int cus, hipStream_t s,
+                               const float* gate = nullptr, const int32_t* tor = nullptr,
+                               uint16_t* y = nullptr);
 
 // Dense bf16 GEMM with optional bias and GELU epilogue (gemm_mfma.hip).
 hipError_t launch_mfma_dense(const uint16_t* A, const uint16_t* B, const float* bias, int act,

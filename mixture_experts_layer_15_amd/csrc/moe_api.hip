@@ -443,9 +443,17 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                             w_up, w + L.h, cfg->E, cfg->d, cfg->d_ff, max_rows(cfg),
                             gemm_grid_cap(), s, gather ? tor : nullptr);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/gate_up");
+    // bf16 top-1 layers that keep every token (capacity >= T): each row is one
+    // token's only assignment, so the down GEMM writes y = gate * O itself
+    // (same roundings as the combine, so the same bits) and the combine is
+    // not launched
+    const bool direct = cfg->dtype == MOE_BF16 && cfg->k == 1 &&
+                        cfg->layout == MOE_LAYOUT_COMPACT && capacity_eff(cfg) >= cfg->T;
     e = moe::launch_down(cfg->dtype, w + L.h, offset, w_down, w + L.y_perm, cfg->E, cfg->d,
-                         cfg->d_ff, max_rows(cfg), gemm_grid_cap(), s);
+                         cfg->d_ff, max_rows(cfg), gemm_grid_cap(), s, direct ? gate : nullptr,
+                         direct ? tor : nullptr, direct ? y : nullptr);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/down");
+    if (direct) return MOE_OK;
     e = moe::launch_combine(cfg->dtype, w + L.y_perm, row_of, gate, y, cfg->T, cfg->d, cfg->k, s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
     return MOE_OK;
