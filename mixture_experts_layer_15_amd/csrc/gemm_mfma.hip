@@ -457,44 +457,52 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
 }  // namespace
 
 // Tile shape policy.  Rows per expert are only known on the device; the host
-// knows their mean (max_rows / E, exact when nothing is dropped).  Layers
-// whose experts hold up to ~320 rows (weight-streaming bound: every weight
-// byte is used by that few rows) take 320-row tiles so that one M-tile covers
-// an expert and each weight tile is streamed once; larger experts take
-// 256 x 256 tiles (the most flops per byte moved into a CU).  The down GEMM
-// of small experts takes 320 x 256 tiles too when they fill the CUs, else
-// 320 x 128 (below).  The 320 x 256
-// gate/up tile runs 32-deep K-steps in a ring of four stages per operand
-// (three in flight while one is multiplied): 321 against 334 us with 64-deep
-// steps in two stages on the ZAYA1-like layer, the same on the wide layer;
-// the down GEMM's 320 x 128 tile measured 34% slower that way.  The down GEMM's
-// 320 x 128 tile arranges its waves 4 (M) x 2 (N): 80 x 64 per wave instead of
-// 160 x 32 reads 27% fewer fragment bytes from LDS per stage (measured 4%
-// faster); for the 320 x 256 gate/up tile the two layouts measure the same.
-static bool small_experts(long long max_rows, int E) { return max_rows <= 320LL * E; }
+// knows their mean (max_rows / E, exact when nothing is dropped).  Up to 2048
+// rows per expert on average the GEMMs take 320-row tiles: one M-tile covers a
+// ZAYA1-like or wide-layer expert (about 256 rows: weight-streaming bound, so
+// each weight tile is streamed once), and the skewed layer's capacity-bound
+// experts of 1280 rows take four instead of five 256-row tiles (1.21 -> 1.17
+// ms per step).  Above that, 256 x 256 tiles (long-sequence layer, about 16k
+// rows per expert: 16.5 against 17.4 ms per step on 320-row tiles).
+//   gate/up: 320 x 256, 32-deep K-steps in rings of four stages per operand
+//     (three in flight while one is multiplied): 321 against 334 us with
+//     64-deep steps in two stages on the ZAYA1-like layer, the same on the
+//     wide layer.
+//   down: 320 x 256 likewise when E * ceil(d / 256) tiles fill the CUs (each
+//     CU then moves 36% fewer bytes per output than with 320 x 128: the wide
+//     layer 2.95 -> 2.36 ms), else 320 x 128 with 64-deep K-steps (the
+//     ZAYA1-like layer: 128 tiles of 320 x 256 would leave half the CUs idle,
+//     261 against 214 us; 32-deep four-stage rings measured 34% slower on
+//     this tile).  Its waves are arranged 4 (M) x 2 (N): 80 x 64 per wave
+//     instead of 160 x 32 reads 27% fewer fragment bytes from LDS per stage
+//     (measured 4% faster).
+static bool tiles320(long long max_rows, int E) { return max_rows <= 2048LL * E; }
 
-// Layers on 256 x 256 tiles can still hold experts with only a few rows (the
-// skewed layer: 45 of 64 experts under 64 rows).  Those experts go to a second
-// launch of 128 x 256 tiles with 32-deep K-steps and four stages per operand
-// (more weight bytes in flight per CU for tiles that are all weight
-// streaming); each launch skips the other's experts.  The per-row arithmetic
-// is the same in both shapes (K ascending in steps of 32), so the result is
-// bit-identical to one launch.  Measured on the skewed layer: down 442 -> 399
-// us, gate/up 761 -> 740 us; no change on the long-sequence layer, whose
-// second launch finds no tiles.
+// On 256-row tiles, experts with only a few rows (a skewed layer's tail) go
+// to a second launch of 128 x 256 tiles with 32-deep K-steps and four stages
+// per operand (more weight bytes in flight per CU for tiles that are all
+// weight streaming); each launch skips the other's experts.  The per-row
+// arithmetic is the same in every shape (K ascending in steps of 32), so the
+// result is bit-identical to one launch.  Measured on the skewed layer (45 of
+// 64 experts under 64 rows) when it ran on 256-row tiles: down 442 -> 399 us,
+// gate/up 761 -> 740 us.  On the 320-row tiles it takes now, the same split
+// measured slower (down 366 -> 420 us), so 320-row layers launch once.
 constexpr int kFewRows = 64;
+static bool split_few(long long max_rows, int E) { return !tiles320(max_rows, E); }
 
 hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const int32_t* off,
                                const uint16_t* w_gate,
                                const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
                                long long max_rows, int cus, hipStream_t s) {
-    if (small_experts(max_rows, E))
-        return launch_shape<true, 10, 4, 32, 4, 4>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0,
-                                                   E, d, d_ff, max_rows, cus, s);
-    const hipError_t e = launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0,
-                                                            nullptr, 0, E, d, d_ff, max_rows, cus,
-                                                            s, nullptr, kFewRows);
-    if (e != hipSuccess) return e;
+    const bool split = split_few(max_rows, E);
+    const int lo = split ? kFewRows : 0;
+    const hipError_t e =
+        tiles320(max_rows, E)
+            ? launch_shape<true, 10, 4, 32, 4, 4>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0,
+                                                  E, d, d_ff, max_rows, cus, s, nullptr, lo)
+            : launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0,
+                                                 E, d, d_ff, max_rows, cus, s, nullptr, lo);
+    if (e != hipSuccess || !split) return e;
     return launch_shape<true, 4, 4, 32, 4, 4>(a, w_gate, w_up, h, off, a_rows, 0, nullptr, 0, E,
                                               d, d_ff, max_rows, cus, s, nullptr, 0, kFewRows);
 }
@@ -505,13 +513,15 @@ hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, con
                                    const uint16_t* w_gate, const uint16_t* w_up, uint16_t* g,
                                    uint16_t* u, int E, int d, int d_ff, long long max_rows,
                                    int cus, hipStream_t s) {
-    if (small_experts(max_rows, E))
-        return launch_shape<true, 10, 4, 32, 4, 4>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2,
-                                                   E, d, d_ff, max_rows, cus, s, u);
-    const hipError_t e = launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0,
-                                                            nullptr, 2, E, d, d_ff, max_rows, cus,
-                                                            s, u, kFewRows);
-    if (e != hipSuccess) return e;
+    const bool split = split_few(max_rows, E);
+    const int lo = split ? kFewRows : 0;
+    const hipError_t e =
+        tiles320(max_rows, E)
+            ? launch_shape<true, 10, 4, 32, 4, 4>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2,
+                                                  E, d, d_ff, max_rows, cus, s, u, lo)
+            : launch_shape<true, 8, 4, 64, 2, 2>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2,
+                                                 E, d, d_ff, max_rows, cus, s, u, lo);
+    if (e != hipSuccess || !split) return e;
     return launch_shape<true, 4, 4, 32, 4, 4>(a, w_gate, w_up, g, off, a_rows, 0, nullptr, 2, E,
                                               d, d_ff, max_rows, cus, s, u, 0, kFewRows);
 }
@@ -520,24 +530,22 @@ hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const i
                                const uint16_t* B, uint16_t* C, int E, int K, int N,
                                long long max_rows, int cus, hipStream_t s, const float* gate,
                                const int32_t* tor, uint16_t* y) {
-    if (small_experts(max_rows, E)) {
-        // 320 x 256 tiles when they still fill the CUs (each CU then moves 36%
-        // fewer bytes per output: the wide layer's down GEMM 2.95 -> 2.36 ms);
-        // else 320 x 128 (ZAYA1-like: 128 tiles of 320 x 256 would leave half
-        // the CUs idle; 214 against 261 us)
-        if ((long long)E * ((N + 255) / 256) >= cus)
-            return launch_shape<false, 10, 4, 32, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr,
-                                                        0, E, K, N, max_rows, cus, s, nullptr, 0,
-                                                        0x7fffffff, gate, tor, y);
-        return launch_shape<false, 5, 4, 64, 2, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0,
-                                                      E, K, N, max_rows, cus, s, nullptr, 0,
-                                                      0x7fffffff, gate, tor, y);
-    }
-    const hipError_t e = launch_shape<false, 8, 4, 64, 2, 2>(A, B, nullptr, C, off, a_rows, 0,
-                                                             nullptr, 0, E, K, N, max_rows, cus, s,
-                                                             nullptr, kFewRows, 0x7fffffff, gate,
-                                                             tor, y);
-    if (e != hipSuccess) return e;
+    const bool split = split_few(max_rows, E);
+    const int lo = split ? kFewRows : 0;
+    constexpr int HI = 0x7fffffff;
+    hipError_t e;
+    if (!tiles320(max_rows, E))
+        e = launch_shape<false, 8, 4, 64, 2, 2>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E, K,
+                                                N, max_rows, cus, s, nullptr, lo, HI, gate, tor, y);
+    else if ((long long)E * ((N + 255) / 256) >= cus)
+        e = launch_shape<false, 10, 4, 32, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E,
+                                                 K, N, max_rows, cus, s, nullptr, lo, HI, gate,
+                                                 tor, y);
+    else
+        e = launch_shape<false, 5, 4, 64, 2, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0,
+                                                   E, K, N, max_rows, cus, s, nullptr, lo, HI,
+                                                   gate, tor, y);
+    if (e != hipSuccess || !split) return e;
     return launch_shape<false, 4, 4, 32, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E, K,
                                                N, max_rows, cus, s, nullptr, 0, kFewRows, gate,
                                                tor, y);

@@ -114,12 +114,15 @@ SMALL = [
     ("many_chunks", configs.get("tiny").scaled(T=70000, d=64, E=16, k=2, d_ff=64, cap_num=5,
                                                cap_den=4, renormalize=True, dtype="bf16")),
     ("tiles_2x", configs.get("tiny").scaled(T=2500, d=384, E=3, k=1, d_ff=448, dtype="bf16")),
-    # 256-row tiles with experts under 64 rows (their own launch of 128-row
-    # tiles): 15 rows in the first (top-2), 1, 2 and 11 rows in the second
-    ("few_rows_split", configs.get("tiny").scaled(T=4096, d=128, E=6, k=2, d_ff=192,
-                                                  temperature=0.5, renormalize=True,
-                                                  dtype="bf16", zipf_bias=2.5)),
-    ("few_rows_empty", configs.get("tiny").scaled(T=2048, d=128, E=5, k=1, d_ff=192,
+    # 320-row tiles over experts of very different sizes: 15 to 4054 rows
+    # (top-2), 1 to 1868 rows (top-1)
+    ("skew_320", configs.get("tiny").scaled(T=4096, d=128, E=6, k=2, d_ff=192, temperature=0.5,
+                                            renormalize=True, dtype="bf16", zipf_bias=2.5)),
+    ("skew_320_top1", configs.get("tiny").scaled(T=2048, d=128, E=5, k=1, d_ff=192,
+                                                 temperature=0.5, dtype="bf16", zipf_bias=3.0)),
+    # more than 2048 rows per expert on average: 256-row tiles, and the experts
+    # under 64 rows in their own launch of 128-row tiles (7 and 2 rows here)
+    ("few_rows_split", configs.get("tiny").scaled(T=12288, d=128, E=5, k=1, d_ff=192,
                                                   temperature=0.5, dtype="bf16", zipf_bias=3.0)),
 ]
 
