@@ -472,8 +472,8 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
 //     CU then moves 36% fewer bytes per output than with 320 x 128: the wide
 //     layer 2.95 -> 2.36 ms), else 320 x 128 with 64-deep K-steps (the
 //     ZAYA1-like layer: 128 tiles of 320 x 256 would leave half the CUs idle,
-//     261 against 214 us; 32-deep four-stage rings measured 34% slower on
-//     this tile).  Its waves are arranged 4 (M) x 2 (N): 80 x 64 per wave
+//     261 against 214 us; 32-deep steps with 4 activation and 8 weight
+//     stages measured 2% slower on this tile).  Its waves are arranged 4 (M) x 2 (N): 80 x 64 per wave
 //     instead of 160 x 32 reads 27% fewer fragment bytes from LDS per stage
 //     (measured 4% faster).
 static bool tiles320(long long max_rows, int E) { return max_rows <= 2048LL * E; }
