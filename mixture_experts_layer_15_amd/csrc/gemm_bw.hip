@@ -54,7 +54,7 @@ struct BwShape {
     static_assert(A_WL >= 1 && B_WL >= 1 && A_WL * WAVES * 1024 == A_STAGE &&
                   B_WL * WAVES * 1024 == B_STAGE, "whole wave-loads per wave");
     static_assert(MI >= 1 && NJ >= 1 && BM % (16 * WMW) == 0 && BN % (16 * WNW) == 0, "waves");
-    static_assert(BM == 128 || BM == 256, "K-row stage rows of 256 or 512 bytes");
+    static_assert(BM == 128 || BM == 256 || BM == 320, "K-row stage rows of 256 or 512 bytes");
     static_assert(BN == 128 || BN == 256, "K-row stage rows of 256 or 512 bytes");
     static_assert(NS >= 2 && NS <= 4, "stages");
     static_assert(NS * (A_STAGE + B_STAGE) + 4096 <= 160 * 1024, "LDS budget");
@@ -93,6 +93,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     const BwOperands ops, const int32_t* __restrict__ off, int E, int M, int N, int K) {
     using S = BwShape<BM, BN, WAVES, WMW, NS, TK>;
     constexpr bool KROW = MODE == 1;
+    static_assert(!KROW || BM != 320, "320-row tiles only with K-contiguous (NT) operands");
     constexpr int MI = S::MI, NJ = S::NJ;
     __shared__ __attribute__((aligned(1024))) char sa0[S::A_STAGE];
     __shared__ __attribute__((aligned(1024))) char sa1[S::A_STAGE];
@@ -331,7 +332,9 @@ hipError_t launch_tn(const BwOperands& ops, const int32_t* off, int E, int M, in
     return hipGetLastError();
 }
 
-constexpr int BW_BM = 256;   // NT rows per tile
+// NT rows per tile: 320 when the experts hold up to 320 rows on average (one
+// M-tile covers a ZAYA1-like expert, as in the forward GEMMs), else 256.
+static int bw_nt_bm(long long max_rows, int E) { return max_rows <= 320LL * E ? 320 : 256; }
 // K-step and ring depth: the NT products read their weight operand in 128-byte
 // row pieces (64 K values) through a two-stage ring; the TN products, whose K
 // runs over an expert's ragged rows, keep 32-deep steps and three stages
@@ -348,7 +351,8 @@ constexpr int BW_TN_TK = 32, BW_TN_NS = 3;
 // the ZAYA1-like layer 2.38 ms against 2.95 and 2.72); a 4 x 2 wave layout and
 // a fourth stage measure within 1.5%.
 int bw_nt_ksplit(long long max_rows, int E, int N, int K, int nsrc, int cus) {
-    const long long tiles = ((max_rows + BW_BM - 1) / BW_BM + E) * ((N + 255) / 256) * nsrc;
+    const int bm = bw_nt_bm(max_rows, E);
+    const long long tiles = ((max_rows + bm - 1) / bm + E) * ((N + 255) / 256) * nsrc;
     const long long want = 3LL * (cus / 2);   // three sweeps of one workgroup per CU
     int ks = 1;
     while (ks < 4 && tiles * ks < want && (K / (2 * ks)) % BW_NT_TK == 0 && K % (2 * ks) == 0)
@@ -364,7 +368,10 @@ hipError_t launch_bw_nt(const uint16_t* A0, const uint16_t* W0, const uint16_t* 
     if (N % 8 != 0 || N < 8 || ksplit < 1 || K % ksplit != 0 || (K / ksplit) % BW_NT_TK != 0)
         return hipErrorInvalidValue;
     BwOperands ops{{A0, A1}, {W0, W1}, C, part_stride, A1 ? 2 : 1, ksplit};
-    return launch_nt<BW_BM, 256, 8, 2, BW_NT_NS, BW_NT_TK>(ops, off, E, N, K, max_rows, cus / 2, s);
+    if (bw_nt_bm(max_rows, E) == 320)
+        return launch_nt<320, 256, 8, 2, BW_NT_NS, BW_NT_TK>(ops, off, E, N, K, max_rows, cus / 2,
+                                                             s);
+    return launch_nt<256, 256, 8, 2, BW_NT_NS, BW_NT_TK>(ops, off, E, N, K, max_rows, cus / 2, s);
 }
 
 hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off,
