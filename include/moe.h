@@ -273,12 +273,16 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
                        const float* topk_gate, void* y, void* stream);
 
 /* Steps 1-7 on one stream, intermediates in the workspace
- * (ws_bytes >= moe_workspace_size(cfg, 0, .)).  Same arguments and results as
- * the four calls above in sequence, bit for bit.  Some intermediates are never
- * formed: bf16 layers gather their x rows inside the gate/up GEMM (no x_perm),
- * and bf16 top-1 layers whose capacity keeps every token have the down GEMM
- * write y itself (no y_perm, no combine).  The workspace's contents after the
- * call are unspecified. */
+ * (ws_bytes >= moe_workspace_size(cfg, 0, .), sized for the current device).
+ * Same arguments and results as the four calls above in sequence, bit for bit,
+ * with one exception below.  Some intermediates are never formed: bf16 layers
+ * gather their x rows inside the gate/up GEMM (no x_perm), and bf16 top-1
+ * layers whose capacity keeps every token have the down GEMM write y itself
+ * (no y_perm, no combine).  When such a layer has too few experts to fill the
+ * device's CUs with down-GEMM tiles, the down GEMM runs in two K slices whose
+ * fp32 partial sums a second kernel adds (rounding and gating as the combine
+ * does); its y then differs from the staged calls' by that fp32 summation
+ * order only.  The workspace's contents after the call are unspecified. */
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* bias, const void* w_gate, const void* w_up,
                        const void* w_down, void* y, void* workspace, size_t ws_bytes,

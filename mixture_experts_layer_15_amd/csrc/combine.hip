@@ -74,7 +74,50 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     }
 }
 
+// Top-1 layer that keeps every token, down GEMM in two K slices: one wave
+// per token, 8 columns per lane and step; o = bf16(P0 + P1) as the GEMM's
+// epilogue rounds its accumulators, then y = bf16(g * o) as the combine does.
+__global__ __launch_bounds__(256) void combine_split_kernel(const float* __restrict__ P,
+                                                            long long p_stride,
+                                                            const int32_t* __restrict__ row_of,
+                                                            const float* __restrict__ gate,
+                                                            u32x4* __restrict__ y, long long ntok,
+                                                            int d) {
+    const int lane = threadIdx.x & 63;
+    const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+    const int r = row_of[t];
+    const float g = gate[t];
+    const f32x4* p0 = (const f32x4*)(P + (long long)r * d);
+    const f32x4* p1 = (const f32x4*)(P + p_stride + (long long)r * d);
+    u32x4* dst = y + t * (d / 8);
+    for (int v = lane; v < d / 8; v += 64) {
+        const f32x4 a0 = p0[2 * v], a1 = p0[2 * v + 1];
+        const f32x4 b0 = p1[2 * v], b1 = p1[2 * v + 1];
+        float o[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            o[q] = (float)(__bf16)(a0[q] + b0[q]);
+            o[q + 4] = (float)(__bf16)(a1[q] + b1[q]);
+        }
+        u32x4 out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            out[q] = pack_bf16x2(fmaf(g, o[2 * q], 0.f), fmaf(g, o[2 * q + 1], 0.f));
+        dst[v] = out;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_combine_split(const float* P, long long p_stride, const int32_t* row_of,
+                                const float* gate, void* y, long long T, int d, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (d % 8 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_split_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, P,
+                       p_stride, row_of, gate, (u32x4*)y, T, d);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* row_of,
                           const float* gate, void* y, long long T, int d, int k,

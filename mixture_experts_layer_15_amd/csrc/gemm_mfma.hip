@@ -190,7 +190,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, uint16_t* __restrict__ C2,
     const int32_t* __restrict__ off, const int32_t* __restrict__ a_rows, int E, int K, int N,
     int dense_rows, const float* __restrict__ bias, int act, int rlo, int rhi,
-    const float* __restrict__ gate, const int32_t* __restrict__ tor, uint16_t* __restrict__ Y) {
+    const float* __restrict__ gate, const int32_t* __restrict__ tor, uint16_t* __restrict__ Y,
+    int ksplit, float* __restrict__ P, long long p_stride) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB, WM>;
     // one distinct __shared__ array per stage buffer, so that the compiler can
     // tell the reads of one stage from the fills of the others
@@ -211,7 +212,10 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
 
     const int ntn = (N + S::OUTC - 1) / S::OUTC;
     build_tile_table<S::BM>(off, E, ntn, tt, s_wave, dense_rows, rlo, rhi);
-    const long long total = tt.start[E];
+    // ksplit > 1 (plain GEMMs only): each output tile is computed as ksplit
+    // tiles over consecutive K slices, adjacent in the tile order, each
+    // writing its fp32 partial product to P + slice * p_stride
+    const long long total = tt.start[E] * ksplit;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const int lw = w & 3;                   // index among the loaders of its operand
     const int c16 = lane & 15, g4 = lane >> 4;
     const int G = gridDim.x;
-    const int nk = K / BKT;
+    const int nk = K / BKT / ksplit;   // K-steps per tile
 
     // Per-lane LDS read offsets: the rows a lane reads differ only in
     // multiples of 16 (A) or 4 (B), so the swizzles are lane constants.
@@ -248,8 +252,11 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     for (long long base = 0; base < total; base += G) {
         const long long t = sweep_tile(blockIdx.x, G, base, total);
         if (t < 0) continue;   // uniform across the workgroup
+        const long long to = t / ksplit;                  // output tile
+        const int slice = (int)(t - to * ksplit);         // its K slice
+        const int kb = slice * nk;                        // first K-step of the slice
         int e, mtile, ntile;
-        decode_tile<GM>(tt, E, ntn, t, e, mtile, ntile);
+        decode_tile<GM>(tt, E, ntn, to, e, mtile, ntile);
         const int row0 = (off ? off[e] : 0) + mtile * S::BM;
         const int rows = min(S::BM, (off ? off[e + 1] : dense_rows) - row0);
         const int n0 = ntile * S::OUTC;
@@ -288,13 +295,14 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         // wave-load q of A stage kt / B stage kt into the stage buffer at LDS
         // address lb
         auto load_a = [&](int kt, uint32_t lb, int q) {
-            load_to_lds(rs_a, l_off[q], (uint32_t)(kt * BKT * 2),
+            load_to_lds(rs_a, l_off[q], (uint32_t)((kb + kt) * BKT * 2),
                         lb + (lw * S::A_LOADS + q) * 1024);
         };
         auto load_b = [&](int kt, uint32_t lb, int q) {
             const int gl = lw * S::B_LOADS + q;
             load_to_lds((GATEUP && gl >= S::SUB_LOADS) ? rs_b1 : rs_b0, l_off[q],
-                        (uint32_t)kt * (uint32_t)(BKT * 2) * (uint32_t)N, lb + gl * 1024);
+                        (uint32_t)(kb + kt) * (uint32_t)(BKT * 2) * (uint32_t)N,
+                        lb + gl * 1024);
         };
         auto lds_base = [](char* p) { return __builtin_amdgcn_readfirstlane(lds_addr(p)); };
 
@@ -384,6 +392,15 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         for (int i = 0; i < MI; ++i) {
             const int r = wm * MI * 16 + i * 16 + c16;
             if (i < nvm && r < rows) {
+                if (!GATEUP && P != nullptr) {   // fp32 partial of this K slice
+                    float* prow = P + slice * p_stride + (long long)(row0 + r) * N + n0;
+#pragma unroll
+                    for (int jj = 0; jj < S::OUTW / 16; ++jj) {
+                        const int col = wn * S::OUTW + jj * 16 + g4 * 4;
+                        if (n0 + col < N) *(f32x4*)(prow + col) = acc[i][jj];
+                    }
+                    continue;
+                }
                 uint16_t* crow = C + (long long)(row0 + r) * N + n0;
                 float gr = 0.f;
                 if (!GATEUP && Y != nullptr) {
@@ -442,15 +459,16 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
                         const float* bias, int act, int E, int K, int N, long long max_rows, int cus,
                         hipStream_t s, uint16_t* C2 = nullptr, int rlo = 0,
                         int rhi = 0x7fffffff, const float* gate = nullptr,
-                        const int32_t* tor = nullptr, uint16_t* Y = nullptr) {
+                        const int32_t* tor = nullptr, uint16_t* Y = nullptr, int ksplit = 1,
+                        float* P = nullptr, long long p_stride = 0) {
     using S = Shape<GATEUP, MI, NJ, BKT, NA, NB, WM>;
     const long long mt = (max_rows + S::BM - 1) / S::BM + E;   // >= sum_e ceil(rows_e / BM)
-    const long long tiles = mt * ((N + S::OUTC - 1) / S::OUTC);
+    const long long tiles = mt * ((N + S::OUTC - 1) / S::OUTC) * ksplit;
     long long g = std::min<long long>(cus, (tiles + 7) / 8 * 8);
     g = std::max<long long>(8, g / 8 * 8);
     hipLaunchKernelGGL((gemm_mfma_kernel<GATEUP, MI, NJ, BKT, NA, NB, WM>), dim3((unsigned)g),
                        dim3(S::THREADS), 0, s, A, B0, B1, C, C2, off, a_rows, E, K, N,
-                       dense_rows, bias, act, rlo, rhi, gate, tor, Y);
+                       dense_rows, bias, act, rlo, rhi, gate, tor, Y, ksplit, P, p_stride);
     return hipGetLastError();
 }
 
@@ -549,6 +567,26 @@ hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const i
     return launch_shape<false, 4, 4, 32, 4, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E, K,
                                                N, max_rows, cus, s, nullptr, 0, kFewRows, gate,
                                                tor, y);
+}
+
+// The down GEMM in two K slices on 320 x 256 tiles: fp32 partial products
+// P[s][rows][d], s = 0, 1, to be summed by the consumer.  For layers whose
+// 320 x 256 tiles alone would not fill the CUs (the ZAYA1-like layer: 128
+// tiles), the two slices make 256 tiles, each CU moving 36% fewer bytes than
+// with 320 x 128 tiles over the whole of K.
+bool down_split_applies(long long max_rows, int E, int d, int d_ff, int cus) {
+    return tiles320(max_rows, E) && (long long)E * ((d + 255) / 256) < cus &&
+           d_ff % 128 == 0 && max_rows > 0;
+}
+
+hipError_t launch_mfma_down_split(const uint16_t* h, const int32_t* off, const uint16_t* w_down,
+                                  float* P, long long p_stride, int E, int d, int d_ff,
+                                  long long max_rows, int cus, hipStream_t s) {
+    if (!down_split_applies(max_rows, E, d, d_ff, cus)) return hipErrorInvalidValue;
+    return launch_shape<false, 10, 4, 64, 2, 2>(h, w_down, nullptr, nullptr, off, nullptr, 0,
+                                                nullptr, 0, E, d_ff, d, max_rows, cus, s, nullptr,
+                                                0, 0x7fffffff, nullptr, nullptr, nullptr, 2, P,
+                                                p_stride);
 }
 
 hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_t* w_down,

@@ -83,6 +83,18 @@ hipError_t launch_mfma_down(const uint16_t* h, const int32_t* off, const uint16_
                             int cus, hipStream_t s, const float* gate = nullptr,
                             const int32_t* tor = nullptr, uint16_t* y = nullptr);
 
+// The down GEMM in two K slices (bf16 in, fp32 partials P[2][rows][d] out,
+// p_stride floats apart), for layers where down_split_applies(): small
+// experts whose 320 x 256 down tiles alone would leave CUs idle.
+bool down_split_applies(long long max_rows, int E, int d, int d_ff, int cus);
+hipError_t launch_mfma_down_split(const uint16_t* h, const int32_t* off, const uint16_t* w_down,
+                                  float* P, long long p_stride, int E, int d, int d_ff,
+                                  long long max_rows, int cus, hipStream_t s);
+// y[t] = gate[t] * bf16(P[0][r] + P[1][r]) with r = row_of[t], for top-1
+// layers that keep every token (bf16 out, rounded as the combine rounds).
+hipError_t launch_combine_split(const float* P, long long p_stride, const int32_t* row_of,
+                                const float* gate, void* y, long long T, int d, hipStream_t s);
+
 // The gate/up GEMM's two products stored separately (bf16): g = X W_gate,
 // u = X W_up (rows of X as in launch_mfma_gate_up).
 hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, const int32_t* off,

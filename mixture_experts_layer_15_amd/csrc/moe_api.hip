@@ -140,8 +140,25 @@ int gemm_grid_cap() {
 }
 
 struct FwdLayout {
-    size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, h, y_perm, total;
+    size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, h, y_perm, part,
+        total;
 };
+
+// The fused forward's output path for bf16 top-1 layers that keep every token
+// (capacity >= T, compact layout): each row is its token's only assignment,
+// so the down GEMM's result goes straight to y, bit-identical to writing
+// y_perm and combining -- unless the down GEMM runs in two K slices
+// (down_split_applies: small experts too few to fill the CUs), whose fp32
+// partials a second kernel sums, rounds and gates (the summation order then
+// differs from the staged calls' by the split).
+bool fwd_direct(const moe_config* c) {
+    return c->dtype == MOE_BF16 && c->k == 1 && c->layout == MOE_LAYOUT_COMPACT &&
+           capacity_eff(c) >= c->T;
+}
+bool fwd_down_split(const moe_config* c) {
+    return fwd_direct(c) &&
+           moe::down_split_applies(max_rows(c), c->E, c->d, c->d_ff, gemm_grid_cap() / 2);
+}
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -163,6 +180,7 @@ FwdLayout fwd_layout(const moe_config* c) {
     L.x_perm = take(R * (size_t)c->d * esize(c));
     L.h = take(R * (size_t)c->d_ff * esize(c));
     L.y_perm = take(R * (size_t)c->d * esize(c));
+    L.part = take(fwd_down_split(c) ? 2 * R * (size_t)c->d * 4 : 0);   // fp32 K-slice partials
     L.total = o;
     return L;
 }
@@ -443,12 +461,19 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                             w_up, w + L.h, cfg->E, cfg->d, cfg->d_ff, max_rows(cfg),
                             gemm_grid_cap(), s, gather ? tor : nullptr);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/gate_up");
-    // bf16 top-1 layers that keep every token (capacity >= T): each row is one
-    // token's only assignment, so the down GEMM writes y = gate * O itself
-    // (same roundings as the combine, so the same bits) and the combine is
-    // not launched
-    const bool direct = cfg->dtype == MOE_BF16 && cfg->k == 1 &&
-                        cfg->layout == MOE_LAYOUT_COMPACT && capacity_eff(cfg) >= cfg->T;
+    // output path: see fwd_direct / fwd_down_split
+    const bool direct = fwd_direct(cfg);
+    if (fwd_down_split(cfg)) {
+        const long long pst = max_rows(cfg) * cfg->d;
+        float* P = (float*)(w + L.part);
+        e = moe::launch_mfma_down_split((const uint16_t*)(w + L.h), offset,
+                                        (const uint16_t*)w_down, P, pst, cfg->E, cfg->d,
+                                        cfg->d_ff, max_rows(cfg), gemm_grid_cap() / 2, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_forward/down");
+        e = moe::launch_combine_split(P, pst, row_of, gate, y, cfg->T, cfg->d, s);
+        if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
+        return MOE_OK;
+    }
     e = moe::launch_down(cfg->dtype, w + L.h, offset, w_down, w + L.y_perm, cfg->E, cfg->d,
                          cfg->d_ff, max_rows(cfg), gemm_grid_cap(), s, direct ? gate : nullptr,
                          direct ? tor : nullptr, direct ? y : nullptr);

@@ -131,3 +131,34 @@ def sample_rows(offset, n, full, rng, extra=96):
 
 def to_np(t):
     return t.float().cpu().double().numpy() if t.dtype == torch.bfloat16 else t.cpu().double().numpy()
+
+
+def fused_down_split(cfg) -> bool:
+    """Whether moe_forward runs this layer's down GEMM in two K slices (fp32
+    partials summed by a second kernel): bf16, top-1, compact layout, every
+    token kept, at most 2048 rows per expert on average, and too few
+    320 x 256 down tiles (E * ceil(d / 256)) to fill the CUs.  Its output then
+    differs from the staged calls' by the fp32 summation order only."""
+    import torch
+    if cfg.dtype != "bf16" or cfg.k != 1 or cfg.layout != 0 or cfg.T == 0:
+        return False
+    cap = cfg.T if cfg.cap_den == 0 else -(-cfg.cap_num * cfg.k * cfg.T // (cfg.cap_den * cfg.E))
+    if cap < cfg.T:
+        return False
+    rows = cfg.T * cfg.k
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (rows <= 2048 * cfg.E and cfg.E * -(-cfg.d // 256) < cus and cfg.d_ff % 128 == 0)
+
+
+def bf16_ulp_distance(a, b) -> int:
+    """Largest distance, in units in the last place, between two bf16 tensors
+    of the same shape (+0 and -0 are the same value)."""
+    import torch
+    def key(t):
+        u = t.contiguous().view(torch.int16).to(torch.int32) & 0xFFFF
+        mag = u & 0x7FFF
+        return torch.where((u & 0x8000) != 0, -mag, mag)
+    if a.numel() == 0:
+        return 0
+    return int((key(a) - key(b)).abs().max().item())
+

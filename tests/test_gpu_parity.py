@@ -19,8 +19,9 @@ import mixture_experts_layer_15_amd as moe
 from mixture_experts_layer_15_amd import configs
 from oracle import oracle as orc
 
-from parity_util import (TOL_Y, check_dispatch, check_logits, check_route, check_x_perm,
-                         expert_of_rows, gpu_inputs, rel_err, sample_rows, say, to_np)
+from parity_util import (TOL_Y, bf16_ulp_distance, check_dispatch, check_logits, check_route,
+                         check_x_perm, expert_of_rows, fused_down_split, gpu_inputs, rel_err,
+                         sample_rows, say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,7 +96,18 @@ def run_layer(cfg, dev, host, full, seed=0, label=""):
     yf = moe.forward(cfg, x, wr, b, dev["w_gate"], dev["w_up"], dev["w_down"])
     torch.cuda.synchronize()
     iv = torch.int16 if y.dtype == torch.bfloat16 else torch.int32
-    assert torch.equal(yf.view(iv), y.view(iv)), "fused forward differs from the staged calls"
+    if fused_down_split(cfg):
+        # the fused down GEMM sums K in two fp32 slices: the outputs differ from
+        # the staged calls' only by that summation order -- a rounding step at
+        # most, measured against the output's scale (near-cancelling values can
+        # differ by many of their own ulps) -- and meet the oracle's tolerance
+        d_fs = rel_err(to_np(yf), to_np(y))
+        e_f = rel_err(to_np(yf[torch.from_numpy(stoks).cuda()]), ofw["y"]) if cfg.T else 0.0
+        say(f"[{label}] fused forward: {d_fs:.3g} of max |y| from the staged calls "
+            f"({bf16_ulp_distance(yf, y)} ulp at most), y err {e_f:.3g}")
+        assert d_fs <= 2.0 ** -7 and e_f <= TOL_Y[cfg.dtype]
+    else:
+        assert torch.equal(yf.view(iv), y.view(iv)), "fused forward differs from the staged calls"
     return dict(logits=logits, idx=idx, gate=gate, dsp=dsp, h=h, y_perm=y_perm, y=y, n=n)
 
 
@@ -120,6 +132,10 @@ SMALL = [
                                             renormalize=True, dtype="bf16", zipf_bias=2.5)),
     ("skew_320_top1", configs.get("tiny").scaled(T=2048, d=128, E=5, k=1, d_ff=192,
                                                  temperature=0.5, dtype="bf16", zipf_bias=3.0)),
+    # top-1, every token kept, few experts: the fused forward's down GEMM in two
+    # K slices (d = 320: a ragged second N-tile)
+    ("split_down", configs.get("tiny").scaled(T=3000, d=320, E=6, k=1, d_ff=384,
+                                              temperature=0.7, dtype="bf16")),
     # more than 2048 rows per expert on average: 256-row tiles, and the experts
     # under 64 rows in their own launch of 128-row tiles (7 and 2 rows here)
     ("few_rows_split", configs.get("tiny").scaled(T=12288, d=128, E=5, k=1, d_ff=192,
