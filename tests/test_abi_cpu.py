@@ -167,6 +167,23 @@ def test_choice_order_workspace_is_sized_for_the_walked_choices(L):
             want(cfg.T * cfg.k, cfg.E)
 
 
+def test_forward_workspace_holds_the_split_down_partials(L):
+    # moe_forward's workspace: dispatch tables and the intermediates, plus two
+    # fp32 partial products [2][R][d] when a bf16 top-1 layer that keeps every
+    # token runs its down GEMM in two K slices (the ZAYA1-like layer: 16
+    # experts give 128 down tiles of 320 x 256, too few for 256 CUs); a top-2
+    # layer never does.  Host-only: sizes, no GPU call.
+    z = configs.get("zaya1")
+    R, d = moe.max_rows(z), z.d
+    parts = 2 * R * d * 4
+    base = z.T * z.E * 4 + R * (2 * d + z.d_ff) * 2   # logits, x_perm, h, y_perm
+    assert moe.workspace_bytes(z) >= base + parts
+    two = z.scaled(k=2, renormalize=True)
+    R2 = moe.max_rows(two)
+    assert moe.workspace_bytes(two) < two.T * two.E * 4 + R2 * (2 * d + two.d_ff) * 2 + \
+        2 * R2 * d * 4
+
+
 def test_workspace_too_small_rejected(L):
     cfg = configs.get("wide")
     c = moe.cconfig(cfg)
