@@ -126,6 +126,9 @@ SMALL = [
     ("many_chunks", configs.get("tiny").scaled(T=70000, d=64, E=16, k=2, d_ff=64, cap_num=5,
                                                cap_den=4, renormalize=True, dtype="bf16")),
     ("tiles_2x", configs.get("tiny").scaled(T=2500, d=384, E=3, k=1, d_ff=448, dtype="bf16")),
+    # k = E: every expert chosen, renormalised gates = the softmax over all experts
+    ("k_eq_E", configs.get("tiny").scaled(T=500, d=128, E=4, k=4, d_ff=128, temperature=0.5,
+                                          renormalize=True, dtype="bf16")),
     # 320-row tiles over experts of very different sizes: 15 to 4054 rows
     # (top-2), 1 to 1868 rows (top-1)
     ("skew_320", configs.get("tiny").scaled(T=4096, d=128, E=6, k=2, d_ff=192, temperature=0.5,
