@@ -71,17 +71,20 @@ __device__ __forceinline__ int kc_sw(int r) { return TK == 32 ? (r >> 2) & 3 : (
 // GEMM for rows of 256 or 512 bytes).
 __device__ __forceinline__ int kr_sw(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
-// Operands of one launch.  NT runs nsrc x ksplit independent parts: part p
-// multiplies source s = p / ksplit (A[s] [rows][K] by W = B[s] [E][N][K]) over
-// the K slice p % ksplit of K / ksplit, into its own fp32 buffer
+// Operands of one launch.  NT runs ksplit parts per source group: part p
+// covers the K slice p % ksplit of K / ksplit, into its own fp32 buffer
 // C + p * c_stride ([rows][N]); the parts are summed by their consumer, in
-// part order.  TN uses A[0], B[0] and C.
+// part order.  With fuse == 0 each of the nsrc sources is its own group (part
+// p multiplies source p / ksplit: A[s] [rows][K] by W = B[s] [E][N][K]); with
+// fuse == 1 (nsrc == 2) one accumulator runs over the slice of source 0 and
+// then the same slice of source 1, so the two products are summed in the
+// tile and there are ksplit parts in all.  TN uses A[0], B[0] and C.
 struct BwOperands {
     const uint16_t* A[2];
     const uint16_t* B[2];
     float* C;
     long long c_stride;
-    int nsrc, ksplit;
+    int nsrc, ksplit, fuse;
 };
 
 // MODE 0 (NT): tiles from the expert row counts (ragged M) for every part;
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     if (MODE == 0) {
         build_tile_table<BM>(off, E, ntn, tt, s_wave);
         per_part = tt.start[E];
-        total = per_part * ops.nsrc * ops.ksplit;
+        total = per_part * (ops.fuse ? 1 : ops.nsrc) * ops.ksplit;
     } else {
         mtn = (M + BM - 1) / BM;
         total = (long long)E * mtn * ntn;
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
         const uint16_t* B = ops.B[0];
         if (MODE == 0) {
             part = (int)(t / per_part);
-            const int src = part / ops.ksplit;
+            const int src = ops.fuse ? 0 : part / ops.ksplit;
             A = src ? ops.A[1] : ops.A[0];
             B = src ? ops.B[1] : ops.B[0];
             k_len = K / ops.ksplit;
@@ -156,7 +159,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
             row0 = off[e];
             k_len = off[e + 1] - row0;
         }
-        const int nk = (k_len + TK - 1) / TK;
+        const int nks = (k_len + TK - 1) / TK;              // K-steps per source
+        const bool two = MODE == 0 && ops.fuse;             // NT: both sources, one accumulator
+        const int nk = two ? 2 * nks : nks;
 
         // this lane's byte offset for each of its wave-loads (q < A_WL: A, else B)
         uint32_t l_off[S::LOADS];
@@ -188,11 +193,17 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
                                            : B + (long long)row0 * N + n0;
         const i32x4 rs_a0 = buffer_rsrc(a_base);
         const i32x4 rs_b0 = buffer_rsrc(b_base);
+        // fused NT: the second source's descriptors (same rows, same K slice)
+        const i32x4 rs_a1 =
+            two ? buffer_rsrc(ops.A[1] + (long long)row0 * K + k_beg) : rs_a0;
+        const i32x4 rs_b1 =
+            two ? buffer_rsrc(ops.B[1] + ((long long)e * N + n0) * K + k_beg) : rs_b0;
 
         // all loads of K-step kt into stage buffers (la, lb)
         auto issue = [&](int kt, uint32_t la, uint32_t lb) {
-            const int k0 = kt * TK;
-            i32x4 ra = rs_a0, rb = rs_b0;
+            const bool second = two && kt >= nks;            // uniform
+            const int k0 = (second ? kt - nks : kt) * TK;
+            i32x4 ra = second ? rs_a1 : rs_a0, rb = second ? rs_b1 : rs_b0;
             uint32_t so = (uint32_t)k0 * 2u;
             if (MODE == 1) {
                 // descriptors that start at row k0 and end at the expert's last
@@ -316,8 +327,8 @@ unsigned grid_of(long long tiles, int cap) {
 template <int BM, int BN, int WAVES, int WMW, int NS, int TK>
 hipError_t launch_nt(const BwOperands& ops, const int32_t* off, int E, int N, int K,
                      long long max_rows, int cap, hipStream_t s) {
-    const long long tiles =
-        ((max_rows + BM - 1) / BM + E) * ((N + BN - 1) / BN) * ops.nsrc * ops.ksplit;
+    const long long tiles = ((max_rows + BM - 1) / BM + E) * ((N + BN - 1) / BN) *
+                            (ops.fuse ? 1 : ops.nsrc) * ops.ksplit;
     hipLaunchKernelGGL((gemm_bw_kernel<0, BM, BN, WAVES, WMW, NS, TK>), dim3(grid_of(tiles, cap)),
                        dim3(64 * WAVES), 0, s, ops, off, E, 0, N, K);
     return hipGetLastError();
@@ -367,7 +378,8 @@ hipError_t launch_bw_nt(const uint16_t* A0, const uint16_t* W0, const uint16_t* 
     if (max_rows == 0) return hipSuccess;
     if (N % 8 != 0 || N < 8 || ksplit < 1 || K % ksplit != 0 || (K / ksplit) % BW_NT_TK != 0)
         return hipErrorInvalidValue;
-    BwOperands ops{{A0, A1}, {W0, W1}, C, part_stride, A1 ? 2 : 1, ksplit};
+    // two sources accumulate in one tile: ksplit parts in all
+    BwOperands ops{{A0, A1}, {W0, W1}, C, part_stride, A1 ? 2 : 1, ksplit, A1 ? 1 : 0};
     if (bw_nt_bm(max_rows, E) == 320)
         return launch_nt<320, 256, 8, 2, BW_NT_NS, BW_NT_TK>(ops, off, E, N, K, max_rows, cus / 2,
                                                              s);
@@ -378,7 +390,7 @@ hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const in
                         int E, int M, int N, int cus, hipStream_t s) {
     if (E == 0) return hipSuccess;
     if (M % 8 != 0 || N % 8 != 0 || M < 8 || N < 8) return hipErrorInvalidValue;
-    BwOperands ops{{A, nullptr}, {B, nullptr}, C, 0, 1, 1};
+    BwOperands ops{{A, nullptr}, {B, nullptr}, C, 0, 1, 1, 0};
     return launch_tn<256, 256, 8, 2, BW_TN_NS, BW_TN_TK>(ops, off, E, M, N, cus / 2, s);
 }
 

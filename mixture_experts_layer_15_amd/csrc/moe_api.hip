@@ -493,7 +493,7 @@ namespace {
 struct BwdLayout {
     size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, dy_perm, G, U,
         gH, dHr, dXp, dgrow, dl, dwr, total;
-    int dx_parts;   // parts of dx_perm (gate and up, each in K slices)
+    int dx_parts;   // parts of dx_perm (K slices; each sums the gate and up products)
 };
 
 BwdLayout bwd_layout(const moe_config* c) {
@@ -517,7 +517,7 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.U = take(R * F * 2);
     L.gH = take(R * F * 2);
     L.dHr = take(R * F * 4);
-    L.dx_parts = 2 * moe::bw_nt_ksplit((long long)R, c->E, c->d, c->d_ff, 2, gemm_grid_cap());
+    L.dx_parts = moe::bw_nt_ksplit((long long)R, c->E, c->d, c->d_ff, 1, gemm_grid_cap());
     L.dXp = take((size_t)L.dx_parts * R * d * 4);
     L.dgrow = take(R * 4);
     L.dl = take(T * E * 4);
@@ -624,10 +624,11 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     BWD(moe::launch_geglu_bwd(G, U, dHr, gH, dgrow, offset, tor, row_of, gate, Ei, ki, Fi, Rl, s),
         "moe_backward/geglu");
     // G, U now hold dg, du
-    // dx_perm in parts: (dg W_gate^T, du W_up^T) x K slices, summed by launch_dx
+    // dx_perm in parts, one per K slice, each dg W_gate^T + du W_up^T over that
+    // slice in one accumulator; summed by launch_dx
     const long long part = Rl * (long long)di;
     BWD(moe::launch_bw_nt(G, (const uint16_t*)w_gate, U, (const uint16_t*)w_up, dXp, part,
-                          L.dx_parts / 2, offset, Ei, di, Fi, Rl, cus, s), "moe_backward/dx_perm");
+                          L.dx_parts, offset, Ei, di, Fi, Rl, cus, s), "moe_backward/dx_perm");
     BWD(moe::launch_bw_tn(x_perm, G, dw_gate, offset, Ei, di, Fi, cus, s), "moe_backward/dw_gate");
     BWD(moe::launch_bw_tn(x_perm, U, dw_up, offset, Ei, di, Fi, cus, s), "moe_backward/dw_up");
     BWD(moe::launch_bw_tn(gH, dy_perm, dw_down, offset, Ei, Fi, di, cus, s), "moe_backward/dw_down");
