@@ -23,9 +23,11 @@
  *   - Pointers are DEVICE pointers (memory of the current HIP device) unless
  *     the comment says "host".  Arrays are row-major and contiguous.  Device
  *     arrays must be 16-byte aligned.
- *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *     enqueues work on that stream and returns; nothing synchronises with the
- *     host.  Results are visible after the caller synchronises the stream.
+ *   - `stream` is a hipStream_t (NULL = the default stream), passed as void*
+ *     so that this header needs no HIP header and plain C callers can include
+ *     it.  Every call only enqueues work on that stream and returns; nothing
+ *     synchronises with the host.  Results are visible after the caller
+ *     synchronises the stream.
  *   - The caller owns every buffer.  The library allocates no memory, frees
  *     nothing and keeps no pointer after a call returns.
  *   - Errors are reported by the returned moe_status; nothing is thrown across
@@ -49,10 +51,10 @@ extern "C" {
 
 typedef enum {
     MOE_OK = 0,
-    MOE_ERR_INVALID_ARG = 1,  /* a size, pointer, alignment or config field is out of range */
-    MOE_ERR_UNSUPPORTED = 2,  /* a valid layer this build does not run (dtype) */
-    MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than moe_workspace_size() */
-    MOE_ERR_HIP = 4           /* the HIP runtime reported an error when enqueuing */
+    MOE_ERR_INVALID_ARG = -1,  /* a size, pointer, alignment or config field is out of range */
+    MOE_ERR_UNSUPPORTED = -2,  /* a valid layer this build does not run (dtype) */
+    MOE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the *_workspace_size() */
+    MOE_ERR_HIP = -4           /* the HIP runtime reported an error when enqueuing */
 } moe_status;
 
 typedef enum {
@@ -124,9 +126,13 @@ int64_t moe_capacity(const moe_config* cfg);
  * token_of_row needs max(T * k, this) entries. */
 int64_t moe_max_rows(const moe_config* cfg);
 
-/* Host.  Bytes of workspace moe_dispatch (dispatch_only = 1) or moe_forward
- * (dispatch_only = 0) needs for this config, written to *bytes. */
-moe_status moe_workspace_size(const moe_config* cfg, int dispatch_only, size_t* bytes);
+/* Host.  Bytes of workspace moe_forward needs for this config (on the
+ * current device), written to *bytes.  It is also enough for moe_dispatch. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Host.  Bytes of workspace moe_dispatch needs for this config (at most
+ * moe_workspace_size's), written to *bytes. */
+moe_status moe_dispatch_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* Host.  Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);
@@ -214,7 +220,7 @@ moe_status moe_route_mlp(const moe_config* cfg, const moe_mlp_router* router, co
  *                                int32  out  token of each kept row; empty rows and
  *                                            entries past offset[E] are set to -1
  * In the padded layout the empty rows of x_perm are set to zero.
- *   workspace     ws_bytes >= moe_workspace_size(cfg, 1, .)
+ *   workspace     ws_bytes >= moe_dispatch_workspace_size(cfg, .)
  * An assignment (t, j) to expert e is kept iff fewer than C assignments to e
  * come before it in cfg->drop_policy's order; with MOE_DROP_TOKEN_ORDER, iff
  * fewer than C earlier tokens (t' < t, at any rank) chose e ("drop overflow
@@ -273,7 +279,7 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
                        const float* topk_gate, void* y, void* stream);
 
 /* Steps 1-7 on one stream, intermediates in the workspace
- * (ws_bytes >= moe_workspace_size(cfg, 0, .), sized for the current device).
+ * (ws_bytes >= moe_workspace_size(cfg, .), sized for the current device).
  * Same arguments and results as the four calls above in sequence, bit for bit,
  * with one exception below.  Some intermediates are never formed: bf16 layers
  * gather their x rows inside the gate/up GEMM (no x_perm), and bf16 top-1

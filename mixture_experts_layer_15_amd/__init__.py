@@ -18,12 +18,13 @@ from .configs import CONFIGS, MoEConfig, get  # noqa: F401
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_DROP_TOKEN_ORDER, MOE_DROP_CHOICE_ORDER = 0, 1
 MOE_LAYOUT_COMPACT, MOE_LAYOUT_PADDED = 0, 1
 
-EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_status_string",
+EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_dispatch_workspace_size",
+           "moe_status_string",
            "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
            "moe_forward", "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",
@@ -72,8 +73,10 @@ def lib() -> ctypes.CDLL:
         L.moe_capacity.restype = ctypes.c_int64
         L.moe_max_rows.argtypes = [cp]
         L.moe_max_rows.restype = ctypes.c_int64
-        L.moe_workspace_size.argtypes = [cp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_workspace_size.argtypes = [cp, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_workspace_size.restype = ctypes.c_int
+        L.moe_dispatch_workspace_size.argtypes = [cp, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_dispatch_workspace_size.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
@@ -135,6 +138,35 @@ def _need(t, name, dtype, shape, device):
                          f"{'' if t.is_contiguous() else ' (not contiguous)'}")
 
 
+# Output sentinels, off by default (tests turn them on): every output the
+# binding allocates then starts as NaN (floating) or -7 (integer) and every
+# workspace as 0xFF bytes, so an element that a kernel fails to write shows
+# up in a comparison instead of passing on a stale value.
+_SENTINELS = os.environ.get("MOE_OUTPUT_SENTINELS", "") == "1"
+
+
+def set_output_sentinels(on: bool) -> None:
+    global _SENTINELS
+    _SENTINELS = bool(on)
+
+
+def _out(shape, dtype, device):
+    import torch
+    shape = (shape,) if isinstance(shape, int) else tuple(shape)
+    if not _SENTINELS:
+        return torch.empty(shape, dtype=dtype, device=device)
+    fill = float("nan") if dtype.is_floating_point else -7
+    return torch.full(shape, fill, dtype=dtype, device=device)
+
+
+def _workspace(nbytes: int, device):
+    import torch
+    n = max(int(nbytes), 16)
+    if not _SENTINELS:
+        return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device=device)
+
+
 def _dt(cfg: MoEConfig):
     import torch
     return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -149,9 +181,11 @@ def max_rows(cfg: MoEConfig) -> int:
 
 
 def workspace_bytes(cfg: MoEConfig, dispatch_only: bool = False) -> int:
+    """moe_workspace_size (moe_forward), or moe_dispatch_workspace_size."""
     n = ctypes.c_size_t(0)
-    _check(lib().moe_workspace_size(ctypes.byref(cconfig(cfg)), int(dispatch_only),
-                                    ctypes.byref(n)), "moe_workspace_size")
+    fn = lib().moe_dispatch_workspace_size if dispatch_only else lib().moe_workspace_size
+    _check(fn(ctypes.byref(cconfig(cfg)), ctypes.byref(n)),
+           "moe_dispatch_workspace_size" if dispatch_only else "moe_workspace_size")
     return n.value
 
 
@@ -163,9 +197,9 @@ def route(cfg: MoEConfig, x, w_router, bias=None):
     _need(w_router, "w_router", _dt(cfg), (cfg.d, cfg.E), dev)
     if bias is not None:
         _need(bias, "bias", torch.float32, (cfg.E,), dev)
-    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
-    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
-    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    logits = _out((cfg.T, cfg.E), torch.float32, dev)
+    idx = _out((cfg.T, cfg.k), torch.int32, dev)
+    gate = _out((cfg.T, cfg.k), torch.float32, dev)
     _check(lib().moe_route(ctypes.byref(cconfig(cfg)), _ptr(x), _ptr(w_router), _ptr(bias),
                            _ptr(logits), _ptr(idx), _ptr(gate), _stream()), "moe_route")
     return logits, idx, gate
@@ -176,8 +210,8 @@ def route_from_logits(cfg: MoEConfig, logits):
     import torch
     dev = logits.device
     _need(logits, "logits", torch.float32, (cfg.T, cfg.E), dev)
-    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
-    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    idx = _out((cfg.T, cfg.k), torch.int32, dev)
+    gate = _out((cfg.T, cfg.k), torch.float32, dev)
     _check(lib().moe_route_from_logits(ctypes.byref(cconfig(cfg)), _ptr(logits), _ptr(idx),
                                        _ptr(gate), _stream()), "moe_route_from_logits")
     return idx, gate
@@ -191,13 +225,13 @@ def dispatch(cfg: MoEConfig, topk_idx, x) -> Dict:
     _need(x, "x", _dt(cfg), (cfg.T, cfg.d), dev)
     R = max_rows(cfg)
     out = dict(
-        x_perm=torch.empty((R, cfg.d), dtype=_dt(cfg), device=dev),
-        expert_count=torch.empty(cfg.E, dtype=torch.int32, device=dev),
-        expert_offset=torch.empty(cfg.E + 1, dtype=torch.int32, device=dev),
-        row_of=torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
-        token_of_row=torch.empty(max(cfg.T * cfg.k, R), dtype=torch.int32, device=dev))
+        x_perm=_out((R, cfg.d), _dt(cfg), dev),
+        expert_count=_out(cfg.E, torch.int32, dev),
+        expert_offset=_out(cfg.E + 1, torch.int32, dev),
+        row_of=_out((cfg.T, cfg.k), torch.int32, dev),
+        token_of_row=_out(max(cfg.T * cfg.k, R), torch.int32, dev))
     wsb = workspace_bytes(cfg, dispatch_only=True)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    ws = _workspace(wsb, dev)
     _check(lib().moe_dispatch(ctypes.byref(cconfig(cfg)), _ptr(topk_idx), _ptr(x),
                               _ptr(out["x_perm"]), _ptr(out["expert_count"]),
                               _ptr(out["expert_offset"]), _ptr(out["row_of"]),
@@ -232,10 +266,10 @@ def route_mlp(cfg: MoEConfig, x, prev, router: Dict, gamma: float, eps: float):
     n = ctypes.c_size_t(0)
     _check(lib().moe_mlp_router_workspace_size(ctypes.byref(c), ctypes.byref(cr), ctypes.byref(n)),
            "moe_mlp_router_workspace_size")
-    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
-    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
-    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
-    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    ws = _workspace(n.value, dev)
+    logits = _out((cfg.T, cfg.E), torch.float32, dev)
+    idx = _out((cfg.T, cfg.k), torch.int32, dev)
+    gate = _out((cfg.T, cfg.k), torch.float32, dev)
     _check(lib().moe_route_mlp(ctypes.byref(c), ctypes.byref(cr), _ptr(x), _ptr(prev),
                                _ptr(logits), _ptr(idx), _ptr(gate), _ptr(ws), n.value, _stream()),
            "moe_route_mlp")
@@ -249,7 +283,7 @@ def load_stats(cfg: MoEConfig, expert_count):
     import torch
     dev = expert_count.device
     _need(expert_count, "expert_count", torch.int32, (cfg.E,), dev)
-    stats = torch.empty(8, dtype=torch.float64, device=dev)
+    stats = _out(8, torch.float64, dev)
     _check(lib().moe_load_stats(ctypes.byref(cconfig(cfg)), _ptr(expert_count), _ptr(stats),
                                 _stream()), "moe_load_stats")
     return stats
@@ -265,8 +299,8 @@ def expert_ffn(cfg: MoEConfig, x_perm, expert_offset, w_gate, w_up, w_down) -> T
     _need(w_gate, "w_gate", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
     _need(w_up, "w_up", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
     _need(w_down, "w_down", _dt(cfg), (cfg.E, cfg.d_ff, cfg.d), dev)
-    h = torch.empty((R, cfg.d_ff), dtype=_dt(cfg), device=dev)
-    y_perm = torch.empty((R, cfg.d), dtype=_dt(cfg), device=dev)
+    h = _out((R, cfg.d_ff), _dt(cfg), dev)
+    y_perm = _out((R, cfg.d), _dt(cfg), dev)
     _check(lib().moe_expert_ffn(ctypes.byref(cconfig(cfg)), _ptr(x_perm), _ptr(expert_offset),
                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(y_perm),
                                 _stream()), "moe_expert_ffn")
@@ -283,7 +317,7 @@ def expert_gate_up(cfg: MoEConfig, x_perm, expert_offset, w_gate, w_up, h=None):
     _need(w_gate, "w_gate", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
     _need(w_up, "w_up", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
     if h is None:
-        h = torch.empty((R, cfg.d_ff), dtype=_dt(cfg), device=dev)
+        h = _out((R, cfg.d_ff), _dt(cfg), dev)
     _need(h, "h", _dt(cfg), (R, cfg.d_ff), dev)
     _check(lib().moe_expert_gate_up(ctypes.byref(cconfig(cfg)), _ptr(x_perm), _ptr(expert_offset),
                                     _ptr(w_gate), _ptr(w_up), _ptr(h), _stream()),
@@ -300,7 +334,7 @@ def expert_down(cfg: MoEConfig, h, expert_offset, w_down, y_perm=None):
     _need(expert_offset, "expert_offset", torch.int32, (cfg.E + 1,), dev)
     _need(w_down, "w_down", _dt(cfg), (cfg.E, cfg.d_ff, cfg.d), dev)
     if y_perm is None:
-        y_perm = torch.empty((R, cfg.d), dtype=_dt(cfg), device=dev)
+        y_perm = _out((R, cfg.d), _dt(cfg), dev)
     _need(y_perm, "y_perm", _dt(cfg), (R, cfg.d), dev)
     _check(lib().moe_expert_down(ctypes.byref(cconfig(cfg)), _ptr(h), _ptr(expert_offset),
                                  _ptr(w_down), _ptr(y_perm), _stream()), "moe_expert_down")
@@ -314,7 +348,7 @@ def combine(cfg: MoEConfig, y_perm, row_of, topk_gate):
     _need(y_perm, "y_perm", _dt(cfg), (max_rows(cfg), cfg.d), dev)
     _need(row_of, "row_of", torch.int32, (cfg.T, cfg.k), dev)
     _need(topk_gate, "topk_gate", torch.float32, (cfg.T, cfg.k), dev)
-    y = torch.empty((cfg.T, cfg.d), dtype=_dt(cfg), device=dev)
+    y = _out((cfg.T, cfg.d), _dt(cfg), dev)
     _check(lib().moe_combine(ctypes.byref(cconfig(cfg)), _ptr(y_perm), _ptr(row_of),
                              _ptr(topk_gate), _ptr(y), _stream()), "moe_combine")
     return y
@@ -328,7 +362,7 @@ class Forward:
         self.cfg = cfg
         self.c = cconfig(cfg)
         self.ws_bytes = workspace_bytes(cfg)
-        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.ws = _workspace(self.ws_bytes, device)
 
     def __call__(self, x, w_router, bias, w_gate, w_up, w_down, y=None):
         import torch
@@ -342,7 +376,9 @@ class Forward:
         _need(w_up, "w_up", _dt(cfg), (cfg.E, cfg.d, cfg.d_ff), dev)
         _need(w_down, "w_down", _dt(cfg), (cfg.E, cfg.d_ff, cfg.d), dev)
         if y is None:
-            y = torch.empty((cfg.T, cfg.d), dtype=_dt(cfg), device=dev)
+            y = _out((cfg.T, cfg.d), _dt(cfg), dev)
+        if _SENTINELS:   # no call may depend on what an earlier one left behind
+            self.ws.fill_(0xFF)
         _check(lib().moe_forward(ctypes.byref(self.c), _ptr(x), _ptr(w_router), _ptr(bias),
                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(self.ws),
                                  self.ws_bytes, _stream()), "moe_forward")
@@ -369,7 +405,7 @@ class Backward:
         self.cfg = cfg
         self.c = cconfig(cfg)
         self.ws_bytes = backward_workspace_bytes(cfg)
-        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.ws = _workspace(self.ws_bytes, device)
 
     def __call__(self, x, w_router, bias, w_gate, w_up, w_down, dy, out: Optional[Dict] = None,
                  want_dgate: bool = True, want_dbias: bool = True) -> Dict:
@@ -399,8 +435,10 @@ class Backward:
                 g[name] = None
                 continue
             if g.get(name) is None:
-                g[name] = torch.empty(shape, dtype=tdt, device=dev)
+                g[name] = _out(shape, tdt, dev)
             _need(g[name], name, tdt, shape, dev)
+        if _SENTINELS:
+            self.ws.fill_(0xFF)
         _check(lib().moe_backward(ctypes.byref(self.c), _ptr(x), _ptr(w_router), _ptr(bias),
                                   _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dy), _ptr(g["dx"]),
                                   _ptr(g["dw_router"]), _ptr(g["dbias"]), _ptr(g["dw_gate"]),

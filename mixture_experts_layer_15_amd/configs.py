@@ -15,7 +15,10 @@ Where each number comes from (page titles as printed on the pages):
 * ``wide`` -- FFN width 8192, 128 experts, capacity factor 1.25, gate
   temperature 0.3, top-2, from the TorchTitan 1K-GPU article, section 2.1.
 * ``skewed`` -- a routing stress case: 64 experts, top-2, capacity factor 1.25,
-  temperature 0.3, with a Zipf(s = 1.2) log-popularity router bias.
+  temperature 0.3, with a Zipf(s = 1.2) log-popularity router bias scaled by
+  0.4, so that about 30% of the tokens have expert 0 among their two choices
+  (30.3% on the CPU-drawn inputs of seed 0; the unscaled prior, whose mass on
+  expert 0 is 29.3%, sends 77% of the tokens there on N(0, 1)-scale logits).
 * ``longseq`` -- 65,536 tokens x hidden 6,144 from "Training a 1T-Params MoE on
   EU public infrastructure" (the activation-offload paragraph), as one GPU's
   share with 8 local experts.
@@ -40,6 +43,7 @@ class MoEConfig:
     renormalize: bool    # gates renormalised over the chosen k experts
     dtype: str           # "f32" or "bf16" for activations and weights
     zipf_bias: Optional[float] = None  # Zipf exponent of the router bias, or None for no bias
+    zipf_scale: float = 1.0  # factor on the Zipf log-prior bias
     drop_policy: int = 0  # 0: overflow dropped in token order; 1: choice order (first choices first)
     layout: int = 0       # 0: compact expert-grouped rows; 1: padded to C rows per expert
 
@@ -56,7 +60,8 @@ CONFIGS = [
     MoEConfig("wide", T=16384, d=4096, E=128, k=2, d_ff=8192, temperature=0.3,
               cap_num=5, cap_den=4, renormalize=True, dtype="bf16"),
     MoEConfig("skewed", T=32768, d=2048, E=64, k=2, d_ff=4096, temperature=0.3,
-              cap_num=5, cap_den=4, renormalize=True, dtype="bf16", zipf_bias=1.2),
+              cap_num=5, cap_den=4, renormalize=True, dtype="bf16", zipf_bias=1.2,
+              zipf_scale=0.4),
     MoEConfig("longseq", T=65536, d=6144, E=8, k=2, d_ff=4096, temperature=1.0,
               cap_num=5, cap_den=4, renormalize=True, dtype="bf16"),
 ]

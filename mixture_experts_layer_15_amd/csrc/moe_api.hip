@@ -160,6 +160,14 @@ bool fwd_down_split(const moe_config* c) {
            moe::down_split_applies(max_rows(c), c->E, c->d, c->d_ff, gemm_grid_cap() / 2);
 }
 
+// The fused forward's input path for bf16 compact layers: the gate/up GEMM
+// gathers its rows of x through token_of_row, so x_perm is never formed (the
+// GEMM's 32-bit byte offsets must span x).
+bool fwd_gather(const moe_config* c) {
+    return c->dtype == MOE_BF16 && c->layout == MOE_LAYOUT_COMPACT &&
+           (size_t)c->T * (size_t)c->d * esize(c) < ((size_t)1 << 32);
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 FwdLayout fwd_layout(const moe_config* c) {
@@ -177,9 +185,11 @@ FwdLayout fwd_layout(const moe_config* c) {
     L.row_of = take(T * k * 4);
     L.token_of_row = take((size_t)tor_len(c) * 4);
     L.dsp = take(moe::dispatch_workspace_bytes(p));
-    L.x_perm = take(R * (size_t)c->d * esize(c));
+    // x_perm only when the gate/up GEMM does not gather x itself, y_perm only
+    // when the down GEMM does not write y itself
+    L.x_perm = take(fwd_gather(c) ? 0 : R * (size_t)c->d * esize(c));
     L.h = take(R * (size_t)c->d_ff * esize(c));
-    L.y_perm = take(R * (size_t)c->d * esize(c));
+    L.y_perm = take(fwd_direct(c) ? 0 : R * (size_t)c->d * esize(c));
     L.part = take(fwd_down_split(c) ? 2 * R * (size_t)c->d * 4 : 0);   // fp32 K-slice partials
     L.total = o;
     return L;
@@ -199,15 +209,18 @@ int64_t moe_max_rows(const moe_config* cfg) {
     return max_rows(cfg);
 }
 
-moe_status moe_workspace_size(const moe_config* cfg, int dispatch_only, size_t* bytes) {
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
     CHECK(check_cfg(cfg));
     if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-    if (dispatch_only) {
-        *bytes = moe::dispatch_workspace_bytes(
-            moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout));
-    } else {
-        *bytes = fwd_layout(cfg).total;
-    }
+    *bytes = fwd_layout(cfg).total;
+    return MOE_OK;
+}
+
+moe_status moe_dispatch_workspace_size(const moe_config* cfg, size_t* bytes) {
+    CHECK(check_cfg(cfg));
+    if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = moe::dispatch_workspace_bytes(
+        moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout));
     return MOE_OK;
 }
 
@@ -449,10 +462,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     hipError_t e = moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T,
                                      cfg->d, cfg->E, cfg->k, cfg->temperature, cfg->renormalize, s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
-    // bf16: the gate/up GEMM gathers its rows of x through token_of_row, so
-    // x_perm is never written (its 32-bit byte offsets must span x)
-    const bool gather = cfg->dtype == MOE_BF16 && cfg->layout == MOE_LAYOUT_COMPACT &&
-                        T * d * es < ((size_t)1 << 32);
+    const bool gather = fwd_gather(cfg);   // no x_perm: see fwd_gather
     const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout);
     e = moe::launch_dispatch(p, cfg->dtype, idx, x, w + L.x_perm, count, offset, row_of, tor,
                              w + L.dsp, cfg->d, s, !gather);

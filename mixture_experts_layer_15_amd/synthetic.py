@@ -15,8 +15,8 @@ independently and large tensors never need a full-size fp32 temporary):
   for the backward)
 * router bias: none (zero-initialised gate bias, TorchTitan 1K-GPU article
   section 4.2), except for the skewed-routing case, where b_e is the fp32
-  rounding of ln p_e with p_e = (e+1)^-s / sum_i i^-s (a Zipf(s) prior over
-  experts, expert 0 the most popular).
+  rounding of a * ln p_e with p_e = (e+1)^-s / sum_i i^-s (a Zipf(s) prior
+  over experts, expert 0 the most popular) and a the config's zipf_scale.
 
 Normals are fp32 draws from torch's generator on the chosen device, scaled by
 fp32(1/sqrt(fan_in)) and rounded to nearest-even into bf16 for bf16 layers.
@@ -54,11 +54,12 @@ def _normal(shape, std: float, dt: torch.dtype, device: str, seed: int,
     return v.to(dt)
 
 
-def zipf_bias(E: int, s: float) -> torch.Tensor:
-    """fp32 ln of a Zipf(s) prior over E experts (expert 0 most popular)."""
+def zipf_bias(E: int, s: float, scale: float = 1.0) -> torch.Tensor:
+    """fp32 of scale * ln p_e for a Zipf(s) prior p over E experts (expert 0
+    most popular)."""
     w = [(e + 1) ** (-s) for e in range(E)]
     h = math.fsum(w)
-    return torch.tensor([math.log(v / h) for v in w], dtype=torch.float32)
+    return torch.tensor([scale * math.log(v / h) for v in w], dtype=torch.float32)
 
 
 def make_inputs(cfg: MoEConfig, seed: int = 0, device: str = "cpu",
@@ -76,7 +77,8 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, device: str = "cpu",
     out: Dict[str, Optional[torch.Tensor]] = {}
     out["x"] = _normal((T, d), 1.0, dt, device, seed, "x", 0)
     out["w_router"] = _normal((d, E), 1.0 / math.sqrt(d), dt, device, seed, "w_router", 0)
-    out["bias"] = None if cfg.zipf_bias is None else zipf_bias(E, cfg.zipf_bias).to(device)
+    out["bias"] = None if cfg.zipf_bias is None else zipf_bias(E, cfg.zipf_bias,
+                                                                  cfg.zipf_scale).to(device)
     for name, shape, fan_in in (("w_gate", (d, F), d), ("w_up", (d, F), d),
                                 ("w_down", (F, d), F)):
         w = torch.empty((nE,) + shape, dtype=dt, device=device)

@@ -483,6 +483,48 @@ void orc_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t d_ff, int 
     free(dxa); free(dga); free(dl);
 }
 
+/* Router part of the backward on its own: dlogit [T][E] from the gate
+ * gradients dgate [T][k] (0 for a dropped assignment), the same formulas as
+ * in orc_backward: with p = softmax(l / tau),
+ *   renormalised gates gate_j = p_j / S: dp_j = (dgate_j - sum_j' dgate_j' gate_j') / S,
+ *   raw gates: dp_j = dgate_j; dp = 0 for experts not chosen;
+ *   dl_e = p_e (dp_e - sum_e' p_e' dp_e') / tau.
+ * One token per thread, every sum in ascending index order. */
+void orc_router_backward(int64_t T, int64_t E, int64_t k, double tau, int renorm,
+                         const double* logits, const int32_t* idx, const double* gate,
+                         const double* dgate, double* dl) {
+    #pragma omp parallel
+    {
+        double* dq = (double*)malloc(sizeof(double) * (size_t)E);   /* dL/dp */
+        double* q = (double*)malloc(sizeof(double) * (size_t)E);    /* p */
+        #pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const double* lt = logits + t * E;
+            const int32_t* it = idx + t * k;
+            double mx = lt[0];
+            for (int64_t e = 1; e < E; ++e) if (lt[e] > mx) mx = lt[e];
+            double zs = 0.0;
+            for (int64_t e = 0; e < E; ++e) {
+                q[e] = exp((lt[e] - mx) / tau);
+                zs += q[e];
+            }
+            for (int64_t e = 0; e < E; ++e) { q[e] = q[e] / zs; dq[e] = 0.0; }
+            if (renorm) {
+                double S = 0.0, dot = 0.0;
+                for (int64_t j = 0; j < k; ++j) S += q[it[j]];
+                for (int64_t j = 0; j < k; ++j) dot += dgate[t * k + j] * gate[t * k + j];
+                for (int64_t j = 0; j < k; ++j) dq[it[j]] = (dgate[t * k + j] - dot) / S;
+            } else {
+                for (int64_t j = 0; j < k; ++j) dq[it[j]] = dgate[t * k + j];
+            }
+            double qd = 0.0;
+            for (int64_t e = 0; e < E; ++e) qd += q[e] * dq[e];
+            for (int64_t e = 0; e < E; ++e) dl[t * E + e] = q[e] * (dq[e] - qd) / tau;
+        }
+        free(dq); free(q);
+    }
+}
+
 /* Single entries of the expert weight gradients, each summed straight from
  * its definition over the kept assignments (t, j) of expert e, tokens
  * ascending (same quantities as in orc_backward):

@@ -81,6 +81,9 @@ def _declare(lib):
     lib.orc_ffn_rows.restype = None
     lib.orc_combine.argtypes = [_I64, _P, _I64, _I64, _P, _P, _P, _P]
     lib.orc_combine.restype = None
+    lib.orc_router_backward.argtypes = [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int,
+                                        _P, _P, _P, _P, _P]
+    lib.orc_router_backward.restype = None
     return lib
 
 
@@ -276,6 +279,20 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, dy, *, k: int, tau: float,
                          _ptr(out["dgate"]))
     out.update(logits=lg, idx=idx, gate=gate, row_of=row_of, C=C)
     return out
+
+
+def router_backward(logits_, idx, gate, dgate, tau: float, renormalize: bool) -> np.ndarray:
+    """dlogit [T, E] from the gate gradients dgate [T, k] (0 where dropped):
+    through the renormalised (or raw) gates and the temperature softmax."""
+    lg = np.ascontiguousarray(logits_, dtype=np.float64)
+    T, E = lg.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    k = idx.shape[1]
+    dl = np.empty((T, E), dtype=np.float64)
+    _load().orc_router_backward(T, E, k, float(tau), int(bool(renormalize)), _ptr(lg), _ptr(idx),
+                                _ptr(np.ascontiguousarray(gate, dtype=np.float64)),
+                                _ptr(np.ascontiguousarray(dgate, dtype=np.float64)), _ptr(dl))
+    return dl
 
 
 WGRAD = {"dw_gate": 0, "dw_up": 1, "dw_down": 2}

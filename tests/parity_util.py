@@ -11,6 +11,7 @@ import torch
 
 import mixture_experts_layer_15_amd as moe
 from mixture_experts_layer_15_amd import synthetic
+from oracle import by_expert
 from oracle import oracle as orc
 
 U32 = 2.0 ** -24          # unit roundoff of fp32
@@ -46,21 +47,27 @@ def rel_err(got, want) -> float:
     return diff / scale
 
 
-def check_logits(logits_gpu, x_host, wr_host, bias_host, tokens):
+def check_logits(logits_gpu, x_host, wr_host, bias_host, tokens, chunk=8192):
     """GPU fp32 logits against the oracle's fp64 logits within the fp32
     summation bound |l - l*| <= 2 g_K sum_i |x_i w_i| + 2u |l*| (+ bias term),
-    g_K = K u / (1 - K u) (the factor 2 covers the MFMA's internal order)."""
-    xs = x_host[tokens]
-    want = orc.logits(xs, wr_host, bias_host)
+    g_K = K u / (1 - K u) (the factor 2 covers the MFMA's internal order).
+    Returns the oracle's fp64 logits of the listed tokens."""
+    tokens = np.asarray(tokens)
     K = x_host.shape[1]
     gk = K * U32 / (1 - K * U32)
-    ax = np.abs(xs.double().numpy())
     aw = np.abs(wr_host.double().numpy())
-    bound = 2 * gk * (ax @ aw) + 2 * U32 * np.abs(want) + 1e-30
-    got = logits_gpu[tokens].double().numpy()
-    over = np.abs(got - want) > bound
-    assert not over.any(), f"logits outside the fp32 bound at {np.argwhere(over)[:5]}"
-    return float((np.abs(got - want) / np.maximum(np.abs(want), 1e-30)).max())
+    wants = []
+    for c0 in range(0, tokens.size, chunk):
+        tk = tokens[c0:c0 + chunk]
+        xs = x_host[torch.from_numpy(tk)]
+        want = orc.logits(xs, wr_host, bias_host)
+        ax = np.abs(xs.double().numpy())
+        bound = 2 * gk * (ax @ aw) + 2 * U32 * np.abs(want) + 1e-30
+        got = logits_gpu[torch.from_numpy(tk)].double().numpy()
+        over = np.abs(got - want) > bound
+        assert not over.any(), f"logits outside the fp32 bound at tokens {tk[np.argwhere(over)[:5, 0]]}"
+        wants.append(want)
+    return np.concatenate(wants) if wants else np.zeros((0, wr_host.shape[1]))
 
 
 def check_route(cfg, logits_gpu, idx_gpu, gate_gpu):
@@ -162,3 +169,48 @@ def bf16_ulp_distance(a, b) -> int:
         return 0
     return int((key(a) - key(b)).abs().max().item())
 
+
+
+class MaxRel:
+    """Running max |got - want| and max |want| over blocks of one output, for
+    the R13 measure max |got - want| / max |want| over the whole output."""
+
+    def __init__(self):
+        self.diff = 0.0
+        self.scale = 0.0
+        self.count = 0
+
+    def add(self, got, want):
+        got = np.asarray(got, dtype=np.float64)
+        want = np.asarray(want, dtype=np.float64)
+        if want.size:
+            assert np.isfinite(got).all(), "non-finite values (an unwritten element?)"
+            self.diff = max(self.diff, float(np.abs(got - want).max()))
+            self.scale = max(self.scale, float(np.abs(want).max()))
+            self.count += want.shape[0]
+
+    def value(self) -> float:
+        if self.scale == 0.0:
+            return 0.0 if self.diff == 0.0 else math.inf
+        return self.diff / self.scale
+
+
+def check_ffn_and_combine_by_expert(cfg, host, od, ogate, h, y_perm, label, chunk=8192):
+    """Every row of h and y_perm, and the fp64 layer output y* of every token,
+    from the by-expert oracle (fp64 matrix products per expert block) on the
+    oracle's routing (ogate: its fp64 gates) and dispatch od.  Returns y*."""
+    mh, mo = MaxRel(), MaxRel()
+    n = od["n_kept"]
+
+    def on_block(e, r0, r1, hb, ob):
+        mh.add(to_np(h[r0:r1]), hb)
+        mo.add(to_np(y_perm[r0:r1]), ob)
+
+    ystar = by_expert.forward_full(host["x"], host["w_gate"], host["w_up"], host["w_down"],
+                                   od["offset"], od["token_of_row"], od["row_of"], ogate,
+                                   cfg.T, chunk=chunk, on_block=on_block)
+    assert mh.count == n and mo.count == n
+    eh, eo = mh.value(), mo.value()
+    say(f"[{label}] h err {eh:.3g}  y_perm err {eo:.3g} over all {n} rows")
+    assert eh <= TOL_Y[cfg.dtype] and eo <= TOL_Y[cfg.dtype]
+    return ystar

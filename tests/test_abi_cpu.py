@@ -42,10 +42,17 @@ def test_every_declared_symbol_is_exported(L):
     assert set(decl) <= syms
 
 
-def test_status_strings(L):
-    assert L.moe_status_string(0) == b"MOE_OK"
-    assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+def test_status_codes_and_strings(L):
+    # the status values the header declares: 0 for success, negative errors
+    text = open(HEADER).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"\b(MOE_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", text))
+    assert codes == {"MOE_OK": 0, "MOE_ERR_INVALID_ARG": -1, "MOE_ERR_UNSUPPORTED": -2,
+                     "MOE_ERR_WORKSPACE": -3, "MOE_ERR_HIP": -4}
+    for name, v in codes.items():
+        assert getattr(moe, name) == v
+        assert L.moe_status_string(v) == name.encode()
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+    assert L.moe_status_string(3) == b"MOE_ERR_UNKNOWN"
 
 
 @pytest.mark.parametrize("ci", range(len(configs.CONFIGS)))
@@ -85,7 +92,9 @@ def test_invalid_config_rejected_on_host(L, kw, word):
     c = moe.cconfig(cfg)
     assert L.moe_capacity(ctypes.byref(c)) == -1
     n = ctypes.c_size_t(0)
-    assert L.moe_workspace_size(ctypes.byref(c), 0, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_workspace_size(ctypes.byref(c), ctypes.byref(n)) == \
+        moe.MOE_ERR_INVALID_ARG
     fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
     st = L.moe_route(ctypes.byref(c), fake, fake, None, fake, fake, fake, None)
     assert st == moe.MOE_ERR_INVALID_ARG
@@ -99,8 +108,11 @@ def test_bad_flags_and_dtype(L):
     c = moe.cconfig(configs.get("tiny"))
     c.dtype = 7
     n = ctypes.c_size_t(0)
-    assert L.moe_workspace_size(ctypes.byref(c), 1, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_workspace_size(None, 1, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_workspace_size(ctypes.byref(c), ctypes.byref(n)) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_size(None, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_workspace_size(None, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_null_and_misaligned_pointers_rejected(L):
@@ -167,21 +179,46 @@ def test_choice_order_workspace_is_sized_for_the_walked_choices(L):
             want(cfg.T * cfg.k, cfg.E)
 
 
-def test_forward_workspace_holds_the_split_down_partials(L):
-    # moe_forward's workspace: dispatch tables and the intermediates, plus two
-    # fp32 partial products [2][R][d] when a bf16 top-1 layer that keeps every
-    # token runs its down GEMM in two K slices (the ZAYA1-like layer: 16
-    # experts give 128 down tiles of 320 x 256, too few for 256 CUs); a top-2
-    # layer never does.  Host-only: sizes, no GPU call.
-    z = configs.get("zaya1")
-    R, d = moe.max_rows(z), z.d
-    parts = 2 * R * d * 4
-    base = z.T * z.E * 4 + R * (2 * d + z.d_ff) * 2   # logits, x_perm, h, y_perm
-    assert moe.workspace_bytes(z) >= base + parts
-    two = z.scaled(k=2, renormalize=True)
-    R2 = moe.max_rows(two)
-    assert moe.workspace_bytes(two) < two.T * two.E * 4 + R2 * (2 * d + two.d_ff) * 2 + \
-        2 * R2 * d * 4
+def _al(v):
+    return (v + 255) // 256 * 256
+
+
+def _fwd_ws_want(cfg, x_perm: bool, y_perm: bool, parts: bool):
+    """moe_forward's workspace, region by region (each 256-byte aligned):
+    logits, topk idx and gate, counts, offsets, row_of, token_of_row, the
+    dispatch tables, then x_perm / h / y_perm / fp32 K-slice partials."""
+    R, d, F, E, T, k = moe.max_rows(cfg), cfg.d, cfg.d_ff, cfg.E, cfg.T, cfg.k
+    es = 2 if cfg.dtype == "bf16" else 4
+    tor = max(T * k, R)
+    fixed = _al(T * E * 4) + 2 * _al(T * k * 4) + _al(E * 4) + _al((E + 1) * 4) + \
+        _al(T * k * 4) + _al(tor * 4) + _al(moe.workspace_bytes(cfg, dispatch_only=True))
+    return fixed + _al(R * d * es if x_perm else 0) + _al(R * F * es) + \
+        _al(R * d * es if y_perm else 0) + _al(2 * R * d * 4 if parts else 0)
+
+
+def test_forward_workspace_holds_only_the_buffers_the_path_uses(L):
+    # bf16 compact layers gather x rows inside the gate/up GEMM (no x_perm);
+    # bf16 top-1 layers that keep every token have the down GEMM write y (no
+    # y_perm), and with too few experts to fill the CUs with down tiles (the
+    # ZAYA1-like layer: 16 experts, 128 tiles of 320 x 256) the down GEMM runs
+    # in two K slices whose fp32 partials [2][R][d] live in the workspace.
+    # Host-only: sizes, no GPU call.
+    assert moe.workspace_bytes(configs.get("zaya1")) == \
+        _fwd_ws_want(configs.get("zaya1"), x_perm=False, y_perm=False, parts=True)
+    for name in ("wide", "skewed", "longseq"):
+        cfg = configs.get(name)
+        assert moe.workspace_bytes(cfg) == _fwd_ws_want(cfg, x_perm=False, y_perm=True,
+                                                       parts=False), name
+    # fp32: the staged buffers all present
+    tiny = configs.get("tiny")
+    assert moe.workspace_bytes(tiny) == _fwd_ws_want(tiny, x_perm=True, y_perm=True, parts=False)
+    # the padded layout scatters x into x_perm
+    pad = configs.get("wide").scaled(layout=1)
+    assert moe.workspace_bytes(pad) == _fwd_ws_want(pad, x_perm=True, y_perm=True, parts=False)
+    # top-1 with drops: y_perm and a combine
+    capped = configs.get("zaya1").scaled(cap_num=1, cap_den=1)
+    assert moe.workspace_bytes(capped) == _fwd_ws_want(capped, x_perm=False, y_perm=True,
+                                                       parts=False)
 
 
 def test_workspace_too_small_rejected(L):
@@ -202,7 +239,7 @@ def test_workspace_sizes_cover_intermediates(L):
     for cfg in configs.CONFIGS:
         R = moe.max_rows(cfg)
         es = 2 if cfg.dtype == "bf16" else 4
-        inter = R * (2 * cfg.d + cfg.d_ff) * es + cfg.T * (cfg.E + 4 * cfg.k) * 4
+        inter = R * cfg.d_ff * es + cfg.T * (cfg.E + 4 * cfg.k) * 4
         assert moe.workspace_bytes(cfg) >= inter
         assert 0 < moe.workspace_bytes(cfg, dispatch_only=True) <= 2 * 256 * cfg.E * 4
 
@@ -262,7 +299,7 @@ def test_padded_layout_validation_and_sizes(L):
     assert L.moe_max_rows(ctypes.byref(bad)) == -1
     assert b"moe_layout" in L.moe_last_error()
     nocap = moe.cconfig(configs.get("zaya1").scaled(layout=1))
-    assert L.moe_workspace_size(ctypes.byref(nocap), 0, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_size(ctypes.byref(nocap), ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
     assert b"capacity limit" in L.moe_last_error()
     huge = moe.cconfig(configs.get("wide").scaled(T=(1 << 28) - 1, E=256, k=8, layout=1))
     assert L.moe_max_rows(ctypes.byref(huge)) == -1 and b"2^31" in L.moe_last_error()

@@ -11,20 +11,24 @@ intermediates that feed a further product (g, u, dg, du, gate h) are rounded
 once to bf16, a relative 2^-9 per element; summed with random signs that
 stays near 2^-9 of the result's scale.
 
-Small layers compare every output; the full-size layers compare dx and dgate
-of sampled tokens, sampled entries of the expert weight gradients (each summed
-by the oracle from its definition), and the router gradients through a
-property that holds at any size (the softmax backward sums to zero over the
-experts of each token)."""
+Small layers compare every output against the row-by-row C oracle; the
+ZAYA1-like and skewed layers at full size compare every output against the
+by-expert oracle (fp64 matrix products per expert, pinned to the C oracle);
+the wide and long-sequence layers compare dx and dgate of sampled tokens,
+sampled entries of the expert weight gradients (each summed by the oracle from
+its definition), and the router gradients through a property that holds at
+any size (the softmax backward sums to zero over the experts of each token).
+Every gradient buffer starts as NaN, so an unwritten element fails."""
 import numpy as np
 import pytest
 import torch
 
 import mixture_experts_layer_15_amd as moe
 from mixture_experts_layer_15_amd import configs, synthetic
+from oracle import by_expert
 from oracle import oracle as orc
 
-from parity_util import check_route, gpu_inputs, rel_err, say, to_np
+from parity_util import MaxRel, check_route, gpu_inputs, rel_err, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -143,7 +147,40 @@ def _sample_tokens(cfg, row_of, rng, n=24):
     return np.unique(pick)
 
 
-@pytest.mark.parametrize("name", ["zaya1", "skewed", "wide", "longseq"])
+@pytest.mark.parametrize("name", ["zaya1", "skewed"])
+def test_backward_full_size_every_gradient(name):
+    cfg = configs.get(name)
+    dev, host = gpu_inputs(cfg, seed=0)
+    dy = synthetic.make_dy(cfg, seed=0, device="cuda")
+    dy_h = dy.cpu()
+    lg, idx, gate, g = _gpu_backward(cfg, dev, dy)
+    oidx, ogate, _ = check_route(cfg, lg, idx, gate)
+    C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    od = orc.dispatch(oidx, cfg.E, C, cfg.drop_policy)
+    errs = {n: MaxRel() for n in ("dw_gate", "dw_up", "dw_down")}
+
+    def on_expert(e, grads):
+        for n, want in grads.items():
+            errs[n].add(g[n][e].double().cpu().numpy(), want)
+
+    say(f"[{name}] by-expert oracle backward over {od['n_kept']} rows")
+    ob = by_expert.backward(host["x"], host["w_router"], host["w_gate"], host["w_up"],
+                            host["w_down"], dy_h, logits=lg.double().numpy(), idx=oidx,
+                            gate=ogate, row_of=od["row_of"], offset=od["offset"],
+                            token_of_row=od["token_of_row"],
+                            tau=float(np.float32(cfg.temperature)),
+                            renormalize=cfg.renormalize, on_expert=on_expert)
+    for n in ("dx", "dgate", "dw_router", "dbias"):
+        err = rel_err(to_np(g[n]), ob[n])
+        say(f"[{name}] {n} err {err:.3g} (max |oracle| {np.abs(ob[n]).max():.3g})")
+        assert err <= TOL, f"{n}: {err}"
+    for n, m in errs.items():
+        say(f"[{name}] {n} err {m.value():.3g} over {m.count} rows of {cfg.E} experts")
+        assert m.count == cfg.E * (cfg.d_ff if n == "dw_down" else cfg.d)
+        assert m.value() <= TOL, f"{n}: {m.value()}"
+
+
+@pytest.mark.parametrize("name", ["wide", "longseq"])
 def test_backward_full_size_sampled(name):
     cfg = configs.get(name)
     dev, host = gpu_inputs(cfg, seed=0)

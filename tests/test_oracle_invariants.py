@@ -71,6 +71,19 @@ def test_zipf_bias_values_and_skew():
     assert abs(H - 3.418596) < 1e-6
     np.testing.assert_allclose(np.exp(b).sum(), 1.0, rtol=1e-6)
     assert abs(b[0] - (-1.22923)) < 1e-5 and np.all(np.diff(b) < 0)
+    np.testing.assert_allclose(synthetic.zipf_bias(64, 1.2, 0.4).double().numpy(), 0.4 * b,
+                               rtol=1e-6)
+
+
+def test_skewed_layer_sends_about_thirty_percent_of_tokens_to_expert_zero():
+    # the skewed layer's bias scale is fitted so that ~30% of the tokens have
+    # expert 0 among their top-2 choices (real token count and width)
+    cfg = configs.get("skewed")
+    inp = synthetic.make_inputs(cfg, seed=0, experts=1)
+    lg = orc.logits(inp["x"], inp["w_router"], inp["bias"])
+    idx, _ = orc.route(lg, cfg.k, float(np.float32(cfg.temperature)), cfg.renormalize)
+    share = (idx == 0).any(1).mean()
+    assert 0.28 <= share <= 0.32, share
 
 
 def test_whole_tiny_layer_invariants():

@@ -14,7 +14,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-        os.path.join(ROOT, "tests", "test_oracle_backward.py")]
+        os.path.join(ROOT, "tests", "test_oracle_backward.py"),
+        os.path.join(ROOT, "tests", "test_oracle_by_expert.py")]
 
 MUTANTS = {
     "bias dropped": ("if (bias) s += (double)bias[e];", "if (0) s += (double)bias[e];"),
@@ -75,6 +76,11 @@ MUTANTS = {
         "acc += gate[s] * (act * u) * dy[t * d + b];", "acc += (act * u) * dy[t * d + b];"),
     "single-entry gate gradient with GELU for its derivative": (
         "xa * dh * u * gelu_grad(g)", "xa * dh * u * gelu(g)"),
+    "router backward without the temperature": (
+        "dl[t * E + e] = q[e] * (dq[e] - qd) / tau;", "dl[t * E + e] = q[e] * (dq[e] - qd);"),
+    "router backward renormalisation without the shared term": (
+        "dq[it[j]] = (dgate[t * k + j] - dot) / S;", "dq[it[j]] = dgate[t * k + j] / S;"),
+    "router backward softmax unnormalised": ("q[e] = q[e] / zs;", "q[e] = q[e];"),
 }
 
 
