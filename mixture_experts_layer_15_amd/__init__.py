@@ -28,7 +28,9 @@ EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_dispatch_w
            "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
            "moe_forward", "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",
-           "moe_backward_workspace_size", "moe_backward")
+           "moe_backward_workspace_size", "moe_backward",
+           # measurement probes (include/moe_probe.h)
+           "moe_probe_copy", "moe_probe_read", "moe_probe_mfma")
 
 
 class CConfig(ctypes.Structure):
@@ -95,10 +97,13 @@ def lib() -> ctypes.CDLL:
         L.moe_route_mlp.argtypes = [cp, rp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_backward_workspace_size.argtypes = [cp, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_backward.argtypes = [cp] + [_P] * 15 + [ctypes.c_size_t, _P]
-        for n in ("moe_route", "moe_route_from_logits", "moe_dispatch", "moe_expert_ffn",
+        for n in ("moe_route", "moe_route_from_logits", "moe_dispatch",
+                  "moe_expert_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
                   "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",
-                  "moe_backward_workspace_size", "moe_backward"):
+                  "moe_backward_workspace_size", "moe_backward",
+           # measurement probes (include/moe_probe.h)
+           "moe_probe_copy", "moe_probe_read", "moe_probe_mfma"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -16,9 +16,13 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    """Every function the headers under include/ declare."""
+    import glob
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -316,3 +320,11 @@ def test_padded_layout_validation_and_sizes(L):
     # on the host (it is a device pointer), but the binding sizes it that way
     cfg = configs.get("skewed").scaled(layout=1)
     assert max(cfg.T * cfg.k, moe.max_rows(cfg)) == moe.max_rows(cfg)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
