@@ -230,6 +230,23 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const vo
                         int32_t* row_of, int32_t* token_of_row, void* workspace,
                         size_t ws_bytes, void* stream);
 
+/* moe_dispatch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels, results bit-identical to moe_dispatch's, with its
+ * workspace (the per-block expert-count tables, at most 2 * 256 * E int32)
+ * in a static device buffer of the library instead of a caller's buffer.
+ * That buffer, MOE_DISPATCH_SCRATCH_BYTES (512 KiB) per device, is held until
+ * the process ends; a config whose tables need more is rejected with
+ * MOE_ERR_INVALID_ARG (no valid config does: blocks <= 256, E <= 256).
+ * Nothing here allocates: no hipMalloc, no hipFree.  Every call on one device
+ * shares that device's buffer and leaves its contents behind (no call relies
+ * on them), so calls that overlap on one device race; calls must be ordered
+ * (e.g. on one stream).  Arguments and results as for moe_dispatch. */
+#define MOE_DISPATCH_SCRATCH_BYTES (512u * 1024u)
+moe_status moe_dispatch_noalloc(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                                void* x_perm, int32_t* expert_count, int32_t* expert_offset,
+                                int32_t* row_of, int32_t* token_of_row, void* stream);
+
 /* Expert-load telemetry from the per-expert assignment counts before drops
  * (expert_count as written by moe_dispatch).  The ZAYA1 page keeps the expert
  * load balance within +-5% (section 3.2) and monitors it during training; the

@@ -26,6 +26,7 @@ MOE_LAYOUT_COMPACT, MOE_LAYOUT_PADDED = 0, 1
 EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_dispatch_workspace_size",
            "moe_status_string",
            "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
+           "moe_dispatch_noalloc",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
            "moe_forward", "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",
            "moe_backward_workspace_size", "moe_backward",
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P]
         L.moe_route_from_logits.argtypes = [cp, _P, _P, _P, _P]
         L.moe_dispatch.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_dispatch_noalloc.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_expert_ffn.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_expert_gate_up.argtypes = [cp, _P, _P, _P, _P, _P, _P]
         L.moe_expert_down.argtypes = [cp, _P, _P, _P, _P, _P]
@@ -97,7 +99,7 @@ def lib() -> ctypes.CDLL:
         L.moe_route_mlp.argtypes = [cp, rp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_backward_workspace_size.argtypes = [cp, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_backward.argtypes = [cp] + [_P] * 15 + [ctypes.c_size_t, _P]
-        for n in ("moe_route", "moe_route_from_logits", "moe_dispatch",
+        for n in ("moe_route", "moe_route_from_logits", "moe_dispatch", "moe_dispatch_noalloc",
                   "moe_expert_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
                   "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",

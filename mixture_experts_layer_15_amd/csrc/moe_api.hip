@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstdarg>
+#include <mutex>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -291,6 +292,73 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const vo
                                         expert_offset, row_of, token_of_row, workspace, cfg->d,
                                         (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_dispatch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// moe_dispatch_noalloc's workspace: a static device buffer, one copy per
+// device.  Host code never uses the array's name as an address: its device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[MOE_DISPATCH_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+moe_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "moe_dispatch_noalloc/hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the %d the static buffer serves", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                            "moe_dispatch_noalloc/hipGetSymbolAddress");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_dispatch_noalloc(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                                void* x_perm, int32_t* expert_count, int32_t* expert_offset,
+                                int32_t* row_of, int32_t* token_of_row, void* stream) {
+    CHECK(check_cfg(cfg));
+    SIZES(cfg);
+    CHECK(check_ptr(topk_idx, "topk_idx", T * k * 4));
+    CHECK(check_ptr(x, "x", T * d * es));
+    CHECK(check_ptr(x_perm, "x_perm", R * d * es));
+    if (expert_count == nullptr || expert_offset == nullptr)
+        return fail(MOE_ERR_INVALID_ARG, "expert_count / expert_offset is NULL");
+    CHECK(check_ptr(expert_count, "expert_count", E * 4));
+    CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
+    CHECK(check_ptr(row_of, "row_of", T * k * 4));
+    CHECK(check_ptr(token_of_row, "token_of_row", (size_t)tor_len(cfg) * 4));
+    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg),
+                                                   cfg->drop_policy, cfg->layout);
+    const size_t need = moe::dispatch_workspace_bytes(p);
+    if (need > MOE_DISPATCH_SCRATCH_BYTES)
+        return fail(MOE_ERR_INVALID_ARG,
+                    "dispatch tables need %zu bytes, more than the %u of the static buffer", need,
+                    (unsigned)MOE_DISPATCH_SCRATCH_BYTES);
+    void* ws = nullptr;
+    CHECK(scratch_for_current_device(&ws));
+    hipError_t e = moe::launch_dispatch(p, cfg->dtype, topk_idx, x, x_perm, expert_count,
+                                        expert_offset, row_of, token_of_row, ws, cfg->d,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_dispatch_noalloc");
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offset,
