@@ -186,6 +186,71 @@ void orc_route(int64_t T, int64_t E, int64_t k, double tau, int renorm,
     }
 }
 
+/* Variant of step 2 -- a dynamic number of experts per token: the TorchTitan
+ * 1K-GPU article (section 2.1) has each token activate 2-4 experts, with no
+ * rule for the count.  Reading taken (cumulative-probability, or "top-p",
+ * routing): the experts are ranked as in orc_route; with p = softmax(l / tau)
+ * over all E experts, token t takes the k_t highest-ranked experts, k_t the
+ * smallest j in [kmin, kmax] whose j largest p sum to at least theta (kmax
+ * when none does).  Gates: p of the k_t chosen experts, divided by their sum
+ * when renorm.  Slots j >= k_t hold idx -1 and gate 0 (no assignment). */
+void orc_route_dynamic(int64_t T, int64_t E, int64_t kmax, int64_t kmin, double theta,
+                       double tau, int renorm, const double* logits, int32_t* idx,
+                       double* gate) {
+    #pragma omp parallel
+    {
+        char* taken = (char*)calloc((size_t)E, 1);
+        double* p = (double*)malloc(sizeof(double) * (size_t)E);
+        #pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const double* l = logits + t * E;
+            int32_t* it = idx + t * kmax;
+            double* gt = gate + t * kmax;
+            memset(taken, 0, (size_t)E);
+            for (int64_t j = 0; j < kmax; ++j) {           /* the kmax best, in rank order */
+                int64_t best = -1;
+                for (int64_t e = 0; e < E; ++e)
+                    if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+                taken[best] = 1;
+                it[j] = (int32_t)best;
+            }
+            double mx = l[0];
+            for (int64_t e = 1; e < E; ++e) if (l[e] > mx) mx = l[e];
+            double z = 0.0;
+            for (int64_t e = 0; e < E; ++e) { p[e] = exp((l[e] - mx) / tau); z += p[e]; }
+            for (int64_t e = 0; e < E; ++e) p[e] /= z;
+            int64_t kt = kmax;                             /* how many this token takes */
+            double mass = 0.0;
+            for (int64_t j = 0; j < kmax; ++j) {
+                mass += p[it[j]];
+                if (j + 1 >= kmin && mass >= theta) { kt = j + 1; break; }
+            }
+            double s = 0.0;
+            for (int64_t j = 0; j < kt; ++j) s += p[it[j]];
+            for (int64_t j = 0; j < kmax; ++j) {
+                if (j < kt) {
+                    gt[j] = renorm ? p[it[j]] / s : p[it[j]];
+                } else {
+                    it[j] = -1;
+                    gt[j] = 0.0;
+                }
+            }
+        }
+        free(taken);
+        free(p);
+    }
+}
+
+/* Capacity of a layer whose tokens take a varying number of experts: the
+ * capacity factor scales the realised mean load, C = ceil(cap_num * A /
+ * (cap_den * E)) for A assignments in the batch (exact integers); no limit
+ * (cap_den == 0) gives C = T. */
+int64_t orc_capacity_realised(int64_t A, int64_t T, int64_t E, int64_t cap_num, int64_t cap_den) {
+    if (cap_den == 0) return T;
+    int64_t num = cap_num * A, den = cap_den * E;
+    return num / den + (num % den != 0);
+}
+
 /* Step 3 -- expert capacity C = ceil(cap_num * k * T / (cap_den * E)),
  * exact integer arithmetic; cap_den == 0 means no limit, C = T (a token picks
  * an expert at most once, so no expert can receive more than T). */
@@ -218,10 +283,13 @@ void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C, const int32_t* idx
                   int32_t* count, int32_t* kept, int32_t* offset, int32_t* pos,
                   int32_t* row_of, int32_t* token_of_row, int policy, int layout) {
     for (int64_t e = 0; e < E; ++e) count[e] = 0;
+    /* a slot with idx -1 (dynamic routing: the token took fewer experts) is
+     * no assignment: it gets pos -1 and row -1 */
     if (policy == 0) {
         for (int64_t t = 0; t < T; ++t)
             for (int64_t j = 0; j < k; ++j) {
                 int32_t e = idx[t * k + j];
+                if (e < 0) { pos[t * k + j] = -1; continue; }
                 pos[t * k + j] = count[e];
                 count[e] += 1;
             }
@@ -229,6 +297,7 @@ void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C, const int32_t* idx
         for (int64_t j = 0; j < k; ++j)
             for (int64_t t = 0; t < T; ++t) {
                 int32_t e = idx[t * k + j];
+                if (e < 0) { pos[t * k + j] = -1; continue; }
                 pos[t * k + j] = count[e];
                 count[e] += 1;
             }
@@ -241,7 +310,7 @@ void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C, const int32_t* idx
     for (int64_t t = 0; t < T; ++t)
         for (int64_t j = 0; j < k; ++j) {
             int64_t a = t * k + j;
-            if (pos[a] < C) {
+            if (pos[a] >= 0 && pos[a] < C) {
                 int32_t row = offset[idx[a]] + pos[a];
                 row_of[a] = row;
                 token_of_row[row] = (int32_t)t;

@@ -84,6 +84,11 @@ def _declare(lib):
     lib.orc_router_backward.argtypes = [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int,
                                         _P, _P, _P, _P, _P]
     lib.orc_router_backward.restype = None
+    lib.orc_route_dynamic.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_double, ctypes.c_double,
+                                      ctypes.c_int, _P, _P, _P]
+    lib.orc_route_dynamic.restype = None
+    lib.orc_capacity_realised.argtypes = [_I64, _I64, _I64, _I64, _I64]
+    lib.orc_capacity_realised.restype = _I64
     return lib
 
 
@@ -126,18 +131,34 @@ def logits(x, w_router, bias=None) -> np.ndarray:
     return out
 
 
-def route(logits_, k: int, tau: float, renormalize: bool):
-    """Top-k experts (logit descending, lower index on ties) and fp64 gates."""
+def route(logits_, k: int, tau: float, renormalize: bool, k_min: int = 0,
+          threshold: float = 0.0):
+    """Top-k experts (logit descending, lower index on ties) and fp64 gates.
+    threshold > 0: dynamic count per token (k_min .. k experts, the fewest
+    whose softmax mass reaches threshold); unused slots hold -1 and gate 0."""
     lg = np.ascontiguousarray(logits_, dtype=np.float64)
     T, E = lg.shape
     idx = np.empty((T, k), dtype=np.int32)
     gate = np.empty((T, k), dtype=np.float64)
-    _load().orc_route(T, E, k, float(tau), int(bool(renormalize)), _ptr(lg), _ptr(idx), _ptr(gate))
+    if threshold > 0:
+        _load().orc_route_dynamic(T, E, k, int(k_min), float(threshold), float(tau),
+                                  int(bool(renormalize)), _ptr(lg), _ptr(idx), _ptr(gate))
+    else:
+        _load().orc_route(T, E, k, float(tau), int(bool(renormalize)), _ptr(lg), _ptr(idx),
+                          _ptr(gate))
     return idx, gate
 
 
 def capacity(T: int, E: int, k: int, cap_num: int, cap_den: int) -> int:
     return int(_load().orc_capacity(T, E, k, cap_num, cap_den))
+
+
+def capacity_realised(idx: np.ndarray, E: int, cap_num: int, cap_den: int) -> int:
+    """Capacity of a dynamically routed batch: from the realised number of
+    assignments (slots of idx that are not -1)."""
+    idx = np.asarray(idx)
+    A = int((idx >= 0).sum())
+    return int(_load().orc_capacity_realised(A, idx.shape[0], E, cap_num, cap_den))
 
 
 def dispatch(idx: np.ndarray, E: int, C: int, policy: int = 0,
@@ -335,7 +356,8 @@ def load_stats(count: np.ndarray, C: int) -> np.ndarray:
 def forward(x, w_router, bias, w_gate, w_up, w_down, *, k: int, tau: float,
             renormalize: bool, cap_num: int, cap_den: int, drop_policy: int = 0,
             logits_in: Optional[np.ndarray] = None,
-            tokens: Optional[Sequence[int]] = None, want_h: bool = False) -> Dict:
+            tokens: Optional[Sequence[int]] = None, want_h: bool = False,
+            k_min: int = 0, threshold: float = 0.0) -> Dict:
     """The whole layer in fp64.
 
     ``logits_in`` replaces step 1 (routing then runs on exactly those values,
@@ -347,12 +369,13 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, *, k: int, tau: float,
     T = xr.shape[0]
     E = _raw(w_router)[0].shape[1]
     lg = logits(x, w_router, bias) if logits_in is None else np.asarray(logits_in, np.float64)
-    idx, gate = route(lg, k, tau, renormalize)
-    C = capacity(T, E, k, cap_num, cap_den)
+    idx, gate = route(lg, k, tau, renormalize, k_min, threshold)
+    C = capacity_realised(idx, E, cap_num, cap_den) if threshold > 0 else \
+        capacity(T, E, k, cap_num, cap_den)
     dsp = dispatch(idx, E, C, drop_policy)
     toks = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
     slot_tok = np.repeat(toks, k)
-    slot_ex = idx[toks].reshape(-1)
+    slot_ex = np.maximum(idx[toks].reshape(-1), 0)   # unused slots (-1) are never kept
     kept_mask = dsp["row_of"][toks].reshape(-1) >= 0
     d = xr.shape[1]
     d_ff = _raw(w_gate)[0].shape[2]

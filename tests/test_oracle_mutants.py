@@ -15,7 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
         os.path.join(ROOT, "tests", "test_oracle_backward.py"),
-        os.path.join(ROOT, "tests", "test_oracle_by_expert.py")]
+        os.path.join(ROOT, "tests", "test_oracle_by_expert.py"),
+        os.path.join(ROOT, "tests", "test_oracle_dynamic.py")]
 
 MUTANTS = {
     "bias dropped": ("if (bias) s += (double)bias[e];", "if (0) s += (double)bias[e];"),
@@ -28,7 +29,7 @@ MUTANTS = {
     "always renormalised": ("renorm ? p[idx[t * k + j]] / s : p[idx[t * k + j]]",
                             "p[idx[t * k + j]] / s"),
     "capacity floor": ("return (num + den - 1) / den;", "return num / den;"),
-    "keep one too many": ("if (pos[a] < C) {", "if (pos[a] <= C) {"),
+    "keep one too many": ("if (pos[a] >= 0 && pos[a] < C) {", "if (pos[a] >= 0 && pos[a] <= C) {"),
     "choice-major drops": (
         "for (int64_t t = 0; t < T; ++t)\n            for (int64_t j = 0; j < k; ++j) {\n"
         "                int32_t e = idx[t * k + j];",
@@ -81,6 +82,16 @@ MUTANTS = {
     "router backward renormalisation without the shared term": (
         "dq[it[j]] = (dgate[t * k + j] - dot) / S;", "dq[it[j]] = dgate[t * k + j] / S;"),
     "router backward softmax unnormalised": ("q[e] = q[e] / zs;", "q[e] = q[e];"),
+    "dynamic count: strict threshold": ("if (j + 1 >= kmin && mass >= theta)",
+                                        "if (j + 1 >= kmin && mass > theta)"),
+    "dynamic count: floor ignored": ("if (j + 1 >= kmin && mass >= theta)", "if (mass >= theta)"),
+    "dynamic count: gates renormalised over every slot": (
+        "for (int64_t j = 0; j < kt; ++j) s += p[it[j]];",
+        "for (int64_t j = 0; j < kmax; ++j) s += p[it[j]];"),
+    "dynamic count: unused slots keep their expert": ("it[j] = -1;", "(void)0;"),
+    "realised capacity floor": ("return num / den + (num % den != 0);", "return num / den;"),
+    "realised capacity from the token count": ("int64_t num = cap_num * A, den = cap_den * E;",
+                                               "int64_t num = cap_num * T, den = cap_den * E;"),
 }
 
 
