@@ -282,10 +282,14 @@ def cpu_baseline(cfg, host, idx_gpu, row_of_gpu, target_s):
     from oracle import oracle as orc
     kw = dict(k=cfg.k, tau=float(np.float32(cfg.temperature)), renormalize=cfg.renormalize,
               cap_num=cfg.cap_num, cap_den=cfg.cap_den)
+    dyn = dict(k_min=cfg.k_min, threshold=float(np.float32(cfg.route_threshold))) \
+        if cfg.route_threshold > 0 else {}
+    kw.update(dyn)
     t0 = time.perf_counter()
     lg = orc.logits(host["x"], host["w_router"], host["bias"])
-    idx, gate = orc.route(lg, cfg.k, kw["tau"], cfg.renormalize)
-    C = orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
+    idx, gate = orc.route(lg, cfg.k, kw["tau"], cfg.renormalize, **dyn)
+    C = orc.capacity_realised(idx, cfg.E, cfg.cap_num, cfg.cap_den) if dyn else \
+        orc.capacity(cfg.T, cfg.E, cfg.k, cfg.cap_num, cfg.cap_den)
     od = orc.dispatch(idx, cfg.E, C)
     t_route = time.perf_counter() - t0
     # probe the per-token FFN cost, then size the sample
@@ -415,7 +419,7 @@ def measure(cfg, args, headline: bool, clock=None):
     fused_ev = [a.elapsed_time(b) for a, b in fe]
 
     bwd_ms = None
-    if cfg.dtype == "bf16" and not args.no_backward:
+    if cfg.dtype == "bf16" and not args.no_backward and cfg.route_threshold == 0:
         dy = synthetic.make_dy(cfg, seed=1, device="cuda")
         bw = moe.Backward(cfg)
         bargs = (wr, bias, wg, wu, wd, dy)
@@ -496,6 +500,13 @@ def measure(cfg, args, headline: bool, clock=None):
     }
     if cfg.zipf_bias is not None:
         rec["expert0_token_share"] = round(float((idx_h == 0).any(1).mean()), 4)
+    if cfg.route_threshold > 0:
+        kt = (idx_h >= 0).sum(1)
+        rec["experts_per_token"] = {"k_min": cfg.k_min, "k_max": cfg.k,
+                                    "threshold": cfg.route_threshold,
+                                    "mean": round(float(kt.mean()), 4),
+                                    "tokens_by_count": {str(j): int((kt == j).sum())
+                                                        for j in range(cfg.k_min, cfg.k + 1)}}
     del xs, x_perm, h, y_perm, fwd
     torch.cuda.synchronize()
     if not args.no_cpu_baseline:
@@ -542,6 +553,8 @@ def main():
         for name in OTHERS:
             if name != head_cfg.name:
                 per[name] = measure(configs.get(name), args, False)
+        # the wide layer with the page's 2-4 experts per token (a variant)
+        per["wide_dynamic"] = measure(configs.WIDE_DYNAMIC, args, False)
     hr = per[head_cfg.name]
     roof = dict(hr["roofline"])
     if probes and roof["unit"] == "TFLOP/s":

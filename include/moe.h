@@ -73,7 +73,8 @@ typedef enum {
  *   renormalize: 0 or 1;  dtype: a moe_dtype
  *   drop_policy: a moe_drop_policy (appended field; zero = the default)
  *   layout: a moe_layout (appended field; zero = the default); the padded
- *           layout needs a capacity limit (cap_den > 0) and E * C < 2^31 */
+ *           layout needs a capacity limit (cap_den > 0) and E * C < 2^31
+ *   route_threshold, k_min (appended fields; zero = a fixed k): see below */
 typedef struct {
     int64_t T;
     int32_t d;
@@ -87,6 +88,21 @@ typedef struct {
     int32_t dtype;
     int32_t drop_policy;
     int32_t layout;
+    /* Dynamic number of experts per token (a variant: the TorchTitan 1K-GPU
+     * article, section 2.1, has each token activate 2-4 experts).  With
+     * route_threshold in (0, 1], token t takes k_t experts: the fewest of its
+     * k highest-ranked ones, at least k_min (1 <= k_min <= k), whose softmax
+     * probabilities sum to at least route_threshold (k when none do).  Gates
+     * are p of those k_t experts (renormalised over them when renormalize);
+     * topk_idx / topk_gate slots j >= k_t hold -1 and 0, and no row.  The
+     * decision is evaluated in fp64 from the fp32 logits.  The capacity then
+     * scales the realised mean load: C = ceil(cap_num * A / (cap_den * E))
+     * for the A assignments of the batch, computed on the device
+     * (moe_capacity and moe_max_rows give the bound for A = T * k).  Not with
+     * the padded layout, and not in moe_backward (MOE_ERR_UNSUPPORTED).
+     * route_threshold = 0 (with k_min = 0): every token takes k experts. */
+    float route_threshold;
+    int32_t k_min;
 } moe_config;
 
 /* Which assignments fill an expert's C slots first when it overflows. */

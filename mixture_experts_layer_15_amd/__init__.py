@@ -41,7 +41,8 @@ class CConfig(ctypes.Structure):
                 ("temperature", ctypes.c_float), ("cap_num", ctypes.c_int32),
                 ("cap_den", ctypes.c_int32), ("renormalize", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
-                ("layout", ctypes.c_int32)]
+                ("layout", ctypes.c_int32), ("route_threshold", ctypes.c_float),
+                ("k_min", ctypes.c_int32)]
 
 
 class CMLPRouter(ctypes.Structure):
@@ -116,7 +117,8 @@ def cconfig(cfg: MoEConfig, T: Optional[int] = None) -> CConfig:
                    temperature=cfg.temperature, cap_num=cfg.cap_num, cap_den=cfg.cap_den,
                    renormalize=int(cfg.renormalize),
                    dtype=MOE_BF16 if cfg.dtype == "bf16" else MOE_F32,
-                   drop_policy=int(cfg.drop_policy), layout=int(cfg.layout))
+                   drop_policy=int(cfg.drop_policy), layout=int(cfg.layout),
+                   route_threshold=float(cfg.route_threshold), k_min=int(cfg.k_min))
 
 
 def _check(status: int, where: str) -> None:

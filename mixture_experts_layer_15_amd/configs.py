@@ -46,6 +46,10 @@ class MoEConfig:
     zipf_scale: float = 1.0  # factor on the Zipf log-prior bias
     drop_policy: int = 0  # 0: overflow dropped in token order; 1: choice order (first choices first)
     layout: int = 0       # 0: compact expert-grouped rows; 1: padded to C rows per expert
+    # dynamic expert count: threshold > 0 lets each token take k_min .. k
+    # experts, the fewest whose softmax mass reaches the threshold
+    route_threshold: float = 0.0
+    k_min: int = 0
 
     def scaled(self, **kw) -> "MoEConfig":
         """A copy with some fields replaced (used to make small test cases)."""
@@ -67,6 +71,13 @@ CONFIGS = [
 ]
 
 BY_NAME = {c.name: c for c in CONFIGS}
+
+# Variant of the wide layer with the page's 2-4 experts per token (TorchTitan
+# 1K-GPU article, section 2.1): up to 4 experts, at least 2, the fewest whose
+# softmax mass reaches 0.6 (on seed-0 inputs 54% of tokens take 2, 20% take
+# 3, 26% take 4).  Not one of the five measured layers: it is measured and
+# tested beside them.
+WIDE_DYNAMIC = BY_NAME["wide"].scaled(name="wide_dynamic", k=4, k_min=2, route_threshold=0.6)
 
 
 def get(name_or_index) -> MoEConfig:

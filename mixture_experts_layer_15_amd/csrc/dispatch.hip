@@ -29,6 +29,29 @@ namespace {
 
 constexpr int kInvalid = 256;   // expert code of an empty / out-of-range slot
 
+// Sum of one value per thread over a 256-thread workgroup (every thread must
+// call it; s4 holds 4 entries of LDS).
+__device__ __forceinline__ long long block_sum256(long long v, long long* s4) {
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if ((threadIdx.x & 63) == 0) s4[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const long long t = ((s4[0] + s4[1]) + s4[2]) + s4[3];
+    __syncthreads();
+    return t;
+}
+
+// Capacity of a dynamically routed batch (tokens taking varying numbers of
+// experts): the factor cap_num / cap_den scales the realised mean load,
+// C = ceil(cap_num A / (cap_den E)) for A assignments, at most T (a limit of T
+// or more never drops anything); no limit (cap_den == 0) gives T.
+__device__ __forceinline__ long long realised_capacity(long long A, int cap_num, int cap_den,
+                                                       int E, long long T) {
+    if (cap_den == 0) return T;
+    const long long num = (long long)cap_num * A, den = (long long)cap_den * E;
+    const long long c = (num + den - 1) / den;
+    return c < T ? c : T;
+}
+
 // Slot (index into topk_idx / row_of) of choice j of walked token v, and the
 // real token it belongs to.  Token order walks the real tokens (slot v*k + j);
 // choice order walks the Tr*kr single choices v = j'*Tr + t (k = 1), whose
@@ -65,8 +88,10 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ b
                                                    int32_t* __restrict__ blockbase, int nblk,
                                                    int E, long long C, int padded,
                                                    int32_t* __restrict__ count,
-                                                   int32_t* __restrict__ offset) {
+                                                   int32_t* __restrict__ offset, int dyn,
+                                                   int cap_num, int cap_den, long long Tr) {
     __shared__ int s_wave[4];
+    __shared__ long long s_red[4];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
@@ -78,6 +103,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ b
         }
         count[e] = run;
     }
+    if (dyn) C = realised_capacity(block_sum256(run, s_red), cap_num, cap_den, E, Tr);
     const int kept = (e < E) ? (int)min((long long)run, C) : 0;
     // exclusive scan of kept over the 256 threads
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -174,9 +200,15 @@ __global__ __launch_bounds__(256) void place_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ blockbase,
     const int32_t* __restrict__ offset, long long C, long long T, int E, int k,
     int blk_tokens, int Tr, int kr, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ token_of_row) {
+    int32_t* __restrict__ token_of_row, const int32_t* __restrict__ count, int dyn,
+    int cap_num, int cap_den) {
     __shared__ int run[256];
     __shared__ int wcnt[4][256];
+    __shared__ long long s_red[4];
+    if (dyn) {
+        const long long c = threadIdx.x < E ? count[threadIdx.x] : 0;
+        C = realised_capacity(block_sum256(c, s_red), cap_num, cap_den, E, Tr);
+    }
     for (int e = threadIdx.x; e < 256; e += 256)
         run[e] = (e < E) ? blockbase[(long long)blockIdx.x * E + e] : 0;
     const int n_kept = offset[E];
@@ -197,11 +229,13 @@ template <bool CM>
 __global__ __launch_bounds__(256) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, long long C, long long T, int E, int k, int Tr, int kr,
     int padded, int32_t* __restrict__ count, int32_t* __restrict__ offset_out,
-    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of_row) {
+    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of_row, int dyn, int cap_num,
+    int cap_den) {
     __shared__ int h_all[256], run[256];
     __shared__ int32_t s_off[257];
     __shared__ int wcnt[4][256];
     __shared__ int s_wave[4];
+    __shared__ long long s_red[4];
     const int tid = threadIdx.x;
     h_all[tid] = 0;
     run[tid] = 0;
@@ -228,6 +262,8 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
         }
     }
     __syncthreads();
+    if (dyn) C = realised_capacity(block_sum256(tid < E ? h_all[tid] : 0, s_red), cap_num, cap_den,
+                                   E, Tr);
     // kept = min(count, C); exclusive scan over the experts
     const int e = tid;
     const int kept = (e < E) ? (int)min((long long)h_all[e], C) : 0;
@@ -309,8 +345,12 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict
 
 }  // namespace
 
-DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy, int layout) {
+DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy, int layout,
+                           bool dyn, int cap_num, int cap_den) {
     DispatchPlan p;
+    p.dyn = dyn;
+    p.cap_num = cap_num;
+    p.cap_den = cap_den;
     p.padded = layout == 1;
     p.Tr = T;
     p.kr = k;
@@ -341,7 +381,8 @@ hipError_t dispatch_kernels(const DispatchPlan& p, const int32_t* idx, int32_t* 
     if (p.T > 0 && p.T * p.k <= kSmallAssign) {
         hipLaunchKernelGGL(dispatch_small_kernel<CM>, dim3((unsigned)((p.T + 255) / 256)),
                            dim3(256), 0, s, idx, p.C, p.T, p.E, p.k, Tr, kr, p.padded ? 1 : 0,
-                           count, offset, row_of, token_of_row);
+                           count, offset, row_of, token_of_row, p.dyn ? 1 : 0, p.cap_num,
+                           p.cap_den);
         return hipGetLastError();
     }
     int32_t* blockcount = (int32_t*)workspace;
@@ -353,11 +394,13 @@ hipError_t dispatch_kernels(const DispatchPlan& p, const int32_t* idx, int32_t* 
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, blockcount, blockbase, p.nblk,
-                       p.E, p.C, p.padded ? 1 : 0, count, offset);
+                       p.E, p.C, p.padded ? 1 : 0, count, offset, p.dyn ? 1 : 0, p.cap_num,
+                       p.cap_den, p.Tr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || p.nblk == 0) return err;
     hipLaunchKernelGGL(place_kernel<CM>, dim3(p.nblk), dim3(256), 0, s, idx, blockbase, offset,
-                       p.C, p.T, p.E, p.k, p.blk_tokens, Tr, kr, row_of, token_of_row);
+                       p.C, p.T, p.E, p.k, p.blk_tokens, Tr, kr, row_of, token_of_row, count,
+                       p.dyn ? 1 : 0, p.cap_num, p.cap_den);
     return hipGetLastError();
 }
 
@@ -398,7 +441,12 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, void* x_per
 // Expert-load telemetry: one workgroup, fp64.  stats as documented in moe.h.
 __global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restrict__ count,
                                                          int E, long long C,
-                                                         double* __restrict__ stats) {
+                                                         double* __restrict__ stats, int dyn,
+                                                         int cap_num, int cap_den, long long T) {
+    __shared__ long long s_red[4];
+    if (dyn)   // capacity from the realised assignments (uniform branch)
+        C = realised_capacity(block_sum256(threadIdx.x < E ? count[threadIdx.x] : 0, s_red),
+                              cap_num, cap_den, E, T);
     __shared__ double s_sum[4], s_max[4], s_min[4], s_drop[4], s_empty[4], s_dev[4], s_ss[4];
     const int e = threadIdx.x, lane = e & 63, w = e >> 6;
     const bool ok = e < E;
@@ -446,8 +494,9 @@ __global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restri
 }
 
 hipError_t launch_load_stats(const int32_t* count, int E, long long C, double* stats,
-                             hipStream_t s) {
-    hipLaunchKernelGGL(load_stats_kernel, dim3(1), dim3(256), 0, s, count, E, C, stats);
+                             hipStream_t s, bool dyn, int cap_num, int cap_den, long long T) {
+    hipLaunchKernelGGL(load_stats_kernel, dim3(1), dim3(256), 0, s, count, E, C, stats,
+                       dyn ? 1 : 0, cap_num, cap_den, T);
     return hipGetLastError();
 }
 

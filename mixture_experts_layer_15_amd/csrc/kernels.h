@@ -10,14 +10,25 @@
 
 namespace moe {
 
+// Top-k routing parameters: k slots per token, softmax temperature tau, gates
+// renormalised over the chosen experts or not; theta > 0 makes the count per
+// token dynamic (the fewest of the k ranked experts, at least k_min, whose
+// softmax mass reaches theta; the slots past it hold expert -1, gate 0).
+struct TopkParams {
+    int k;
+    float tau;
+    int renorm;
+    int k_min;
+    float theta;
+};
+
 // Router: logits = x W_r + b (fp32 accumulation), softmax(l / tau), top-k, gates.
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* bias,
                         float* logits, int32_t* idx, float* gate, long long T, int d, int E,
-                        int k, float tau, int renorm, hipStream_t s);
+                        TopkParams tp, hipStream_t s);
 // Top-k and gates from given fp32 logits.
 hipError_t launch_route_from_logits(const float* logits, int32_t* idx, float* gate,
-                                    long long T, int E, int k, float tau, int renorm,
-                                    hipStream_t s);
+                                    long long T, int E, TopkParams tp, hipStream_t s);
 
 // Dispatch.  Tokens are cut into nblk blocks of blk_tokens (a multiple of 256)
 // with nblk <= 256; workspace holds two [nblk][E] int32 tables.
@@ -33,9 +44,14 @@ struct DispatchPlan {
     int kr;                // real choices per token
     bool choice_order;
     bool padded;           // padded layout: expert e owns rows e*C .. e*C + C - 1
+    // dynamic expert counts: C is taken on the device from the realised
+    // assignments, ceil(cap_num A / (cap_den E)) (C above is then only the
+    // host's upper bound)
+    bool dyn;
+    int cap_num, cap_den;
 };
 DispatchPlan plan_dispatch(long long T, int E, int k, long long C, int policy = 0,
-                           int layout = 0);
+                           int layout = 0, bool dyn = false, int cap_num = 0, int cap_den = 0);
 size_t dispatch_workspace_bytes(const DispatchPlan& p);
 // scatter = false leaves x_perm unwritten (for a consumer that gathers rows of
 // x through token_of_row itself).  In the padded layout the empty rows get
@@ -51,7 +67,8 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, void* x_per
 
 // Expert-load telemetry (8 fp64 values, see moe_load_stats).
 hipError_t launch_load_stats(const int32_t* count, int E, long long C, double* stats,
-                             hipStream_t s);
+                             hipStream_t s, bool dyn = false, int cap_num = 0, int cap_den = 0,
+                             long long T = 0);
 
 // Grouped GeGLU expert FFN (gate/up GEMM with fused epilogue, then down GEMM).
 hipError_t launch_expert_ffn(int dtype, const void* x_perm, const int32_t* off,
@@ -123,7 +140,7 @@ hipError_t launch_route_mlp(const uint16_t* x, const uint16_t* prev, float gamma
                             const float* b1, const uint16_t* w2, const float* b2,
                             const uint16_t* w3, const float* b3, const float* pid,
                             float* logits, int32_t* idx, float* gate, long long T, int d, int r,
-                            int m, int E, int k, float tau, int renorm, void* ws, int cus,
+                            int m, int E, TopkParams tp, void* ws, int cus,
                             hipStream_t s);
 
 // Gate-weighted combine.

@@ -68,7 +68,7 @@ hipError_t launch_route_mlp(const uint16_t* x, const uint16_t* prev, float gamma
                             const float* b1, const uint16_t* w2, const float* b2,
                             const uint16_t* w3, const float* b3, const float* pid,
                             float* logits, int32_t* idx, float* gate, long long T, int d, int r,
-                            int m, int E, int k, float tau, int renorm, void* ws, int cus,
+                            int m, int E, TopkParams tp, void* ws, int cus,
                             hipStream_t s) {
     if (T == 0) return hipSuccess;
     char* w = (char*)ws;
@@ -91,7 +91,7 @@ hipError_t launch_route_mlp(const uint16_t* x, const uint16_t* prev, float gamma
     if (e != hipSuccess) return e;
     e = launch_mfma_dense(h1, w2, b2, 1, h2, (int)T, m, m, cus, s);
     if (e != hipSuccess) return e;
-    return launch_route(1, h2, w3, bias_sum, logits, idx, gate, T, m, E, k, tau, renorm, s);
+    return launch_route(1, h2, w3, bias_sum, logits, idx, gate, T, m, E, tp, s);
 }
 
 }  // namespace moe

@@ -63,6 +63,26 @@ int64_t tor_len(const moe_config* c) {
 
 size_t esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
+// Dynamic expert count per token (route_threshold > 0).
+bool dyn_route(const moe_config* c) { return c->route_threshold > 0.f; }
+
+moe::TopkParams topk_params(const moe_config* c) {
+    moe::TopkParams tp;
+    tp.k = c->k;
+    tp.tau = c->temperature;
+    tp.renorm = c->renormalize;
+    tp.k_min = dyn_route(c) ? c->k_min : c->k;
+    tp.theta = dyn_route(c) ? c->route_threshold : 0.f;
+    return tp;
+}
+
+// The dispatch's plan; with a dynamic expert count the kernels take the
+// capacity from the realised assignments, capacity_eff() is its upper bound.
+moe::DispatchPlan dispatch_plan(const moe_config* c) {
+    return moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy, c->layout,
+                              dyn_route(c), c->cap_num, c->cap_den);
+}
+
 moe_status check_cfg(const moe_config* c) {
     if (c == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
     if (c->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld < 0", (long long)c->T);
@@ -87,6 +107,17 @@ moe_status check_cfg(const moe_config* c) {
         return fail(MOE_ERR_INVALID_ARG, "drop_policy %d is not a moe_drop_policy", c->drop_policy);
     if (c->layout != MOE_LAYOUT_COMPACT && c->layout != MOE_LAYOUT_PADDED)
         return fail(MOE_ERR_INVALID_ARG, "layout %d is not a moe_layout", c->layout);
+    if (c->route_threshold != 0.f) {
+        if (!(c->route_threshold > 0.f) || !(c->route_threshold <= 1.f))
+            return fail(MOE_ERR_INVALID_ARG, "route_threshold must be 0 (fixed k) or in (0, 1]");
+        if (c->k_min < 1 || c->k_min > c->k)
+            return fail(MOE_ERR_INVALID_ARG, "k_min = %d outside [1, k = %d]", c->k_min, c->k);
+        if (c->layout == MOE_LAYOUT_PADDED)
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "the padded layout needs a fixed capacity: no dynamic expert count");
+    } else if (c->k_min != 0) {
+        return fail(MOE_ERR_INVALID_ARG, "k_min must be 0 when route_threshold is 0");
+    }
     if (c->layout == MOE_LAYOUT_PADDED) {
         if (c->cap_den == 0)
             return fail(MOE_ERR_INVALID_ARG, "the padded layout needs a capacity limit (cap_den > 0)");
@@ -154,7 +185,7 @@ struct FwdLayout {
 // differs from the staged calls' by the split).
 bool fwd_direct(const moe_config* c) {
     return c->dtype == MOE_BF16 && c->k == 1 && c->layout == MOE_LAYOUT_COMPACT &&
-           capacity_eff(c) >= c->T;
+           capacity_eff(c) >= c->T && !dyn_route(c);
 }
 bool fwd_down_split(const moe_config* c) {
     return fwd_direct(c) &&
@@ -174,7 +205,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 FwdLayout fwd_layout(const moe_config* c) {
     const size_t T = (size_t)c->T, E = (size_t)c->E, k = (size_t)c->k;
     const size_t R = (size_t)max_rows(c);
-    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy, c->layout);
+    const moe::DispatchPlan p = dispatch_plan(c);
     FwdLayout L;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -221,7 +252,7 @@ moe_status moe_dispatch_workspace_size(const moe_config* cfg, size_t* bytes) {
     CHECK(check_cfg(cfg));
     if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
     *bytes = moe::dispatch_workspace_bytes(
-        moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout));
+        dispatch_plan(cfg));
     return MOE_OK;
 }
 
@@ -250,8 +281,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
     CHECK(check_ptr(topk_idx, "topk_idx", T * k * 4));
     CHECK(check_ptr(topk_gate, "topk_gate", T * k * 4));
     hipError_t e = moe::launch_route(cfg->dtype, x, w_router, bias, logits, topk_idx, topk_gate,
-                                     cfg->T, cfg->d, cfg->E, cfg->k, cfg->temperature,
-                                     cfg->renormalize, (hipStream_t)stream);
+                                     cfg->T, cfg->d, cfg->E, topk_params(cfg),
+                                     (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
 }
 
@@ -263,8 +294,7 @@ moe_status moe_route_from_logits(const moe_config* cfg, const float* logits, int
     CHECK(check_ptr(topk_idx, "topk_idx", T * k * 4));
     CHECK(check_ptr(topk_gate, "topk_gate", T * k * 4));
     hipError_t e = moe::launch_route_from_logits(logits, topk_idx, topk_gate, cfg->T, cfg->E,
-                                                 cfg->k, cfg->temperature, cfg->renormalize,
-                                                 (hipStream_t)stream);
+                                                 topk_params(cfg), (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_from_logits");
 }
 
@@ -283,7 +313,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const vo
     CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
     CHECK(check_ptr(row_of, "row_of", T * k * 4));
     CHECK(check_ptr(token_of_row, "token_of_row", (size_t)tor_len(cfg) * 4));
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout);
+    const moe::DispatchPlan p = dispatch_plan(cfg);
     const size_t need = moe::dispatch_workspace_bytes(p);
     if (workspace == nullptr || ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "dispatch workspace: need %zu bytes, got %zu", need, ws_bytes);
@@ -346,8 +376,7 @@ moe_status moe_dispatch_noalloc(const moe_config* cfg, const int32_t* topk_idx, 
     CHECK(check_ptr(expert_offset, "expert_offset", (E + 1) * 4));
     CHECK(check_ptr(row_of, "row_of", T * k * 4));
     CHECK(check_ptr(token_of_row, "token_of_row", (size_t)tor_len(cfg) * 4));
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg),
-                                                   cfg->drop_policy, cfg->layout);
+    const moe::DispatchPlan p = dispatch_plan(cfg);
     const size_t need = moe::dispatch_workspace_bytes(p);
     if (need > MOE_DISPATCH_SCRATCH_BYTES)
         return fail(MOE_ERR_INVALID_ARG,
@@ -483,8 +512,8 @@ moe_status moe_route_mlp(const moe_config* cfg, const moe_mlp_router* rt, const 
         (const uint16_t*)x, (const uint16_t*)prev, rt->gamma, rt->eps,
         (const uint16_t*)rt->w_down, rt->b_down, (const uint16_t*)rt->w1, rt->b1,
         (const uint16_t*)rt->w2, rt->b2, (const uint16_t*)rt->w3, rt->b3, rt->pid_bias, logits,
-        topk_idx, topk_gate, cfg->T, cfg->d, rt->r, rt->m, cfg->E, cfg->k, cfg->temperature,
-        cfg->renormalize, workspace, gemm_grid_cap() / 2, (hipStream_t)stream);
+        topk_idx, topk_gate, cfg->T, cfg->d, rt->r, rt->m, cfg->E, topk_params(cfg), workspace,
+        gemm_grid_cap() / 2, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_mlp");
 }
 
@@ -497,7 +526,8 @@ moe_status moe_load_stats(const moe_config* cfg, const int32_t* expert_count, do
     if (stats == nullptr) return fail(MOE_ERR_INVALID_ARG, "stats is NULL");
     CHECK(check_ptr(stats, "stats", 8 * sizeof(double)));
     hipError_t e = moe::launch_load_stats(expert_count, cfg->E, capacity_eff(cfg), stats,
-                                          (hipStream_t)stream);
+                                          (hipStream_t)stream, dyn_route(cfg), cfg->cap_num,
+                                          cfg->cap_den, cfg->T);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_load_stats");
 }
 
@@ -528,10 +558,10 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     int32_t* tor = (int32_t*)(w + L.token_of_row);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T,
-                                     cfg->d, cfg->E, cfg->k, cfg->temperature, cfg->renormalize, s);
+                                     cfg->d, cfg->E, topk_params(cfg), s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
     const bool gather = fwd_gather(cfg);   // no x_perm: see fwd_gather
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, cfg->E, cfg->k, capacity_eff(cfg), cfg->drop_policy, cfg->layout);
+    const moe::DispatchPlan p = dispatch_plan(cfg);
     e = moe::launch_dispatch(p, cfg->dtype, idx, x, w + L.x_perm, count, offset, row_of, tor,
                              w + L.dsp, cfg->d, s, !gather);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/dispatch");
@@ -577,7 +607,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(const moe_config* c) {
     const size_t T = (size_t)c->T, E = (size_t)c->E, k = (size_t)c->k, d = (size_t)c->d;
     const size_t F = (size_t)c->d_ff, R = (size_t)max_rows(c);
-    const moe::DispatchPlan p = moe::plan_dispatch(c->T, c->E, c->k, capacity_eff(c), c->drop_policy, c->layout);
+    const moe::DispatchPlan p = dispatch_plan(c);
     BwdLayout L;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -607,6 +637,8 @@ BwdLayout bwd_layout(const moe_config* c) {
 moe_status check_bwd(const moe_config* cfg) {
     CHECK(check_cfg(cfg));
     if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
+    if (dyn_route(cfg))
+        return fail(MOE_ERR_UNSUPPORTED, "the backward runs on a fixed expert count per token only");
     if (cfg->layout != MOE_LAYOUT_COMPACT)
         return fail(MOE_ERR_UNSUPPORTED, "the backward runs on the compact layout only");
     return MOE_OK;
@@ -684,9 +716,9 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     const int cus = gemm_grid_cap();
 
     // forward recompute: routing, dispatch maps and x_perm, g = x W_gate, u = x W_up
-    BWD(moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T, di, Ei, ki,
-                          cfg->temperature, cfg->renormalize, s), "moe_backward/route");
-    const moe::DispatchPlan p = moe::plan_dispatch(cfg->T, Ei, ki, capacity_eff(cfg), cfg->drop_policy, cfg->layout);
+    BWD(moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T, di, Ei,
+                          topk_params(cfg), s), "moe_backward/route");
+    const moe::DispatchPlan p = dispatch_plan(cfg);
     uint16_t* x_perm = (uint16_t*)(w + L.x_perm);
     uint16_t* dy_perm = (uint16_t*)(w + L.dy_perm);
     BWD(moe::launch_dispatch(p, cfg->dtype, idx, x, x_perm, count, offset, row_of, tor,

@@ -31,10 +31,13 @@ constexpr int kNone = 0x7fffffff;
 // One token per 16-lane group; lane q owns experts q + 16 m.  All 16 lanes
 // must call this together (shuffles); only `write` lanes store.
 template <int NT>
-__device__ __forceinline__ void topk_group16(const float (&v)[NT], int q, int E, int k,
-                                             float tau, int renorm, bool write,
+__device__ __forceinline__ void topk_group16(const float (&v)[NT], int q, int E,
+                                             const TopkParams& tp, bool write,
                                              int32_t* __restrict__ idx_row,
                                              float* __restrict__ gate_row) {
+    const int k = tp.k;
+    const float tau = tp.tau;
+    const int renorm = tp.renorm;
     unsigned taken = 0;
     float cv[8];
     int ce[8];
@@ -74,19 +77,44 @@ __device__ __forceinline__ void topk_group16(const float (&v)[NT], int q, int E,
     // butterfly sum: every lane ends with the same value (pairs add x+y / y+x)
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) z += __shfl_xor(z, o, 16);
+    // dynamic count (theta > 0): the fewest of the k ranked experts, at least
+    // k_min, whose softmax mass reaches theta.  This integer decision is taken
+    // in fp64 from the fp32 logits (exp and sums in double), so that it agrees
+    // with an fp64 evaluation of the same definition except when the mass
+    // lies within a few fp64 rounding steps of theta.
+    int kt = k;
+    if (tp.theta > 0.f) {
+        const double dmx = (double)mx, dtau = (double)tau;
+        double zd = 0.0;
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+            if (m * 16 + q < E) zd += exp(((double)v[m] - dmx) / dtau);
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) zd += __shfl_xor(zd, o, 16);
+        double mass = 0.0;
+        bool done = false;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < k && !done) {
+                mass += exp(((double)cv[j] - dmx) / dtau) / zd;
+                if (j + 1 >= tp.k_min && mass >= (double)tp.theta) { kt = j + 1; done = true; }
+            }
+        }
+    }
     float ev[8];
     float sk = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         ev[j] = 0.f;
-        if (j < k) { ev[j] = expf((cv[j] - mx) / tau); sk += ev[j]; }
+        if (j < kt) { ev[j] = expf((cv[j] - mx) / tau); sk += ev[j]; }
     }
     if (write && q == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             if (j < k) {
-                idx_row[j] = ce[j];
-                gate_row[j] = renorm ? ev[j] / sk : ev[j] / z;
+                // slots past the token's count hold no assignment
+                idx_row[j] = j < kt ? ce[j] : -1;
+                gate_row[j] = j < kt ? (renorm ? ev[j] / sk : ev[j] / z) : 0.f;
             }
     }
 }
@@ -97,7 +125,7 @@ template <int NT, int MT>
 __global__ __launch_bounds__(256) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, float* __restrict__ logits, int32_t* __restrict__ idx,
-    float* __restrict__ gate, long long T, int d, int E, int k, float tau, int renorm) {
+    float* __restrict__ gate, long long T, int d, int E, TopkParams tp) {
     constexpr int EP = 16 * NT;
     constexpr int W_LD = EP + 8;   // LDS row stride (elements)
     __shared__ __attribute__((aligned(16))) uint16_t ws[RBK * W_LD];
@@ -185,7 +213,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
             }
             const bool ok = t < T;
             const long long tt = ok ? t : 0;
-            topk_group16<NT>(v, c16, E, k, tau, renorm, ok, idx + tt * k, gate + tt * k);
+            topk_group16<NT>(v, c16, E, tp, ok, idx + tt * tp.k, gate + tt * tp.k);
         }
     }
 }
@@ -200,7 +228,7 @@ template <int NT, int MT, int D>
 __global__ __launch_bounds__(256) void router_ks_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, float* __restrict__ logits, int32_t* __restrict__ idx,
-    float* __restrict__ gate, long long T, int d, int E, int k, float tau, int renorm) {
+    float* __restrict__ gate, long long T, int d, int E, TopkParams tp) {
     constexpr int EP = 16 * NT;
     constexpr int W_LD = EP + 8;               // LDS row stride (elements)
     constexpr int WCH = RBK * EP / 8 / 64;     // 16-byte W_r chunks per lane per K-step
@@ -310,7 +338,7 @@ __global__ __launch_bounds__(256) void router_ks_kernel(
         }
         const bool ok = t < T;
         const long long tt = ok ? t : 0;
-        topk_group16<NT>(v, c16, E, k, tau, renorm, ok, idx + tt * k, gate + tt * k);
+        topk_group16<NT>(v, c16, E, tp, ok, idx + tt * tp.k, gate + tt * tp.k);
     }
 }
 
@@ -320,7 +348,7 @@ template <int NT>
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gate,
-    long long T, int d, int E, int k, float tau, int renorm) {
+    long long T, int d, int E, TopkParams tp) {
     constexpr int EP = 16 * NT;
     __shared__ float lg[64][EP + 1];
     const long long t0 = (long long)blockIdx.x * 64;
@@ -345,7 +373,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
         for (int m = 0; m < NT; ++m) v[m] = lg[tl][m * 16 + q];
         const bool ok = t < T;
         const long long tt = ok ? t : 0;
-        topk_group16<NT>(v, q, E, k, tau, renorm, ok, idx + tt * k, gate + tt * k);
+        topk_group16<NT>(v, q, E, tp, ok, idx + tt * tp.k, gate + tt * tp.k);
     }
 }
 
@@ -354,7 +382,7 @@ template <int NT>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    int32_t* __restrict__ idx,
                                                    float* __restrict__ gate, long long T,
-                                                   int E, int k, float tau, int renorm) {
+                                                   int E, TopkParams tp) {
     const int q = threadIdx.x & 15, grp = threadIdx.x >> 4;
     const long long t = (long long)blockIdx.x * 16 + grp;
     const bool ok = t < T;
@@ -365,15 +393,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         const int e = m * 16 + q;
         v[m] = (e < E) ? logits[tt * E + e] : 0.f;
     }
-    topk_group16<NT>(v, q, E, k, tau, renorm, ok, idx + tt * k, gate + tt * k);
+    topk_group16<NT>(v, q, E, tp, ok, idx + tt * tp.k, gate + tt * tp.k);
 }
 
 // K-split router launch: 16*MT tokens per workgroup, MT grown only while at
 // least 512 workgroups remain; D K-steps in flight per wave.
 template <int NT>
 hipError_t route_ks(const uint16_t* x, const uint16_t* w, const float* bias, float* logits,
-                    int32_t* idx, float* gate, long long T, int d, int E, int k, float tau,
-                    int renorm, hipStream_t s) {
+                    int32_t* idx, float* gate, long long T, int d, int E, TopkParams tp,
+                    hipStream_t s) {
     // E > 64: W_r chunks take 64 registers per K-step in flight, so two steps
     // in flight.  At most two token tiles per wave: four (fewer re-reads of
     // W_r per token) need more than 256 registers, which leaves one wave per
@@ -382,40 +410,40 @@ hipError_t route_ks(const uint16_t* x, const uint16_t* w, const float* bias, flo
     constexpr int D2 = NT <= 4 ? 3 : 2, D1 = NT <= 4 ? 4 : 2;
     if (T >= 16LL * 2 * 512)
         hipLaunchKernelGGL((router_ks_kernel<NT, 2, D2>), dim3((unsigned)((T + 31) / 32)), dim3(256),
-                           0, s, x, w, bias, logits, idx, gate, T, d, E, k, tau, renorm);
+                           0, s, x, w, bias, logits, idx, gate, T, d, E, tp);
     else
         hipLaunchKernelGGL((router_ks_kernel<NT, 1, D1>), dim3((unsigned)((T + 15) / 16)), dim3(256),
-                           0, s, x, w, bias, logits, idx, gate, T, d, E, k, tau, renorm);
+                           0, s, x, w, bias, logits, idx, gate, T, d, E, tp);
     return hipGetLastError();
 }
 
 template <int NT>
 hipError_t route_nt(int dtype, const void* x, const void* w, const float* bias, float* logits,
-                    int32_t* idx, float* gate, long long T, int d, int E, int k, float tau,
-                    int renorm, hipStream_t s) {
+                    int32_t* idx, float* gate, long long T, int d, int E, TopkParams tp,
+                    hipStream_t s) {
     if (dtype == 1) {
         if constexpr (NT <= 8) {
             if (E % 8 == 0)
                 return route_ks<NT>((const uint16_t*)x, (const uint16_t*)w, bias, logits, idx,
-                                    gate, T, d, E, k, tau, renorm, s);
+                                    gate, T, d, E, tp, s);
         }
         if (T >= 64LL * 1024 && NT <= 8) {
             // two 16-row tiles per wave once there are enough tokens to fill the GPU
             const long long grid = (T + 127) / 128;
             hipLaunchKernelGGL((router_bf16_kernel<NT, 2>), dim3((unsigned)grid), dim3(256), 0, s,
                                (const uint16_t*)x, (const uint16_t*)w, bias, logits, idx, gate,
-                               T, d, E, k, tau, renorm);
+                               T, d, E, tp);
         } else {
             const long long grid = (T + 63) / 64;
             hipLaunchKernelGGL((router_bf16_kernel<NT, 1>), dim3((unsigned)grid), dim3(256), 0, s,
                                (const uint16_t*)x, (const uint16_t*)w, bias, logits, idx, gate,
-                               T, d, E, k, tau, renorm);
+                               T, d, E, tp);
         }
     } else {
         const long long grid = (T + 63) / 64;
         hipLaunchKernelGGL(router_f32_kernel<NT>, dim3((unsigned)grid), dim3(256), 0, s,
                            (const float*)x, (const float*)w, bias, logits, idx, gate, T, d, E,
-                           k, tau, renorm);
+                           tp);
     }
     return hipGetLastError();
 }
@@ -429,28 +457,27 @@ int nt_for(int E) {
 
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* bias,
                         float* logits, int32_t* idx, float* gate, long long T, int d, int E,
-                        int k, float tau, int renorm, hipStream_t s) {
+                        TopkParams tp, hipStream_t s) {
     if (T == 0) return hipSuccess;
     switch (nt_for(E)) {
-        case 1: return route_nt<1>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, k, tau, renorm, s);
-        case 2: return route_nt<2>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, k, tau, renorm, s);
-        case 4: return route_nt<4>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, k, tau, renorm, s);
-        case 8: return route_nt<8>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, k, tau, renorm, s);
-        default: return route_nt<16>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, k, tau, renorm, s);
+        case 1: return route_nt<1>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, tp, s);
+        case 2: return route_nt<2>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, tp, s);
+        case 4: return route_nt<4>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, tp, s);
+        case 8: return route_nt<8>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, tp, s);
+        default: return route_nt<16>(dtype, x, w_router, bias, logits, idx, gate, T, d, E, tp, s);
     }
 }
 
 hipError_t launch_route_from_logits(const float* logits, int32_t* idx, float* gate,
-                                    long long T, int E, int k, float tau, int renorm,
-                                    hipStream_t s) {
+                                    long long T, int E, TopkParams tp, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const dim3 grid((unsigned)((T + 15) / 16));
     switch (nt_for(E)) {
-        case 1: hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(256), 0, s, logits, idx, gate, T, E, k, tau, renorm); break;
-        case 2: hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, s, logits, idx, gate, T, E, k, tau, renorm); break;
-        case 4: hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, s, logits, idx, gate, T, E, k, tau, renorm); break;
-        case 8: hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(256), 0, s, logits, idx, gate, T, E, k, tau, renorm); break;
-        default: hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, s, logits, idx, gate, T, E, k, tau, renorm); break;
+        case 1: hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(256), 0, s, logits, idx, gate, T, E, tp); break;
+        case 2: hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, s, logits, idx, gate, T, E, tp); break;
+        case 4: hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, s, logits, idx, gate, T, E, tp); break;
+        case 8: hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(256), 0, s, logits, idx, gate, T, E, tp); break;
+        default: hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, s, logits, idx, gate, T, E, tp); break;
     }
     return hipGetLastError();
 }

@@ -328,3 +328,24 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_dynamic_expert_count_validation_on_host(L):
+    # each token takes k_min .. k experts by a softmax-mass threshold: host
+    # checks of its fields, and the places it is not supported (no GPU call)
+    cfg = configs.get("tiny").scaled(dtype="bf16", k=4, E=16, k_min=2, route_threshold=0.6,
+                                     renormalize=True, cap_num=5, cap_den=4)
+    ok = ctypes.c_void_p(1 << 20)
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(moe.cconfig(cfg)), ctypes.byref(n)) == moe.MOE_OK
+    # capacity and rows: the bound for T * k assignments
+    assert moe.capacity(cfg) == orc.capacity(cfg.T, cfg.E, cfg.k, 5, 4)
+    assert L.moe_backward_workspace_size(ctypes.byref(moe.cconfig(cfg)), ctypes.byref(n)) == \
+        moe.MOE_ERR_UNSUPPORTED
+    pad = moe.cconfig(cfg.scaled(layout=1))
+    assert L.moe_workspace_size(ctypes.byref(pad), ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    for bad in (cfg.scaled(k_min=0), cfg.scaled(k_min=5), cfg.scaled(route_threshold=1.5),
+                cfg.scaled(route_threshold=0.0), cfg.scaled(route_threshold=float("nan")),
+                cfg.scaled(route_threshold=-0.5)):
+        assert L.moe_route(ctypes.byref(moe.cconfig(bad)), ok, ok, None, ok, ok, ok, None) == \
+            moe.MOE_ERR_INVALID_ARG

@@ -96,7 +96,9 @@ def run_layer(cfg, dev, host, full=True, seed=0, label=""):
                               tau=float(np.float32(cfg.temperature)),
                               renormalize=cfg.renormalize, cap_num=cfg.cap_num,
                               cap_den=cfg.cap_den, drop_policy=cfg.drop_policy,
-                              logits_in=lg_h.double().numpy(), tokens=stoks)
+                              logits_in=lg_h.double().numpy(), tokens=stoks,
+                              k_min=cfg.k_min,
+                              threshold=float(np.float32(cfg.route_threshold)))
             ystar = ofw["y"]
         ey = rel_err(to_np(y[torch.from_numpy(stoks).cuda()]), ystar)
         say(f"[{label}] y err {ey:.3g} over {stoks.size} tokens")

@@ -2,6 +2,8 @@
 the choice-order drop priority (every first choice before every second
 choice) and the expert-load telemetry.  Integer outputs bit-exact; the layer
 output within the same tolerance as the main parity tests."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,8 @@ import mixture_experts_layer_15_amd as moe
 from mixture_experts_layer_15_amd import configs
 from oracle import oracle as orc
 
-from parity_util import TOL_Y, check_route, gpu_inputs, rel_err, say, to_np
+from parity_util import (TOL_Y, check_route, gpu_inputs, oracle_capacity, rel_err, say,
+                         to_np)
 from test_gpu_parity import run_layer
 
 pytestmark = pytest.mark.gpu
@@ -212,3 +215,55 @@ def test_padded_layout_full_size_skewed():
     cfg = configs.get("skewed")
     dev, host = gpu_inputs(cfg, seed=0)
     _check_padded(cfg, dev, host, full=False, label="skewed/padded")
+
+
+# ---------------------------------------------------------------- dynamic expert count
+# each token takes k_min .. k experts: the fewest whose softmax mass reaches the
+# threshold (the TorchTitan 1K-GPU article's 2-4 experts per token, section 2.1)
+DYN = configs.get("tiny").scaled(dtype="bf16", renormalize=True, cap_num=5, cap_den=4,
+                                 k=4, k_min=2, route_threshold=0.6)
+DYN_CASES = {
+    # one-launch dispatch path, temperature 0.3 as on the page's layer
+    "dyn_small": DYN.scaled(T=2000, d=128, E=16, d_ff=192, temperature=0.3),
+    # multi-block dispatch path, ragged token count, capacity factor 1 (drops)
+    "dyn_blocks": DYN.scaled(T=9001, d=128, E=24, d_ff=128, temperature=0.5, cap_num=1,
+                             cap_den=1),
+    # choice-order drops, raw gates, k_min 1 up to 3 experts
+    "dyn_choice_raw": DYN.scaled(T=6000, d=64, E=10, k=3, k_min=1, route_threshold=0.8,
+                                 d_ff=128, renormalize=False, drop_policy=1),
+    # no capacity limit, threshold 1: every token takes all k
+    "dyn_all": DYN.scaled(T=700, d=64, E=6, d_ff=64, cap_num=0, cap_den=0,
+                          route_threshold=1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(DYN_CASES))
+def test_dynamic_expert_count_layer(name):
+    cfg = DYN_CASES[name]
+    dev, host = gpu_inputs(cfg, seed=8)
+    out = run_layer(cfg, dev, host, full=True, seed=8, label=name)
+    kt = (out["oidx"] >= 0).sum(1)
+    assert kt.min() >= cfg.k_min and kt.max() <= cfg.k
+    if name == "dyn_all":
+        assert (kt == cfg.k).all()
+    else:
+        assert len(set(kt.tolist())) > 1, "every token took the same number of experts"
+
+
+def test_dynamic_expert_count_full_size_wide():
+    """The page's layer (128 experts, capacity factor 1.25, temperature 0.3)
+    with 2-4 experts per token, at full size, every output element."""
+    cfg = configs.WIDE_DYNAMIC
+    dev, host = gpu_inputs(cfg, seed=0)
+    out = run_layer(cfg, dev, host, full=True, seed=0, label="wide_dynamic")
+    kt = (out["oidx"] >= 0).sum(1)
+    say(f"[wide_dynamic] tokens taking 2/3/4 experts: "
+        f"{np.bincount(kt, minlength=5)[2:].tolist()}, capacity "
+        f"{oracle_capacity(cfg, out['oidx'])}, rows kept {out['n']}")
+    assert kt.min() >= 2 and kt.max() <= 4
+    st = moe.load_stats(cfg, out["dsp"]["expert_count"])
+    torch.cuda.synchronize()
+    want = orc.load_stats(out["dsp"]["expert_count"].cpu().numpy(),
+                          oracle_capacity(cfg, out["oidx"]))
+    got = st.cpu().numpy()
+    np.testing.assert_array_equal(got[[0, 1, 2, 3, 4, 6, 7]], want[[0, 1, 2, 3, 4, 6, 7]])
