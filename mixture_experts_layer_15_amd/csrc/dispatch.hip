@@ -92,15 +92,36 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ b
                                                    int cap_num, int cap_den, long long Tr) {
     __shared__ int s_wave[4];
     __shared__ long long s_red[4];
+    __shared__ int s_part[256];
+    // per-block prefix: with Ep = E rounded up to a power of two, thread
+    // (part, ex) = (tid / Ep, tid % Ep) scans a contiguous range of the nblk
+    // blocks of expert ex, so the 256 threads share the loads (a chain of nblk
+    // dependent loads per expert was the cost of this kernel)
+    int Ep = 1;
+    while (Ep < E) Ep <<= 1;
+    const int P = 256 / Ep, part = threadIdx.x / Ep, ex = threadIdx.x % Ep;
+    const int b0 = (int)((long long)nblk * part / P), b1 = (int)((long long)nblk * (part + 1) / P);
+    int psum = 0;
+    if (ex < E) {
+#pragma unroll 8
+        for (int b = b0; b < b1; ++b) psum += blockcount[b * E + ex];
+    }
+    s_part[threadIdx.x] = psum;
+    __syncthreads();
+    if (ex < E) {
+        int base = 0;
+        for (int q = 0; q < part; ++q) base += s_part[q * Ep + ex];
+#pragma unroll 8
+        for (int b = b0; b < b1; ++b) {
+            const int v = blockcount[b * E + ex];
+            blockbase[b * E + ex] = base;
+            base += v;
+        }
+    }
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-#pragma unroll 8
-        for (int b = 0; b < nblk; ++b) {
-            const int v = blockcount[b * E + e];
-            blockbase[b * E + e] = run;
-            run += v;
-        }
+        for (int q = 0; q < P; ++q) run += s_part[q * Ep + e];
         count[e] = run;
     }
     if (dyn) C = realised_capacity(block_sum256(run, s_red), cap_num, cap_den, E, Tr);
@@ -131,7 +152,8 @@ __device__ __forceinline__ void place_chunk(const int32_t* __restrict__ idx, int
                                             int (*wcnt)[256], const int32_t* offset, int n_kept,
                                             long long C, long long T, int E, int k, long long tb,
                                             int Tr, int kr, int32_t* __restrict__ row_of,
-                                            int32_t* __restrict__ token_of_row) {
+                                            int32_t* __restrict__ token_of_row,
+                                            int (*rows_out)[8] = nullptr) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int i = tid; i < 4 * 256; i += 256) (&wcnt[0][0])[i] = 0;
@@ -186,6 +208,7 @@ __device__ __forceinline__ void place_chunk(const int32_t* __restrict__ idx, int
                 }
             }
             row_of[slot_of<CM>((int)t, j, k, Tr, kr)] = row;
+            if (rows_out != nullptr) rows_out[tid][j] = row;
             // every slot index a >= rows kept is past the kept rows: mark it empty
             if (a >= n_kept) token_of_row[a] = -1;
         }
@@ -290,6 +313,97 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     __syncthreads();
     place_chunk<CM>(idx, run, wcnt, s_off, s_off[E], C, T, E, k, tb, Tr, kr, row_of,
                     token_of_row);
+}
+
+// Small batches with the scatter (compact layout): the one-launch index work
+// of dispatch_small_kernel and the copy of x rows into x_perm in one launch.
+// Each workgroup takes tpb (<= 256) consecutive walked tokens -- few enough
+// that the grid spreads the copy over the CUs -- counts all assignments
+// itself, places its tokens, keeps their rows in LDS and copies their x rows
+// (one wave per walked token, 16-byte non-temporal loads and stores).
+template <bool CM>
+__global__ __launch_bounds__(256) void dispatch_small_scatter_kernel(
+    const int32_t* __restrict__ idx, long long C, long long T, int E, int k, int Tr, int kr,
+    int32_t* __restrict__ count, int32_t* __restrict__ offset_out,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of_row, int dyn, int cap_num,
+    int cap_den, const u32x4* __restrict__ x, u32x4* __restrict__ x_perm, int nvec, int tpb) {
+    __shared__ int h_all[256], run[256];
+    __shared__ int32_t s_off[257];
+    __shared__ int wcnt[4][256];
+    __shared__ int s_wave[4];
+    __shared__ long long s_red[4];
+    __shared__ int s_rows[256][8];
+    const int tid = threadIdx.x;
+    h_all[tid] = 0;
+    run[tid] = 0;
+    __syncthreads();
+    const long long tb = (long long)blockIdx.x * tpb;
+    const long long n_assign = T * k, pre = tb * k;
+    constexpr int U = 8;
+    for (long long a0 = tid; a0 < n_assign; a0 += 256 * U) {
+        int ev[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long a = a0 + 256LL * u;
+            ev[u] = a < n_assign ? idx[CM ? slot_of<CM>((int)a, 0, 1, Tr, kr) : a] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = ev[u];
+            if ((unsigned)e < (unsigned)E) {
+                atomicAdd(&h_all[e], 1);
+                if (a0 + 256LL * u < pre) atomicAdd(&run[e], 1);
+            }
+        }
+    }
+    __syncthreads();
+    if (dyn) C = realised_capacity(block_sum256(tid < E ? h_all[tid] : 0, s_red), cap_num, cap_den,
+                                   E, Tr);
+    const int e = tid;
+    const int kept = (e < E) ? (int)min((long long)h_all[e], C) : 0;
+    const int lane = tid & 63, w = tid >> 6;
+    int v = kept;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) s_wave[w] = v;
+    __syncthreads();
+    int add = 0;
+    for (int i = 0; i < w; ++i) add += s_wave[i];
+    const int incl = v + add;
+    if (e < E) s_off[e] = incl - kept;
+    if (e == E - 1) s_off[E] = incl;
+    if (blockIdx.x == 0 && e < E) {
+        count[e] = h_all[e];
+        offset_out[e] = incl - kept;
+        if (e == E - 1) offset_out[E] = incl;
+    }
+    __syncthreads();
+    const long long te = min(T, tb + tpb);   // walked tokens of this block: [tb, te)
+    place_chunk<CM>(idx, run, wcnt, s_off, s_off[E], C, te, E, k, tb, Tr, kr, row_of,
+                    token_of_row, s_rows);
+    // place_chunk ends with a barrier: s_rows holds every token's rows
+    for (long long t = tb + w; t < te; t += 4) {
+        const int tl = (int)(t - tb);
+        const u32x4* src = x + (long long)token_of<CM>((int)t, Tr) * nvec;
+        for (int v0 = lane; v0 < nvec; v0 += 4 * 64) {
+            u32x4 val[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (v0 + u * 64 < nvec) val[u] = __builtin_nontemporal_load(src + v0 + u * 64);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j >= k) break;
+                const int r = s_rows[tl][j];
+                if (r < 0) continue;
+                u32x4* dst = x_perm + (long long)r * nvec;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (v0 + u * 64 < nvec) __builtin_nontemporal_store(val[u], dst + v0 + u * 64);
+            }
+        }
+    }
 }
 
 // One wave per token: copy x[t] to each kept row (16-byte vectors).
@@ -410,11 +524,28 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
                            void* x_perm, int32_t* count, int32_t* offset, int32_t* row_of,
                            int32_t* token_of_row, void* workspace, int d, hipStream_t s,
                            bool scatter) {
+    const int nvec = d * (dtype == 1 ? 2 : 4) / 16;
+    if (scatter && !p.padded && p.T > 0 && p.T * p.k <= kSmallAssign) {
+        // tokens per workgroup: the grid covers about 256 CUs (4 .. 256 tokens each)
+        int tpb = 4;
+        while (tpb < 256 && (p.T + tpb - 1) / tpb > 256) tpb *= 2;
+        const unsigned grid = (unsigned)((p.T + tpb - 1) / tpb);
+        if (p.choice_order)
+            hipLaunchKernelGGL(dispatch_small_scatter_kernel<true>, dim3(grid), dim3(256), 0, s, idx,
+                               p.C, p.T, p.E, p.k, (int)p.Tr, p.kr, count, offset, row_of,
+                               token_of_row, p.dyn ? 1 : 0, p.cap_num, p.cap_den, (const u32x4*)x,
+                               (u32x4*)x_perm, nvec, tpb);
+        else
+            hipLaunchKernelGGL(dispatch_small_scatter_kernel<false>, dim3(grid), dim3(256), 0, s,
+                               idx, p.C, p.T, p.E, p.k, (int)p.Tr, p.kr, count, offset, row_of,
+                               token_of_row, p.dyn ? 1 : 0, p.cap_num, p.cap_den, (const u32x4*)x,
+                               (u32x4*)x_perm, nvec, tpb);
+        return hipGetLastError();
+    }
     hipError_t err = p.choice_order
         ? dispatch_kernels<true>(p, idx, count, offset, row_of, token_of_row, workspace, s)
         : dispatch_kernels<false>(p, idx, count, offset, row_of, token_of_row, workspace, s);
     if (err != hipSuccess) return err;
-    const int nvec = d * (dtype == 1 ? 2 : 4) / 16;
     const long long padded_rows = p.padded ? p.C * p.E : 0;
     if (padded_rows > 0) {
         hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((padded_rows + 3) / 4)), dim3(256), 0,
