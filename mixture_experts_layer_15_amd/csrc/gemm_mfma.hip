@@ -510,6 +510,20 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
 //     (measured 4% faster).
 static bool tiles320(long long max_rows, int E) { return max_rows <= 2048LL * E; }
 
+// Between 320 and 640 rows per expert on average (the wide layer with 2-4
+// experts per token: about 350 rows, up to 512 by its mean bound), 320-row
+// tiles would take two M-tiles per expert, the second nearly empty, and so
+// stream every weight tile twice.  There the GEMMs take 640 x 128 tiles (four
+// waves in M, two in N, each still 160 x 64), 32-deep K-steps in rings of
+// three stages per operand: one M-tile per expert, half the weight bytes per
+// tile.  Measured with 351 rows per expert (E = 128, d = 4096, d_ff = 8192):
+// gate/up 9.67 -> 7.64 ms, down 4.60 -> 3.61 ms; at 448 rows 9.76 -> 8.98
+// and 4.53 -> 4.24 ms; at 512 rows 10.03 -> 9.75 and 4.83 -> 4.52 ms.  Rings
+// of two activation and four or eight weight stages measured 15-25% slower.
+static bool tiles640(long long max_rows, int E) {
+    return max_rows > 320LL * E && max_rows <= 640LL * E;
+}
+
 // On 256-row tiles, experts with only a few rows (a skewed layer's tail) go
 // to a second launch of 128 x 256 tiles with 32-deep K-steps and four stages
 // per operand (more weight bytes in flight per CU for tiles that are all
@@ -526,6 +540,9 @@ hipError_t launch_mfma_gate_up(const uint16_t* a, const int32_t* a_rows, const i
                                const uint16_t* w_gate,
                                const uint16_t* w_up, uint16_t* h, int E, int d, int d_ff,
                                long long max_rows, int cus, hipStream_t s) {
+    if (tiles640(max_rows, E))
+        return launch_shape<true, 10, 4, 32, 3, 3, 4>(a, w_gate, w_up, h, off, a_rows, 0, nullptr,
+                                                      0, E, d, d_ff, max_rows, cus, s);
     const bool split = split_few(max_rows, E);
     const int lo = split ? kFewRows : 0;
     const hipError_t e =
@@ -545,6 +562,9 @@ hipError_t launch_mfma_gate_up_pre(const uint16_t* a, const int32_t* a_rows, con
                                    const uint16_t* w_gate, const uint16_t* w_up, uint16_t* g,
                                    uint16_t* u, int E, int d, int d_ff, long long max_rows,
                                    int cus, hipStream_t s) {
+    if (tiles640(max_rows, E))
+        return launch_shape<true, 10, 4, 32, 3, 3, 4>(a, w_gate, w_up, g, off, a_rows, 0, nullptr,
+                                                      2, E, d, d_ff, max_rows, cus, s, u);
     const bool split = split_few(max_rows, E);
     const int lo = split ? kFewRows : 0;
     const hipError_t e =
@@ -565,6 +585,10 @@ hipError_t launch_mfma_grouped(const uint16_t* A, const int32_t* a_rows, const i
     const bool split = split_few(max_rows, E);
     const int lo = split ? kFewRows : 0;
     constexpr int HI = 0x7fffffff;
+    if (tiles640(max_rows, E))
+        return launch_shape<false, 10, 4, 32, 3, 3, 4>(A, B, nullptr, C, off, a_rows, 0, nullptr,
+                                                       0, E, K, N, max_rows, cus, s, nullptr, 0,
+                                                       HI, gate, tor, y);
     hipError_t e;
     if (!tiles320(max_rows, E))
         e = launch_shape<false, 8, 4, 64, 2, 2>(A, B, nullptr, C, off, a_rows, 0, nullptr, 0, E, K,

@@ -60,6 +60,10 @@ CASES = {
     "bw_one_expert": BASE.scaled(T=200, d=64, E=1, k=1, d_ff=64),
     # capacity 0: every assignment dropped, every gradient zero
     "bw_all_dropped": BASE.scaled(T=256, d=64, E=4, k=2, d_ff=128, cap_num=0, cap_den=1),
+    # 320-640 rows per expert on average: the forward recompute's gate/up
+    # GEMM takes its 640-row tiles (ragged last tile, d_ff not a multiple of 128)
+    "bw_tall_tiles": BASE.scaled(T=1100, d=128, E=4, k=2, d_ff=192, temperature=0.7,
+                                 renormalize=True),
     # the widest routing: 256 experts, 8 choices per token, ragged token count
     "bw_e256_k8": BASE.scaled(T=130, d=64, E=256, k=8, d_ff=64, temperature=0.5,
                               renormalize=True, cap_num=3, cap_den=2),

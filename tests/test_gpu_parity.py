@@ -152,6 +152,10 @@ SMALL = [
                                             renormalize=True, dtype="bf16", zipf_bias=2.5)),
     ("skew_320_top1", configs.get("tiny").scaled(T=2048, d=128, E=5, k=1, d_ff=192,
                                                  temperature=0.5, dtype="bf16", zipf_bias=3.0)),
+    # 320-640 rows per expert on average: 640-row tiles, with skew so that the
+    # hot experts take two or more of them and the cold ones a few rows
+    ("skew_640", configs.get("tiny").scaled(T=2000, d=192, E=8, k=2, d_ff=320, temperature=0.5,
+                                            renormalize=True, dtype="bf16", zipf_bias=2.0)),
     # top-1, every token kept, few experts: the fused forward's down GEMM in two
     # K slices (d = 320: a ragged second N-tile)
     ("split_down", configs.get("tiny").scaled(T=3000, d=320, E=6, k=1, d_ff=384,
