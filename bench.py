@@ -16,7 +16,8 @@ for at least a quarter second, which also brings the clocks up from idle)
 with HIP events recorded on the launch stream between the stages: the medians
 give each stage's time, the means the roofline of the dominant kernel (the
 gate/up GEMM with its GeGLU epilogue).  Peak probes (a streaming copy and
-read, a dense bf16 MFMA stream with clock stamps) run outside every timed
+read, a dense bf16 MFMA stream with clock stamps, and the vendor library's
+bf16 GEMM on two expert shapes as a reference) run outside every timed
 region, and the core clock is sampled from sysfs while the headline's
 timed loop runs.  The fp64 oracle is timed on the host's cores on a bounded
 token sample of each layer (`cpu_baseline`), and ranks its own fp64 logits
@@ -269,6 +270,22 @@ def run_probes(L, torch):
                                "median": round(flops / median(tm) / 1e12, 1),
                                "best": round(flops / min(tm) / 1e12, 1),
                                "core_clock_mhz_median": round(median(mhz), 1)}
+    del msink, stamps
+    # the vendor library's bf16 GEMM (torch.matmul -> hipBLASLt) on random
+    # N(0, 1) data of two expert shapes: a reference for what a tuned library
+    # reaches on this chip under its power limit, never part of the layer
+    g = torch.Generator(device="cuda").manual_seed(0)
+    ref = {}
+    for name, (bt, M, K, N) in {"long_sequence_expert_gate_up": (1, 16384, 6144, 8192),
+                                "zaya1_like_experts_gate_up": (16, 256, 2048, 16384)}.items():
+        a = torch.randn(bt, M, K, generator=g, device="cuda", dtype=torch.bfloat16)
+        b = (torch.randn(bt, K, N, generator=g, device="cuda") * K ** -0.5).to(torch.bfloat16)
+        tv = timed(lambda: torch.bmm(a, b), reps=20)
+        fl = 2.0 * bt * M * K * N
+        ref[name] = {"shape": [bt, M, K, N], "median_ms": round(median(tv) * 1e3, 4),
+                     "tflops": round(fl / median(tv) / 1e12, 1)}
+        del a, b
+    out["vendor_gemm_bf16"] = ref
     return out
 
 
@@ -560,6 +577,10 @@ def main():
     if probes and roof["unit"] == "TFLOP/s":
         roof["frac_of_measured_peak"] = round(roof["achieved"] /
                                               probes["mfma_bf16_tflops"]["median"], 4)
+        if head_cfg.name == "longseq":
+            roof["ratio_to_vendor_gemm"] = round(
+                roof["achieved"] /
+                probes["vendor_gemm_bf16"]["long_sequence_expert_gate_up"]["tflops"], 4)
     elif probes:
         roof["frac_of_measured_peak"] = round(roof["achieved"] / probes["hbm_copy_gbs"]["median"], 4)
     out = {

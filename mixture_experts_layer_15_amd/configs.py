@@ -83,4 +83,6 @@ WIDE_DYNAMIC = BY_NAME["wide"].scaled(name="wide_dynamic", k=4, k_min=2, route_t
 def get(name_or_index) -> MoEConfig:
     if isinstance(name_or_index, int):
         return CONFIGS[name_or_index]
+    if name_or_index == WIDE_DYNAMIC.name:
+        return WIDE_DYNAMIC
     return BY_NAME[name_or_index]
