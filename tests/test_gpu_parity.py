@@ -156,6 +156,16 @@ SMALL = [
     # hot experts take two or more of them and the cold ones a few rows
     ("skew_640", configs.get("tiny").scaled(T=2000, d=192, E=8, k=2, d_ff=320, temperature=0.5,
                                             renormalize=True, dtype="bf16", zipf_bias=2.0)),
+    # the validation limits: d = 16384 (router and gate/up K of 16384, down N of 16384) with
+    # the smallest d_ff (one ragged gate/up N-tile); d_ff = 65536 (down K of 65536, fused
+    # two-K-slice down GEMM) with the smallest d; the same d in fp32; E = 256 with k = 8 on
+    # the multi-block dispatch
+    ("max_d", configs.get("tiny").scaled(T=300, d=16384, E=4, k=2, d_ff=64, temperature=0.5,
+                                         renormalize=True, dtype="bf16")),
+    ("max_dff", configs.get("tiny").scaled(T=200, d=64, E=2, k=1, d_ff=65536, dtype="bf16")),
+    ("max_d_f32", configs.get("tiny").scaled(T=100, d=16384, E=3, k=1, d_ff=128)),
+    ("max_Ek_blocks", configs.get("tiny").scaled(T=3000, d=64, E=256, k=8, d_ff=64, cap_num=5,
+                                                 cap_den=4, renormalize=True, dtype="bf16")),
     # top-1, every token kept, few experts: the fused forward's down GEMM in two
     # K slices (d = 320: a ragged second N-tile)
     ("split_down", configs.get("tiny").scaled(T=3000, d=320, E=6, k=1, d_ff=384,
