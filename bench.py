@@ -324,6 +324,10 @@ def cpu_baseline(cfg, host, idx_gpu, row_of_gpu, target_s):
                 host["w_down"], logits_in=lg, tokens=toks, **kw)
     t_ffn = time.perf_counter() - t0
     total = t_route + t_ffn * cfg.T / n
+    # fp64 flops the measured work did: router logits of every token, GeGLU FFN
+    # (three d x d_ff products) of every kept assignment of the sampled tokens
+    kept_sample = int((od["row_of"][toks] >= 0).sum())
+    flops = 2.0 * cfg.T * cfg.d * cfg.E + 6.0 * cfg.d * cfg.d_ff * kept_sample
     topk_differs = ~(np.sort(idx, 1) == np.sort(idx_gpu, 1)).all(1)
     order_differs = ~(idx == idx_gpu).all(1)
     keep_differs = ((od["row_of"] >= 0) != (row_of_gpu >= 0)).any(1)
@@ -332,7 +336,8 @@ def cpu_baseline(cfg, host, idx_gpu, row_of_gpu, target_s):
             "sample": (f"fp64 oracle (C, OpenMP): logits, top-k, capacity and dispatch of all "
                        f"{cfg.T} tokens ({t_route:.2f} s) + GeGLU FFN and combine of {n} random "
                        f"tokens ({t_ffn:.2f} s), scaled to {cfg.T} tokens"),
-            "seconds_measured": round(t_route + t_ffn, 2)}
+            "seconds_measured": round(t_route + t_ffn, 2),
+            "fp64_gflops": round(flops / (t_route + t_ffn) / 1e9, 1)}
     indep = {"tokens": cfg.T,
              "tokens_with_a_different_expert_set": int(topk_differs.sum()),
              "tokens_with_a_different_choice_order": int(order_differs.sum()),
