@@ -409,7 +409,9 @@ static double gelu_grad(double v) {
  * (the step after the forward: every page trains this layer).  Routing is
  * given (idx, gate, row_of from the forward, logits the values it ranked):
  * the top-k choice and the drops are piecewise constant, so no gradient flows
- * through them.  With p = softmax(l / tau) and, per kept assignment (t, j) of
+ * through them; the same holds for a dynamic expert count, whose slots past
+ * a token's count hold -1 and take no part in any sum below.  With
+ * p = softmax(l / tau) and, per kept assignment (t, j) of
  * expert e: g = x Wg[e], u = x Wu[e], a = GELU(g), h = a * u, o = h Wd[e],
  * y_t = sum_j gate_tj o_tj:
  *   dO = gate_tj dy_t, dgate_tj = dy_t . o_tj (0 for a dropped assignment)
@@ -512,13 +514,17 @@ void orc_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t d_ff, int 
                 z += p[e];
             }
             for (int64_t e = 0; e < E; ++e) { p[e] /= z; dp[e] = 0.0; }
+            /* slots holding -1 (a token that took fewer than k experts) carry
+             * no gate and no gradient: the sums run over the chosen experts */
             if (renorm) {
                 double S = 0.0, sg = 0.0;
-                for (int64_t j = 0; j < k; ++j) S += p[idx[t * k + j]];
+                for (int64_t j = 0; j < k; ++j) if (idx[t * k + j] >= 0) S += p[idx[t * k + j]];
                 for (int64_t j = 0; j < k; ++j) sg += dga[t * k + j] * gate[t * k + j];
-                for (int64_t j = 0; j < k; ++j) dp[idx[t * k + j]] = (dga[t * k + j] - sg) / S;
+                for (int64_t j = 0; j < k; ++j)
+                    if (idx[t * k + j] >= 0) dp[idx[t * k + j]] = (dga[t * k + j] - sg) / S;
             } else {
-                for (int64_t j = 0; j < k; ++j) dp[idx[t * k + j]] = dga[t * k + j];
+                for (int64_t j = 0; j < k; ++j)
+                    if (idx[t * k + j] >= 0) dp[idx[t * k + j]] = dga[t * k + j];
             }
             double pd = 0.0;
             for (int64_t e = 0; e < E; ++e) pd += p[e] * dp[e];
@@ -556,7 +562,8 @@ void orc_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t d_ff, int 
  * gradients dgate [T][k] (0 for a dropped assignment), the same formulas as
  * in orc_backward: with p = softmax(l / tau),
  *   renormalised gates gate_j = p_j / S: dp_j = (dgate_j - sum_j' dgate_j' gate_j') / S,
- *   raw gates: dp_j = dgate_j; dp = 0 for experts not chosen;
+ *   raw gates: dp_j = dgate_j; dp = 0 for experts not chosen (slots
+ *   holding -1 choose none);
  *   dl_e = p_e (dp_e - sum_e' p_e' dp_e') / tau.
  * One token per thread, every sum in ascending index order. */
 void orc_router_backward(int64_t T, int64_t E, int64_t k, double tau, int renorm,
@@ -578,13 +585,14 @@ void orc_router_backward(int64_t T, int64_t E, int64_t k, double tau, int renorm
                 zs += q[e];
             }
             for (int64_t e = 0; e < E; ++e) { q[e] = q[e] / zs; dq[e] = 0.0; }
-            if (renorm) {
+            if (renorm) {   /* over the chosen experts: slots holding -1 are skipped */
                 double S = 0.0, dot = 0.0;
-                for (int64_t j = 0; j < k; ++j) S += q[it[j]];
+                for (int64_t j = 0; j < k; ++j) if (it[j] >= 0) S += q[it[j]];
                 for (int64_t j = 0; j < k; ++j) dot += dgate[t * k + j] * gate[t * k + j];
-                for (int64_t j = 0; j < k; ++j) dq[it[j]] = (dgate[t * k + j] - dot) / S;
+                for (int64_t j = 0; j < k; ++j)
+                    if (it[j] >= 0) dq[it[j]] = (dgate[t * k + j] - dot) / S;
             } else {
-                for (int64_t j = 0; j < k; ++j) dq[it[j]] = dgate[t * k + j];
+                for (int64_t j = 0; j < k; ++j) if (it[j] >= 0) dq[it[j]] = dgate[t * k + j];
             }
             double qd = 0.0;
             for (int64_t e = 0; e < E; ++e) qd += q[e] * dq[e];

@@ -253,10 +253,12 @@ def mlp_router(x, prev, gamma: float, eps: float, wd, bd, w1, b1, w2, b2, w3, b3
 def backward(x, w_router, bias, w_gate, w_up, w_down, dy, *, k: int, tau: float,
              renormalize: bool, cap_num: int, cap_den: int, drop_policy: int = 0,
              logits_in: Optional[np.ndarray] = None,
-             tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+             tokens: Optional[Sequence[int]] = None, k_min: int = 0,
+             threshold: float = 0.0) -> Dict[str, np.ndarray]:
     """Gradients of the layer for an upstream dy [T, d] (fp64 or castable), in
     fp64: dx, dw_router, dbias, dw_gate, dw_up, dw_down, dgate, plus the routing
-    they used.  Routing as in forward(): from logits_in when given.
+    they used.  Routing as in forward() (also the dynamic count, threshold > 0,
+    whose unused slots carry no gradient): from logits_in when given.
 
     ``tokens`` limits the computation to the listed tokens (routing, capacity
     and dispatch still cover the whole batch): only dx and dgate are returned,
@@ -272,8 +274,9 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, dy, *, k: int, tau: float,
     d_ff = wgr.shape[2]
     lg = logits(x, w_router, bias) if logits_in is None else np.asarray(logits_in, np.float64)
     lg = np.ascontiguousarray(lg)
-    idx, gate = route(lg, k, tau, renormalize)
-    C = capacity(T, E, k, cap_num, cap_den)
+    idx, gate = route(lg, k, tau, renormalize, k_min, threshold)
+    C = capacity_realised(idx, E, cap_num, cap_den) if threshold > 0 else \
+        capacity(T, E, k, cap_num, cap_den)
     dsp = dispatch(idx, E, C, drop_policy)
     dyr = np.ascontiguousarray(np.asarray(dy, dtype=np.float64))
     row_of = dsp["row_of"]

@@ -144,3 +144,65 @@ def test_token_subset_and_single_entries_match_the_full_backward():
     want = np.array([full[n][e, a, b] for n, e, a, b in ents])
     scale = max(np.abs(full[n]).max() for n in ("dw_gate", "dw_up", "dw_down"))
     np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13 * scale)
+
+
+def _counts(idx):
+    return (np.asarray(idx) >= 0).sum(axis=1)
+
+
+@pytest.mark.parametrize("renorm,cap", [(True, (0, 0)), (False, (0, 0)), (True, (3, 4))])
+def test_dynamic_count_gradients_match_finite_differences(renorm, cap):
+    # each token takes 1..3 of 4 experts (the fewest whose softmax mass reaches
+    # 0.8); the count is piecewise constant in the logits like the top-k choice,
+    # and the gates renormalise over the experts actually taken
+    T, d, E, d_ff = 9, 5, 4, 4
+    p = _layer(T, d, E, d_ff, seed=40 + int(renorm) + cap[0])
+    dy = torch.randn((T, d), generator=torch.Generator().manual_seed(41)).double().numpy()
+    kw = dict(k=3, tau=1.5, renormalize=renorm, cap_num=cap[0], cap_den=cap[1], k_min=1,
+              threshold=0.8)
+    got = _fd_check(p, dy, kw)
+    n = _counts(got["idx"])
+    assert n.min() < n.max(), n          # the counts really vary
+    if cap == (3, 4):
+        assert (got["row_of"] < 0).any() and (got["idx"] >= 0).sum() > (got["row_of"] >= 0).sum()
+
+
+def test_dynamic_count_limits_reduce_to_fixed_top_k():
+    # threshold above 1 (never reached): every token takes k experts, the
+    # capacity from the realised k T assignments is the fixed one, and the
+    # gradients are those of the fixed-k routing, bit for bit; k_min = k with a
+    # small threshold gives the same
+    T, d, E, d_ff = 16, 6, 5, 6
+    p = _layer(T, d, E, d_ff, seed=44)
+    dy = np.random.default_rng(4).standard_normal((T, d))
+    base = dict(k=3, tau=0.9, renormalize=True, cap_num=5, cap_den=4)
+    want = _grads(p, dy, **base)
+    for kmin, th in ((1, 1.5), (3, 1e-3)):
+        got = _grads(p, dy, k_min=kmin, threshold=th, **base)
+        np.testing.assert_array_equal(got["idx"], want["idx"])
+        for _, gname in NAMES + [(None, "dgate")]:
+            np.testing.assert_array_equal(got[gname], want[gname])
+    # k_min = 1 with a threshold below every top probability: top-1 routing
+    t1 = _grads(p, dy, **dict(base, k=1))
+    g1 = _grads(p, dy, k_min=1, threshold=1e-6, **base)
+    assert (_counts(g1["idx"]) == 1).all()
+    for _, gname in NAMES:
+        np.testing.assert_allclose(g1[gname], t1[gname], rtol=0,
+                                   atol=1e-12 * (np.abs(t1[gname]).max() + 1e-300))
+
+
+def test_dynamic_router_backward_alone_matches_the_full_backward():
+    # dlogit from the gate gradients alone, summed over tokens, is the full
+    # backward's dbias; x^T dlogit its router weight gradient
+    T, d, E, d_ff = 30, 8, 6, 8
+    p = _layer(T, d, E, d_ff, seed=46)
+    dy = np.random.default_rng(5).standard_normal((T, d))
+    kw = dict(k=4, tau=0.7, renormalize=True, cap_num=0, cap_den=0, k_min=2, threshold=0.8)
+    g = _grads(p, dy, **kw)
+    n = _counts(g["idx"])
+    assert n.min() == 2 and n.max() > 2
+    dl = orc.router_backward(g["logits"], g["idx"], g["gate"], g["dgate"], 0.7, True)
+    np.testing.assert_allclose(dl.sum(axis=0), g["dbias"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(p["x"].double().numpy().T @ dl, g["dw_router"], rtol=1e-11,
+                               atol=1e-13)
+    assert (g["dgate"][g["idx"] < 0] == 0).all()

@@ -89,6 +89,11 @@ MUTANTS = {
         "for (int64_t j = 0; j < kt; ++j) s += p[it[j]];",
         "for (int64_t j = 0; j < kmax; ++j) s += p[it[j]];"),
     "dynamic count: unused slots keep their expert": ("it[j] = -1;", "(void)0;"),
+    "dynamic backward: unused slots counted as expert 0": (
+        "if (idx[t * k + j] >= 0) S += p[idx[t * k + j]];",
+        "S += p[idx[t * k + j] < 0 ? 0 : idx[t * k + j]];"),
+    "dynamic router backward: unused slots counted as expert 0": (
+        "if (it[j] >= 0) S += q[it[j]];", "S += q[it[j] < 0 ? 0 : it[j]];"),
     "realised capacity floor": ("return num / den + (num % den != 0);", "return num / den;"),
     "realised capacity from the token count": ("int64_t num = cap_num * A, den = cap_den * E;",
                                                "int64_t num = cap_num * T, den = cap_den * E;"),
