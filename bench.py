@@ -441,7 +441,7 @@ def measure(cfg, args, headline: bool, clock=None):
     fused_ev = [a.elapsed_time(b) for a, b in fe]
 
     bwd_ms = None
-    if cfg.dtype == "bf16" and not args.no_backward and cfg.route_threshold == 0:
+    if cfg.dtype == "bf16" and not args.no_backward:
         dy = synthetic.make_dy(cfg, seed=1, device="cuda")
         bw = moe.Backward(cfg)
         bargs = (wr, bias, wg, wu, wd, dy)

@@ -99,7 +99,10 @@ typedef struct {
      * scales the realised mean load: C = ceil(cap_num * A / (cap_den * E))
      * for the A assignments of the batch, computed on the device
      * (moe_capacity and moe_max_rows give the bound for A = T * k).  Not with
-     * the padded layout, and not in moe_backward (MOE_ERR_UNSUPPORTED).
+     * the padded layout (MOE_ERR_UNSUPPORTED).  In moe_backward the count is
+     * piecewise constant in the logits, like the top-k choice: the unused
+     * slots carry no gradient (dgate 0) and renormalised gates are
+     * differentiated over the k_t experts taken.
      * route_threshold = 0 (with k_min = 0): every token takes k experts. */
     float route_threshold;
     int32_t k_min;
@@ -339,14 +342,16 @@ moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
  * pre-activations are recomputed from the inputs, as the activation
  * recomputation of that training page's section 4.1 does (same kernels, same
  * values as moe_forward);
- * top-k selection and capacity drops are piecewise constant, so no gradient
- * passes through them.  With p = softmax(logits / temperature), per kept
+ * top-k selection, the dynamic expert count and capacity drops are piecewise
+ * constant, so no gradient passes through them.  With
+ * p = softmax(logits / temperature), per kept
  * assignment (t, j) of expert e, g = x_t W_gate[e], u = x_t W_up[e],
  * h = GELU_erf(g) u, o = h W_down[e]:
  *   dgate[t][j] = dy_t . o (0 for a dropped assignment)
  *   dh = gate dy_t W_down[e]^T; du = dh GELU(g); dg = dh u GELU'(g)
  *   dw_down[e] += (gate h)^T dy_t, dw_gate[e] += x_t^T dg, dw_up[e] += x_t^T du
- *   gates: renormalised (gate_j = p_j / S): dp_j = (dgate_j - sum dgate gate) / S,
+ *   gates: renormalised (gate_j = p_j / S, S over the experts the token
+ *   took): dp_j = (dgate_j - sum dgate gate) / S,
  *   raw: dp_j = dgate_j; dlogit = p (dp - p . dp) / temperature
  *   dw_router = x^T dlogit, dbias = sum_t dlogit,
  *   dx_t = sum_j (dg W_gate[e]^T + du W_up[e]^T) + dlogit_t W_router^T

@@ -103,8 +103,9 @@ __global__ __launch_bounds__(256) void geglu_bwd_kernel(
 }
 
 // One wave per token: p = softmax(l / tau) from the fp32 logits, dp from the
-// gate gradients of the chosen experts (renormalised: gate_j = p_j / S,
-// dp_j = (dgate_j - sum_j' dgate_j' gate_j') / S), dl = p (dp - p . dp) / tau.
+// gate gradients of the chosen experts (renormalised: gate_j = p_j / S, S the
+// sum over the chosen ones, dp_j = (dgate_j - sum_j' dgate_j' gate_j') / S),
+// dl = p (dp - p . dp) / tau.
 __global__ __launch_bounds__(256) void router_bwd_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const int32_t* __restrict__ row_of,
@@ -143,7 +144,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // every lane walks the k choices (k <= 8)
+    // every lane walks the k choices (k <= 8); a slot holding -1 (a token
+    // that took fewer than k experts) has no expert, gate 0 and no gradient
     float S = 0.f, sg = 0.f;
     float dga[8];
     int ej[8];
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
             const int rr = row_of[a];
             dga[j] = rr >= 0 ? dgate_row[rr] : 0.f;
             ej[j] = idx[a];
-            S += sp[w][ej[j]];
+            if (ej[j] >= 0) S += sp[w][ej[j]];
             sg = fmaf(dga[j], gate[a], sg);
         }
     }

@@ -637,8 +637,6 @@ BwdLayout bwd_layout(const moe_config* c) {
 moe_status check_bwd(const moe_config* cfg) {
     CHECK(check_cfg(cfg));
     if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
-    if (dyn_route(cfg))
-        return fail(MOE_ERR_UNSUPPORTED, "the backward runs on a fixed expert count per token only");
     if (cfg->layout != MOE_LAYOUT_COMPACT)
         return fail(MOE_ERR_UNSUPPORTED, "the backward runs on the compact layout only");
     return MOE_OK;

@@ -332,7 +332,8 @@ def test_bench_refuses_more_than_one_gpu():
 
 def test_dynamic_expert_count_validation_on_host(L):
     # each token takes k_min .. k experts by a softmax-mass threshold: host
-    # checks of its fields, and the places it is not supported (no GPU call)
+    # checks of its fields, and the one place it is not supported, the padded
+    # layout (no GPU call)
     cfg = configs.get("tiny").scaled(dtype="bf16", k=4, E=16, k_min=2, route_threshold=0.6,
                                      renormalize=True, cap_num=5, cap_den=4)
     ok = ctypes.c_void_p(1 << 20)
@@ -340,8 +341,14 @@ def test_dynamic_expert_count_validation_on_host(L):
     assert L.moe_workspace_size(ctypes.byref(moe.cconfig(cfg)), ctypes.byref(n)) == moe.MOE_OK
     # capacity and rows: the bound for T * k assignments
     assert moe.capacity(cfg) == orc.capacity(cfg.T, cfg.E, cfg.k, 5, 4)
+    # the backward runs it too, with the workspace of the fixed-k layer (rows
+    # bounded by the same capacity)
+    nb = ctypes.c_size_t(0)
+    fixed = moe.cconfig(cfg.scaled(k_min=0, route_threshold=0.0))
     assert L.moe_backward_workspace_size(ctypes.byref(moe.cconfig(cfg)), ctypes.byref(n)) == \
-        moe.MOE_ERR_UNSUPPORTED
+        moe.MOE_OK
+    assert L.moe_backward_workspace_size(ctypes.byref(fixed), ctypes.byref(nb)) == moe.MOE_OK
+    assert n.value == nb.value > 0
     pad = moe.cconfig(cfg.scaled(layout=1))
     assert L.moe_workspace_size(ctypes.byref(pad), ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
     for bad in (cfg.scaled(k_min=0), cfg.scaled(k_min=5), cfg.scaled(route_threshold=1.5),
