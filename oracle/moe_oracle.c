@@ -360,6 +360,36 @@ void orc_load_stats(int64_t E, const int32_t* count, int64_t C, double* out) {
     out[7] = empty;
 }
 
+/* The MLP router's load-balance controller: a PID controller on the expert
+ * load ("AMD MI300X平台上的MoE模型训练实践", section 3.2, names a PID balance
+ * controller acting on the router logits; its training notes raise the PID
+ * gains over a warmup).  The page gives no update rule; the reading here is
+ * the textbook discrete PID loop, one per expert, on the relative load error,
+ * whose output is the additive logit bias.  One update per training step
+ * from that step's counts before drops:
+ *   m = sum_e count_e / E;  err_e = (m - count_e) / m  (0 for every e when m = 0)
+ *   I_e <- I_e + err_e;  D_e = err_e - prev_e
+ *   bias_e = scale * (kp * err_e + ki * I_e + kd * D_e);  prev_e <- err_e
+ * state [2][E]: row 0 holds I, row 1 prev (zero before the first step).  An
+ * expert below the mean load gets a positive error, so its bias rises. */
+void orc_pid_update(int64_t E, double kp, double ki, double kd, double scale,
+                    const int32_t* count, double* state, double* bias) {
+    double sum = 0.0;
+    for (int64_t e = 0; e < E; ++e) sum += (double)count[e];
+    double mean = sum / (double)E;
+    for (int64_t e = 0; e < E; ++e) {
+        double err = mean > 0 ? (mean - (double)count[e]) / mean : 0.0;
+        double integral = state[e] + err;
+        double deriv = err - state[E + e];
+        double p_term = kp * err;
+        double i_term = ki * integral;
+        double d_term = kd * deriv;
+        bias[e] = scale * ((p_term + i_term) + d_term);
+        state[e] = integral;
+        state[E + e] = err;
+    }
+}
+
 /* Step 5 -- the GeGLU expert FFN for a list of (token, expert) rows.
  * For row r (token t = tok[r], expert e = ex[r]):
  *   g[n] = sum_i x[t][i] * Wg[e][i][n],  u[n] = sum_i x[t][i] * Wu[e][i][n],

@@ -67,6 +67,8 @@ def _declare(lib):
     lib.orc_dispatch.restype = None
     lib.orc_load_stats.argtypes = [_I64, _P, _I64, _P]
     lib.orc_load_stats.restype = None
+    lib.orc_pid_update.argtypes = [_I64] + [ctypes.c_double] * 4 + [_P, _P, _P]
+    lib.orc_pid_update.restype = None
     lib.orc_mlp_router.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int, _P, _P,
                                    ctypes.c_double, ctypes.c_double] + [_P] * 13
     lib.orc_mlp_router.restype = None
@@ -354,6 +356,21 @@ def load_stats(count: np.ndarray, C: int) -> np.ndarray:
     out = np.empty(8, dtype=np.float64)
     _load().orc_load_stats(count.shape[0], _ptr(count), int(C), _ptr(out))
     return out
+
+
+def pid_update(count: np.ndarray, state: np.ndarray, kp: float, ki: float, kd: float,
+               scale: float = 1.0):
+    """One step of the load-balance PID controller (see orc_pid_update):
+    returns (new state [2, E], bias [E]) in fp64; the input state is not
+    modified."""
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    E = count.shape[0]
+    st = np.array(state, dtype=np.float64, copy=True).reshape(2, E)
+    st = np.ascontiguousarray(st)
+    bias = np.empty(E, dtype=np.float64)
+    _load().orc_pid_update(E, float(kp), float(ki), float(kd), float(scale), _ptr(count),
+                           _ptr(st), _ptr(bias))
+    return st, bias
 
 
 def forward(x, w_router, bias, w_gate, w_up, w_down, *, k: int, tau: float,

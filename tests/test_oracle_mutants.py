@@ -16,7 +16,8 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
         os.path.join(ROOT, "tests", "test_oracle_backward.py"),
         os.path.join(ROOT, "tests", "test_oracle_by_expert.py"),
-        os.path.join(ROOT, "tests", "test_oracle_dynamic.py")]
+        os.path.join(ROOT, "tests", "test_oracle_dynamic.py"),
+        os.path.join(ROOT, "tests", "test_oracle_pid.py")]
 
 MUTANTS = {
     "bias dropped": ("if (bias) s += (double)bias[e];", "if (0) s += (double)bias[e];"),
@@ -94,6 +95,19 @@ MUTANTS = {
         "S += p[idx[t * k + j] < 0 ? 0 : idx[t * k + j]];"),
     "dynamic router backward: unused slots counted as expert 0": (
         "if (it[j] >= 0) S += q[it[j]];", "S += q[it[j] < 0 ? 0 : it[j]];"),
+    "PID error sign flipped": (
+        "double err = mean > 0 ? (mean - (double)count[e]) / mean : 0.0;",
+        "double err = mean > 0 ? ((double)count[e] - mean) / mean : 0.0;"),
+    "PID error not relative": (
+        "double err = mean > 0 ? (mean - (double)count[e]) / mean : 0.0;",
+        "double err = mean > 0 ? (mean - (double)count[e]) : 0.0;"),
+    "PID integral not accumulated": ("double integral = state[e] + err;", "double integral = err;"),
+    "PID derivative reversed": ("double deriv = err - state[E + e];",
+                                "double deriv = state[E + e] - err;"),
+    "PID warmup scale skips the derivative": (
+        "bias[e] = scale * ((p_term + i_term) + d_term);",
+        "bias[e] = scale * (p_term + i_term) + d_term;"),
+    "PID previous error not kept": ("state[E + e] = err;", "state[E + e] = 0.0;"),
     "realised capacity floor": ("return num / den + (num % den != 0);", "return num / den;"),
     "realised capacity from the token count": ("int64_t num = cap_num * A, den = cap_den * E;",
                                                "int64_t num = cap_num * T, den = cap_den * E;"),
