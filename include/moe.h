@@ -282,6 +282,35 @@ moe_status moe_dispatch_noalloc(const moe_config* cfg, const int32_t* topk_idx, 
 moe_status moe_load_stats(const moe_config* cfg, const int32_t* expert_count, double* stats,
                           void* stream);
 
+/* The MLP router's load-balance controller: one step of a PID controller on
+ * the expert load ("AMD MI300X平台上的MoE模型训练实践", section 3.2, puts a
+ * PID balance controller on the router logits; its training notes raise the
+ * PID gains over a warmup).  The page gives no update rule; the one here is
+ * the textbook discrete PID loop, one per expert, on the relative load error,
+ * and its output is the additive logit bias that moe_mlp_router.pid_bias
+ * takes.  Called once per training step with that step's counts before drops
+ * (expert_count as written by moe_dispatch):
+ *   m = sum_e count_e / E;  err_e = (m - count_e) / m  (0 when m = 0)
+ *   I_e <- I_e + err_e;     D_e = err_e - prev_e;      prev_e <- err_e
+ *   pid_bias_e = scale * ((kp err_e + ki I_e) + kd D_e), rounded once to fp32
+ * An expert below the mean load gets a positive error, so its bias rises.
+ *   expert_count [E]     int32 in
+ *   state        [2, E]  fp64  in/out  row 0 the integrals I, row 1 the
+ *                                      previous errors; zero before the first
+ *                                      step (its D is then err itself)
+ *   pid_bias     [E]     fp32  out
+ * gains: kp, ki, kd and scale finite (MOE_ERR_INVALID_ARG otherwise); scale
+ * ramps the controller's output during a warmup (0 = off, 1 = full gains).
+ * One workgroup, fp64 throughout, each operation rounded once in the order
+ * written. */
+typedef struct {
+    double kp, ki, kd;
+    double scale;
+} moe_pid_gains;
+moe_status moe_pid_update(const moe_config* cfg, const moe_pid_gains* gains,
+                          const int32_t* expert_count, double* state, float* pid_bias,
+                          void* stream);
+
 /* Step 6: grouped GeGLU expert FFN over the permuted rows.
  *   x_perm        [max_rows, d]    dtype in   (rows past expert_offset[E] ignored)
  *   expert_offset [E + 1]          int32 in   as written by moe_dispatch

@@ -28,8 +28,8 @@ EXPORTS = ("moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_dispatch_w
            "moe_last_error", "moe_route", "moe_route_from_logits", "moe_dispatch",
            "moe_dispatch_noalloc",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_forward", "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",
-           "moe_backward_workspace_size", "moe_backward",
+           "moe_forward", "moe_load_stats", "moe_pid_update", "moe_mlp_router_workspace_size",
+           "moe_route_mlp", "moe_backward_workspace_size", "moe_backward",
            # measurement probes (include/moe_probe.h)
            "moe_probe_copy", "moe_probe_read", "moe_probe_mfma")
 
@@ -52,6 +52,12 @@ class CMLPRouter(ctypes.Structure):
                 ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("b2", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("b3", ctypes.c_void_p),
                 ("pid_bias", ctypes.c_void_p)]
+
+
+class CPIDGains(ctypes.Structure):
+    """Mirror of moe_pid_gains (include/moe.h)."""
+    _fields_ = [("kp", ctypes.c_double), ("ki", ctypes.c_double), ("kd", ctypes.c_double),
+                ("scale", ctypes.c_double)]
 
 
 class MoEError(RuntimeError):
@@ -95,6 +101,7 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [cp, _P, _P, _P, _P, _P]
         L.moe_forward.argtypes = [cp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_load_stats.argtypes = [cp, _P, _P, _P]
+        L.moe_pid_update.argtypes = [cp, ctypes.POINTER(CPIDGains), _P, _P, _P, _P]
         rp = ctypes.POINTER(CMLPRouter)
         L.moe_mlp_router_workspace_size.argtypes = [cp, rp, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_route_mlp.argtypes = [cp, rp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -103,7 +110,8 @@ def lib() -> ctypes.CDLL:
         for n in ("moe_route", "moe_route_from_logits", "moe_dispatch", "moe_dispatch_noalloc",
                   "moe_expert_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
-                  "moe_load_stats", "moe_mlp_router_workspace_size", "moe_route_mlp",
+                  "moe_load_stats", "moe_pid_update", "moe_mlp_router_workspace_size",
+                  "moe_route_mlp",
                   "moe_backward_workspace_size", "moe_backward",
            # measurement probes (include/moe_probe.h)
            "moe_probe_copy", "moe_probe_read", "moe_probe_mfma"):
@@ -296,6 +304,22 @@ def load_stats(cfg: MoEConfig, expert_count):
     _check(lib().moe_load_stats(ctypes.byref(cconfig(cfg)), _ptr(expert_count), _ptr(stats),
                                 _stream()), "moe_load_stats")
     return stats
+
+
+def pid_update(cfg: MoEConfig, expert_count, state, kp: float, ki: float, kd: float,
+               scale: float = 1.0):
+    """moe_pid_update: one step of the load-balance PID controller.  state
+    [2, E] fp64 (integrals, previous errors) is updated in place; returns the
+    logit bias pid_bias [E] fp32."""
+    import torch
+    dev = expert_count.device
+    _need(expert_count, "expert_count", torch.int32, (cfg.E,), dev)
+    _need(state, "state", torch.float64, (2, cfg.E), dev)
+    bias = _out(cfg.E, torch.float32, dev)
+    g = CPIDGains(kp=float(kp), ki=float(ki), kd=float(kd), scale=float(scale))
+    _check(lib().moe_pid_update(ctypes.byref(cconfig(cfg)), ctypes.byref(g), _ptr(expert_count),
+                                _ptr(state), _ptr(bias), _stream()), "moe_pid_update")
+    return bias
 
 
 def expert_ffn(cfg: MoEConfig, x_perm, expert_offset, w_gate, w_up, w_down) -> Tuple:

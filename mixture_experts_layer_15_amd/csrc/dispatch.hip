@@ -624,6 +624,35 @@ __global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restri
     }
 }
 
+// Load-balance PID controller, one workgroup, one thread per expert, fp64
+// (update rule as documented at moe_pid_update).  No contraction into fused
+// multiply-adds: every operation rounds once, in the documented order.
+__global__ __launch_bounds__(256) void pid_update_kernel(const int32_t* __restrict__ count, int E,
+                                                         double kp, double ki, double kd,
+                                                         double scale, double* __restrict__ state,
+                                                         float* __restrict__ bias) {
+#pragma clang fp contract(off)
+    __shared__ long long s_red[4];
+    const int e = threadIdx.x;
+    const long long tot = block_sum256(e < E ? count[e] : 0, s_red);   // exact
+    if (e >= E) return;
+    const double mean = (double)tot / (double)E;
+    const double err = mean > 0 ? (mean - (double)count[e]) / mean : 0.0;
+    const double integral = state[e] + err;
+    const double deriv = err - state[E + e];
+    const double p_term = kp * err, i_term = ki * integral, d_term = kd * deriv;
+    bias[e] = (float)(scale * ((p_term + i_term) + d_term));
+    state[e] = integral;
+    state[E + e] = err;
+}
+
+hipError_t launch_pid_update(const int32_t* count, int E, double kp, double ki, double kd,
+                             double scale, double* state, float* bias, hipStream_t s) {
+    hipLaunchKernelGGL(pid_update_kernel, dim3(1), dim3(256), 0, s, count, E, kp, ki, kd, scale,
+                       state, bias);
+    return hipGetLastError();
+}
+
 hipError_t launch_load_stats(const int32_t* count, int E, long long C, double* stats,
                              hipStream_t s, bool dyn, int cap_num, int cap_den, long long T) {
     hipLaunchKernelGGL(load_stats_kernel, dim3(1), dim3(256), 0, s, count, E, C, stats,

@@ -65,6 +65,9 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
 hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, void* x_perm, long long T,
                                int row_bytes, int k, hipStream_t s);
 
+// Load-balance PID controller step (see moe_pid_update); E <= 256.
+hipError_t launch_pid_update(const int32_t* count, int E, double kp, double ki, double kd,
+                             double scale, double* state, float* bias, hipStream_t s);
 // Expert-load telemetry (8 fp64 values, see moe_load_stats).
 hipError_t launch_load_stats(const int32_t* count, int E, long long C, double* stats,
                              hipStream_t s, bool dyn = false, int cap_num = 0, int cap_den = 0,

@@ -531,6 +531,26 @@ moe_status moe_load_stats(const moe_config* cfg, const int32_t* expert_count, do
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_load_stats");
 }
 
+moe_status moe_pid_update(const moe_config* cfg, const moe_pid_gains* gains,
+                          const int32_t* expert_count, double* state, float* pid_bias,
+                          void* stream) {
+    CHECK(check_cfg(cfg));
+    const size_t E = (size_t)cfg->E;
+    if (gains == nullptr) return fail(MOE_ERR_INVALID_ARG, "gains is NULL");
+    const double g[4] = {gains->kp, gains->ki, gains->kd, gains->scale};
+    for (double v : g)
+        if (!std::isfinite(v)) return fail(MOE_ERR_INVALID_ARG, "PID gains and scale must be finite");
+    if (expert_count == nullptr) return fail(MOE_ERR_INVALID_ARG, "expert_count is NULL");
+    CHECK(check_ptr(expert_count, "expert_count", E * 4));
+    if (state == nullptr) return fail(MOE_ERR_INVALID_ARG, "state is NULL");
+    CHECK(check_ptr(state, "state", 2 * E * sizeof(double)));
+    if (pid_bias == nullptr) return fail(MOE_ERR_INVALID_ARG, "pid_bias is NULL");
+    CHECK(check_ptr(pid_bias, "pid_bias", E * 4));
+    hipError_t e = moe::launch_pid_update(expert_count, cfg->E, gains->kp, gains->ki, gains->kd,
+                                          gains->scale, state, pid_bias, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_pid_update");
+}
+
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* bias, const void* w_gate, const void* w_up,
                        const void* w_down, void* y, void* workspace, size_t ws_bytes,

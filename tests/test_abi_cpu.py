@@ -356,3 +356,24 @@ def test_dynamic_expert_count_validation_on_host(L):
                 cfg.scaled(route_threshold=-0.5)):
         assert L.moe_route(ctypes.byref(moe.cconfig(bad)), ok, ok, None, ok, ok, ok, None) == \
             moe.MOE_ERR_INVALID_ARG
+
+
+def test_pid_update_validation_on_host(L):
+    # the load-balance PID controller: NULL and non-finite arguments are
+    # rejected before any launch
+    cfg = moe.cconfig(configs.get("tiny").scaled(E=16, k=2))
+    ok = ctypes.c_void_p(1 << 20)
+    good = moe.CPIDGains(kp=0.2, ki=0.02, kd=0.0, scale=1.0)
+    inv = moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pid_update(ctypes.byref(cfg), None, ok, ok, ok, None) == inv
+    for f in ("kp", "ki", "kd", "scale"):
+        for v in (float("nan"), float("inf")):
+            g = moe.CPIDGains(kp=0.2, ki=0.02, kd=0.0, scale=1.0)
+            setattr(g, f, v)
+            assert L.moe_pid_update(ctypes.byref(cfg), ctypes.byref(g), ok, ok, ok, None) == inv
+            assert f in L.moe_last_error().decode() or "finite" in L.moe_last_error().decode()
+    for args in ((None, ok, ok), (ok, None, ok), (ok, ok, None)):
+        assert L.moe_pid_update(ctypes.byref(cfg), ctypes.byref(good), *args, None) == inv
+    bad = moe.cconfig(configs.get("tiny").scaled(E=16, k=2))
+    bad.E = 0
+    assert L.moe_pid_update(ctypes.byref(bad), ctypes.byref(good), ok, ok, ok, None) == inv

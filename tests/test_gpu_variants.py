@@ -90,6 +90,60 @@ def test_load_stats_edge_counts():
         np.testing.assert_allclose(st.cpu().numpy(), want, rtol=1e-12, atol=0)
 
 
+# ---------------------------------------------------------------- PID controller
+# The MLP router's load-balance controller (one PID loop per expert on the
+# relative load error, output the additive logit bias): fp64 on both sides,
+# every operation rounded once in the same order, so the state must match the
+# oracle exactly and the fp32 bias is the oracle's value rounded once.
+@pytest.mark.parametrize("E", [1, 5, 64, 256])
+def test_pid_controller_matches_the_oracle(E):
+    cfg = configs.get("tiny").scaled(E=E, k=1)
+    rng = np.random.default_rng(E)
+    st_dev = torch.zeros((2, E), dtype=torch.float64, device="cuda")
+    st_orc = np.zeros((2, E))
+    say(f"[pid E={E}] six steps of moe_pid_update")
+    for step in range(6):
+        if step == 3:
+            cnt = np.zeros(E, np.int32)                     # no assignments at all
+        else:
+            cnt = rng.integers(0, 3000, E).astype(np.int32)
+            cnt[rng.integers(0, E)] = 0                     # an idle expert
+        kp, ki, kd = rng.uniform(0, 1, 3)
+        scale = min(1.0, (step + 1) / 4)
+        bias = moe.pid_update(cfg, torch.from_numpy(cnt).cuda(), st_dev, kp, ki, kd, scale)
+        st_orc, b_orc = orc.pid_update(cnt, st_orc, kp, ki, kd, scale)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(st_dev.cpu().numpy(), st_orc)
+        np.testing.assert_array_equal(bias.cpu().numpy(), b_orc.astype(np.float32))
+
+
+def test_pid_controller_closed_loop_on_the_gpu_router():
+    """The controller fed back through the layer's own router and dispatch:
+    a Zipf-skewed top-2 routing (about 30% of tokens choose expert 0) evens
+    out, and every step's controller output equals the oracle's."""
+    cfg = configs.get("skewed").scaled(T=8192, d=256, d_ff=64)
+    dev, _ = gpu_inputs(cfg, seed=0)
+    E = cfg.E
+    st_dev = torch.zeros((2, E), dtype=torch.float64, device="cuda")
+    st_orc = np.zeros((2, E))
+    base = dev["bias"].clone()
+    pid = torch.zeros(E, dtype=torch.float32, device="cuda")
+    cv = []
+    say("[pid loop] 80 steps of route, dispatch, moe_pid_update")
+    for step in range(80):
+        _, idx, _ = moe.route(cfg, dev["x"], dev["w_router"], base + pid)
+        cnt = moe.dispatch(cfg, idx, dev["x"])["expert_count"]
+        c = cnt.cpu().numpy()
+        cv.append(float(c.std() / c.mean()))
+        scale = min(1.0, (step + 1) / 10)
+        pid = moe.pid_update(cfg, cnt, st_dev, 0.2, 0.02, 0.0, scale)
+        st_orc, b_orc = orc.pid_update(c, st_orc, 0.2, 0.02, 0.0, scale)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(pid.cpu().numpy(), b_orc.astype(np.float32))
+    say(f"[pid loop] load CV (std / mean): step 0 {cv[0]:.3f}, step 79 {cv[-1]:.3f}")
+    assert cv[0] > 1.0 and cv[-1] < 0.15, cv
+
+
 # ---------------------------------------------------------------- MLP router
 # Logits of a bf16 network (four intermediate roundings): compared with the
 # R13 metric at the layer's bf16 tolerance; the top-k and gates then follow the
