@@ -377,6 +377,61 @@ __global__ __launch_bounds__(256, 2) void dwr_part_kernel(
         }
 }
 
+// The same partial sums for layers with few experts (E <= TE, TE = 8 or 16):
+// a thread owns 8 consecutive columns i and all TE experts, so every x
+// element is read once, straight from global memory (16 bytes per thread and
+// token, a workgroup covering 2048 columns), and the dl row of each token is
+// uniform across the workgroup.  Tokens of the split ascending, four at a
+// time so that four x loads are in flight.  The 64-expert tile of
+// dwr_part_kernel would spend 64 / E of its multiply-adds on padding here.
+template <int TE>
+__global__ __launch_bounds__(256) void dwr_narrow_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ dl, float* __restrict__ part,
+    float* __restrict__ bpart, long long T, int d, int E, long long split) {
+    const int tid = threadIdx.x;
+    const int i0 = blockIdx.x * 2048 + tid * 8;
+    const int s = blockIdx.z;
+    const long long ta = (long long)s * split, tb = min(T, ta + split);
+    const bool active = i0 < d;   // d % 64 == 0: whole 8-column groups
+    float acc[8][TE] = {};
+    float bacc[TE] = {};
+    for (long long t0 = ta; t0 < tb; t0 += 4) {
+        u32x4 raw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const long long t = t0 + q;
+            raw[q] = (active && t < tb) ? *(const u32x4*)(x + t * d + i0) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const long long t = t0 + q;
+            if (t >= tb) break;   // uniform
+            float b[TE];
+#pragma unroll
+            for (int e = 0; e < TE; ++e) b[e] = e < E ? dl[t * E + e] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float a = Elem<uint16_t>::to_f32(raw[q], u);
+#pragma unroll
+                for (int e = 0; e < TE; ++e) acc[u][e] = fmaf(a, b[e], acc[u][e]);
+            }
+#pragma unroll
+            for (int e = 0; e < TE; ++e) bacc[e] += b[e];
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < TE; ++e)
+                if (e < E) part[((long long)s * d + i0 + u) * E + e] = acc[u][e];
+    }
+    if (blockIdx.x == 0 && tid == 0)
+#pragma unroll
+        for (int e = 0; e < TE; ++e)
+            if (e < E) bpart[(long long)s * E + e] = bacc[e];
+}
+
 // Sum of the splits in split order: dwr [d][E], dbias [E] (may be null).
 __global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* __restrict__ part,
                                                          const float* __restrict__ bpart,
@@ -442,8 +497,13 @@ hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp, int 
     return hipGetLastError();
 }
 
+// Few experts: dwr_narrow_kernel (2048 columns per workgroup), else
+// dwr_part_kernel (256 columns x 64 experts).
+static bool dwr_narrow(int E) { return E <= 16; }
+
 int dwr_splits(long long T, int d, int E) {
-    const long long tiles = (long long)((d + 255) / 256) * ((E + 63) / 64);
+    const long long tiles = dwr_narrow(E) ? (long long)((d + 2047) / 2048)
+                                          : (long long)((d + 255) / 256) * ((E + 63) / 64);
     long long ns = (512 + tiles - 1) / tiles;   // about two workgroups per CU
     ns = std::min<long long>(ns, std::max<long long>(1, (T + 63) / 64));
     return (int)std::max<long long>(1, std::min<long long>(ns, 4096));
@@ -461,8 +521,15 @@ hipError_t launch_dwr(const uint16_t* x, const float* dl, float* dwr, float* dbi
     const long long split = T == 0 ? 1 : ((T + ns - 1) / ns + 15) / 16 * 16;
     float* part = (float*)ws;
     float* bpart = part + (size_t)ns * d * E;
-    hipLaunchKernelGGL(dwr_part_kernel, dim3((d + 255) / 256, (E + 63) / 64, ns), dim3(256), 0, s, x, dl,
-                       part, bpart, T, d, E, split);
+    if (dwr_narrow(E) && E <= 8)
+        hipLaunchKernelGGL(dwr_narrow_kernel<8>, dim3((d + 2047) / 2048, 1, ns), dim3(256), 0, s,
+                           x, dl, part, bpart, T, d, E, split);
+    else if (dwr_narrow(E))
+        hipLaunchKernelGGL(dwr_narrow_kernel<16>, dim3((d + 2047) / 2048, 1, ns), dim3(256), 0,
+                           s, x, dl, part, bpart, T, d, E, split);
+    else
+        hipLaunchKernelGGL(dwr_part_kernel, dim3((d + 255) / 256, (E + 63) / 64, ns), dim3(256),
+                           0, s, x, dl, part, bpart, T, d, E, split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long n = (long long)d * E + E;

@@ -98,6 +98,17 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     constexpr bool KROW = MODE == 1;
     static_assert(!KROW || BM != 320, "320-row tiles only with K-contiguous (NT) operands");
     constexpr int MI = S::MI, NJ = S::NJ;
+    // NT spreads each wave's loads of the next stage over the first half of
+    // the current stage's MFMA slots (one (K-step, row block) pair per slot),
+    // so that they do not back up the vector memory queue in one burst and
+    // still have half a stage to land (long-sequence layer: dh 5.46 -> 5.24
+    // ms, dx rows 10.26 -> 9.65 ms; the wide layer's dx rows 4.90 -> 4.64 ms).
+    // TN keeps one burst: spread over its three-stage ring it measured 1-3%
+    // slower.
+    constexpr bool SPREAD = MODE == 0 && NS == 2;
+    constexpr int STRIDE0 = S::KS * MI / S::LOADS / 2;
+    constexpr int STRIDE = STRIDE0 > 0 ? STRIDE0 : 1;
+    static_assert(!SPREAD || S::KS * MI >= STRIDE * S::LOADS, "a slot per wave-load");
     __shared__ __attribute__((aligned(1024))) char sa0[S::A_STAGE];
     __shared__ __attribute__((aligned(1024))) char sa1[S::A_STAGE];
     __shared__ __attribute__((aligned(1024))) char sa2[S::A_STAGE];
@@ -199,8 +210,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
         const i32x4 rs_b1 =
             two ? buffer_rsrc(ops.B[1] + ((long long)e * N + n0) * K + k_beg) : rs_b0;
 
-        // all loads of K-step kt into stage buffers (la, lb)
-        auto issue = [&](int kt, uint32_t la, uint32_t lb) {
+        // the loads of K-step kt into stage buffers (la, lb): all of them, or
+        // only wave-load number only_q (A loads first, then B)
+        auto issue = [&](int kt, uint32_t la, uint32_t lb, int only_q = -1) {
             const bool second = two && kt >= nks;            // uniform
             const int k0 = (second ? kt - nks : kt) * TK;
             i32x4 ra = second ? rs_a1 : rs_a0, rb = second ? rs_b1 : rs_b0;
@@ -218,10 +230,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
             }
 #pragma unroll
             for (int q = 0; q < S::A_WL; ++q)
-                load_to_lds(ra, l_off[q], so, la + (w * S::A_WL + q) * 1024);
+                if (only_q < 0 || only_q == q)
+                    load_to_lds(ra, l_off[q], so, la + (w * S::A_WL + q) * 1024);
 #pragma unroll
             for (int q = 0; q < S::B_WL; ++q)
-                load_to_lds(rb, l_off[S::A_WL + q], so, lb + (w * S::B_WL + q) * 1024);
+                if (only_q < 0 || only_q == S::A_WL + q)
+                    load_to_lds(rb, l_off[S::A_WL + q], so, lb + (w * S::B_WL + q) * 1024);
         };
 
         // per-lane fragment read offsets (lane constants)
@@ -274,9 +288,10 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
                 }
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
-                if (k + NS - 1 < nk)
-                    issue(k + NS - 1, lds_base(abuf[(s + NS - 1) % NS]),
-                          lds_base(bbuf[(s + NS - 1) % NS]));
+                const bool refill = k + NS - 1 < nk;
+                const uint32_t rla = lds_base(abuf[(s + NS - 1) % NS]);
+                const uint32_t rlb = lds_base(bbuf[(s + NS - 1) % NS]);
+                if (!SPREAD && refill) issue(k + NS - 1, rla, rlb);
                 const char* sa = abuf[s];
                 const char* sb = bbuf[s];
 #pragma unroll
@@ -286,6 +301,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
                     for (int j = 0; j < NJ; ++j) fb[j] = frag(sb, (wn * NJ + j) * 16, BN * 2, ks);
 #pragma unroll
                     for (int i = 0; i < MI; ++i) {
+                        if (SPREAD && refill) {
+                            const int slot = ks * MI + i;
+                            if (slot % STRIDE == 0 && slot / STRIDE < S::LOADS)
+                                issue(k + NS - 1, rla, rlb, slot / STRIDE);
+                        }
                         const bf16x8 fa = frag(sa, (wm * MI + i) * 16, BM * 2, ks);
 #pragma unroll
                         for (int j = 0; j < NJ; ++j)
