@@ -195,18 +195,32 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
 // (hi = bf16(dl), lo = bf16(dl - hi): about 16 bits of dl, W_r exact), both
 // operands read from global memory straight into the fragment layout (lane
 // (c16, g4): index c16, K values 8 g4 .. + 7).  Workgroup: 64 tokens x 256
-// columns, each wave 64 x 64 (4 x 4 blocks of 16 x 16).  VEC: E % 8 == 0, so
-// eight K values are one aligned vector.
+// columns, each wave 64 x 64 (4 x 4 blocks of 16 x 16).  The expert parts are
+// then added to the accumulators where they lie (each lane four consecutive
+// columns of one token), with no trip through LDS, at three waves per SIMD
+// (long-sequence layer 1.49 -> 0.94 ms against a version that staged the
+// router part through LDS and added one token row per wave).  VEC: E % 8 ==
+// 0, so eight K values are one aligned vector.
 template <bool VEC>
-__global__ __launch_bounds__(256) void dx_kernel(
+__global__ __launch_bounds__(256, 3) void dx_kernel(
     const float* __restrict__ dl, const uint16_t* __restrict__ wr,
     const float* __restrict__ dXp, int nparts, long long part_stride,
     const int32_t* __restrict__ row_of, uint16_t* __restrict__ dx, long long T, int d, int E,
     int k) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c16 = lane & 15, g4 = lane >> 4;
     const long long t0 = (long long)blockIdx.x * 64;
     const int i0 = blockIdx.y * 256 + w * 64;
+    // the expert rows of this lane's four tokens t0 + 16 ib + c16 (k <= 8),
+    // loaded before the router product so that their latency is hidden; -1
+    // past the last token and for dropped assignments
+    int rj[4][8];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+        const long long t = t0 + ib * 16 + c16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rj[ib][j] = j < k && t < T ? row_of[t * k + j] : -1;
+    }
     f32x4 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -266,42 +280,35 @@ __global__ __launch_bounds__(256) void dx_kernel(
             }
         }
     }
-    // router part through LDS (lane (g4, c16) of block (ib, jb): token
-    // ib*16 + c16, columns jb*16 + 4 g4 .. + 3), then one wave per token row:
-    // its 256 columns of each expert part are one contiguous 1 KB read
-    __shared__ __attribute__((aligned(16))) float s_acc[64][256 + 4];
+    // the expert parts added in the MFMA layout itself (lane (g4, c16) of
+    // block (ib, jb): token t0 + 16 ib + c16, columns i0 + 16 jb + 4 g4 .. + 3),
+    // in choice order, then part order, one 16-token block at a time
+    if (i0 >= d) return;   // d is a multiple of 64: the wave's 64 columns are all in or all out
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int ib = 0; ib < 4; ++ib) {
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            *(f32x4*)&s_acc[ib * 16 + c16][w * 64 + jb * 16 + 4 * g4] = acc[ib][jb];
-    __syncthreads();
-    const int col = blockIdx.y * 256 + 4 * lane;
-    if (col >= d) return;   // d is a multiple of 64: whole 4-column groups
-    for (int r0 = 0; r0 < 16; r0 += 4) {   // four rows at a time: their loads in flight together
-        f32x4 v[4];
-        long long t[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            t[q] = t0 + w * 16 + r0 + q;
-            v[q] = *(const f32x4*)&s_acc[w * 16 + r0 + q][4 * lane];
-        }
-        for (int j = 0; j < k; ++j) {
-            int rr[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) rr[q] = t[q] < T ? row_of[t[q] * k + j] : -1;
+        for (int j = 0; j < 8; ++j) {
+            if (j >= k) break;   // uniform
+            const int rr = rj[ib][j];
             for (int p = 0; p < nparts; ++p) {
-                const float* base = dXp + p * part_stride + col;
+                const float* base = dXp + p * part_stride + i0 + 4 * g4 + (long long)rr * d;
+                f32x4 g[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (rr[q] >= 0) v[q] += *(const f32x4*)(base + (long long)rr[q] * d);
+                for (int jb = 0; jb < 4; ++jb)
+                    if (rr >= 0) g[jb] = *(const f32x4*)(base + jb * 16);
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+                    if (rr >= 0) acc[ib][jb] += g[jb];
             }
         }
+        const long long t = t0 + ib * 16 + c16;
+        if (t < T) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (t[q] < T)
-                *(u32x2*)(dx + t[q] * d + col) =
-                    u32x2{pack_bf16x2(v[q][0], v[q][1]), pack_bf16x2(v[q][2], v[q][3])};
+            for (int jb = 0; jb < 4; ++jb)
+                *(u32x2*)(dx + t * d + i0 + jb * 16 + 4 * g4) =
+                    u32x2{pack_bf16x2(acc[ib][jb][0], acc[ib][jb][1]),
+                          pack_bf16x2(acc[ib][jb][2], acc[ib][jb][3])};
+        }
     }
 }
 
@@ -486,7 +493,7 @@ hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp, int 
                      long long part_stride, const int32_t* row_of, uint16_t* dx, long long T,
                      int d, int E, int k, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (d % 64 != 0) return hipErrorInvalidValue;
+    if (d % 64 != 0 || k < 1 || k > 8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((T + 63) / 64), (d + 255) / 256);
     if (E % 8 == 0)
         hipLaunchKernelGGL(dx_kernel<true>, grid, dim3(256), 0, s, dl, wr, dXp, nparts,
