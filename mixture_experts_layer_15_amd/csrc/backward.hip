@@ -1,7 +1,9 @@
 // backward.hip -- the non-GEMM kernels of the layer's backward pass (bf16
-// layers): GeGLU backward with the gate gradient, softmax/top-k backward into
-// the router logits, the router's weight, bias and input gradients, and the
-// token-side gather-sum of the expert input gradients.
+// layers): the gate of each kept row and the sum of the gate gradient's
+// partials (the GeGLU backward itself runs in the epilogue of the NT GEMM
+// that computes dHr, gemm_bw.hip), softmax/top-k backward into the router
+// logits, the router's weight, bias and input gradients, and the token-side
+// gather-sum of the expert input gradients.
 //
 // Notation (per kept assignment (t, j) of expert e, row r of the expert-
 // grouped layout): g = x Wg[e], u = x Wu[e], a = GELU(g), h = a u,
@@ -19,23 +21,6 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Phi(v) and phi(v) (standard normal CDF and density) in fp32: Phi through
-// the complementary error function of Abramowitz & Stegun, Handbook of
-// Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7), whose
-// exp(-z^2) = exp(-v^2 / 2) also gives the density.
-__device__ __forceinline__ void normal_cdf_pdf(float v, float& Phi, float& phi) {
-    const float z = fabsf(v) * 0.70710678118654752440f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-    float p = fmaf(t, 1.061405429f, -1.453152027f);
-    p = fmaf(t, p, 1.421413741f);
-    p = fmaf(t, p, -0.284496736f);
-    p = fmaf(t, p, 0.254829592f);
-    const float ez = __builtin_amdgcn_exp2f(-z * z * 1.44269504088896341f);
-    const float half_erfc = 0.5f * t * p * ez;
-    Phi = v >= 0.0f ? 1.0f - half_erfc : half_erfc;
-    phi = ez * 0.39894228040143267794f;   // 1 / sqrt(2 pi)
-}
-
 // Sum over the 64 lanes of a wave, the same butterfly order every time.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -48,58 +33,32 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// One workgroup per row r < n_kept (rows past it exit).  In place: G -> dG,
-// U -> dU.  gH = gate h (bf16), dgate_row[r] = h . dHr.
-__global__ __launch_bounds__(256) void geglu_bwd_kernel(
-    uint16_t* __restrict__ G, uint16_t* __restrict__ U, const float* __restrict__ dHr,
-    uint16_t* __restrict__ gH, float* __restrict__ dgate_row, const int32_t* __restrict__ offset,
-    const int32_t* __restrict__ token_of_row, const int32_t* __restrict__ row_of,
-    const float* __restrict__ gate, int E, int k, int F) {
-    const int r = blockIdx.x;
+// row_gate[r] = the gate of the assignment (t, j) that row r < n_kept holds.
+__global__ __launch_bounds__(256) void row_gate_kernel(const int32_t* __restrict__ offset,
+                                                       const int32_t* __restrict__ token_of_row,
+                                                       const int32_t* __restrict__ row_of,
+                                                       const float* __restrict__ gate, int E,
+                                                       int k, float* __restrict__ row_gate) {
+    const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
     if (r >= offset[E]) return;
-    const int t = token_of_row[r];
+    const long long t = token_of_row[r];
     float gt = 0.f;
     for (int j = 0; j < k; ++j)
-        if (row_of[(long long)t * k + j] == r) gt = gate[(long long)t * k + j];
-    const long long base = (long long)r * F;
-    float dot = 0.f;
-    for (int c = threadIdx.x * 8; c < F; c += 256 * 8) {
-        const u32x4 gv = *(const u32x4*)(G + base + c);
-        const u32x4 uv = *(const u32x4*)(U + base + c);
-        const f32x4 d0 = *(const f32x4*)(dHr + base + c);
-        const f32x4 d1 = *(const f32x4*)(dHr + base + c + 4);
-        u32x4 dg_o, du_o, gh_o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float dgv[2], duv[2], ghv[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const float g = Elem<uint16_t>::to_f32(gv, 2 * q + s);
-                const float u = Elem<uint16_t>::to_f32(uv, 2 * q + s);
-                const float dh_raw = (2 * q + s < 4) ? d0[2 * q + s] : d1[2 * q + s - 4];
-                float Phi, phi;
-                normal_cdf_pdf(g, Phi, phi);
-                const float a = g * Phi;
-                const float h = a * u;
-                dot = fmaf(h, dh_raw, dot);
-                const float dh = gt * dh_raw;
-                duv[s] = dh * a;
-                dgv[s] = dh * u * fmaf(g, phi, Phi);
-                ghv[s] = gt * h;
-            }
-            dg_o[q] = pack_bf16x2(dgv[0], dgv[1]);
-            du_o[q] = pack_bf16x2(duv[0], duv[1]);
-            gh_o[q] = pack_bf16x2(ghv[0], ghv[1]);
-        }
-        *(u32x4*)(G + base + c) = dg_o;
-        *(u32x4*)(U + base + c) = du_o;
-        *(u32x4*)(gH + base + c) = gh_o;
-    }
-    __shared__ float part[4];
-    dot = wave_sum(dot);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = dot;
-    __syncthreads();
-    if (threadIdx.x == 0) dgate_row[r] = ((part[0] + part[1]) + part[2]) + part[3];
+        if (row_of[t * k + j] == r) gt = gate[t * k + j];
+    row_gate[r] = gt;
+}
+
+// dgate_row[r] = h . dh_raw of row r < n_kept: its np partial sums (one per
+// 64 columns of d_ff, from the NT epilogue) added in column order.
+__global__ __launch_bounds__(256) void dgate_sum_kernel(const float* __restrict__ dot, int np,
+                                                        const int32_t* __restrict__ offset, int E,
+                                                        float* __restrict__ dgate_row) {
+    const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (r >= offset[E]) return;
+    const float* p = dot + r * np;
+    float v = 0.f;
+    for (int c = 0; c < np; ++c) v += p[c];
+    dgate_row[r] = v;
 }
 
 // One wave per token: p = softmax(l / tau) from the fp32 logits, dp from the
@@ -467,14 +426,20 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, long l
 
 }  // namespace
 
-hipError_t launch_geglu_bwd(uint16_t* G, uint16_t* U, const float* dHr, uint16_t* gH,
-                            float* dgate_row, const int32_t* offset, const int32_t* token_of_row,
-                            const int32_t* row_of, const float* gate, int E, int k, int F,
-                            long long max_rows, hipStream_t s) {
+hipError_t launch_row_gate(const int32_t* offset, const int32_t* token_of_row,
+                           const int32_t* row_of, const float* gate, int E, int k,
+                           long long max_rows, float* row_gate, hipStream_t s) {
     if (max_rows == 0) return hipSuccess;
-    if (F % 8 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(geglu_bwd_kernel, dim3((unsigned)max_rows), dim3(256), 0, s, G, U, dHr, gH,
-                       dgate_row, offset, token_of_row, row_of, gate, E, k, F);
+    hipLaunchKernelGGL(row_gate_kernel, dim3((unsigned)((max_rows + 255) / 256)), dim3(256), 0, s,
+                       offset, token_of_row, row_of, gate, E, k, row_gate);
+    return hipGetLastError();
+}
+
+hipError_t launch_dgate_sum(const float* dot, int np, const int32_t* offset, int E,
+                            long long max_rows, float* dgate_row, hipStream_t s) {
+    if (max_rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(dgate_sum_kernel, dim3((unsigned)((max_rows + 255) / 256)), dim3(256), 0, s,
+                       dot, np, offset, E, dgate_row);
     return hipGetLastError();
 }
 

@@ -26,7 +26,16 @@
 // the buffer descriptor's record count ends at the expert's last row, so they
 // read as zeros.  fp32 results written from the accumulators, four
 // consecutive columns per lane (weights in the MFMA's first operand slot).
+// The NT launch for dh_raw = dy W_down^T instead ends in the GeGLU backward
+// (EPI): it reads g, u of its elements and writes dg, du, gate h (bf16) and
+// per-row partial sums of dgate, so dh_raw is never stored (2.1 GB of fp32
+// on the long-sequence layer, written and read back by a separate kernel
+// before).  Timed against that separate kernel on one GPU, alternating: the
+// long-sequence backward 45.95 -> 45.74 ms, skewed 7.46 -> 7.38, ZAYA1-like
+// 2.121 -> 2.134, wide 28.39 -> 28.57 ms: the epilogue's stores leave at the
+// same per-CU rate the separate kernel's did.
 #include "common.h"
+#include "geglu_bwd.h"
 #include "kernels.h"
 #include "lds_dma.h"
 #include "tiles.h"
@@ -35,6 +44,7 @@ namespace moe {
 namespace {
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 template <int BM, int BN, int WAVES, int WMW, int NS, int TK>
@@ -85,13 +95,22 @@ struct BwOperands {
     float* C;
     long long c_stride;
     int nsrc, ksplit, fuse;
+    // GeGLU epilogue (NT, one source, one K slice): the product is dh_raw;
+    // G, U (bf16 [rows][N], in place -> dG, dU), gH out, gate per row, and
+    // the partial sums of h . dh_raw over each wave's 64 columns,
+    // dot[row][N / 64]
+    uint16_t* G;
+    uint16_t* U;
+    uint16_t* gH;
+    const float* row_gate;
+    float* dot;
 };
 
 // MODE 0 (NT): tiles from the expert row counts (ragged M) for every part;
 //   A rows row0.. of A[s], B = W[e] of source s, one K slice.
 // MODE 1 (TN): tiles (e, M-tile, N-tile); reduction over the rows off[e] ..
 //   off[e+1]-1 of A [rows][M] and B [rows][N].
-template <int MODE, int BM, int BN, int WAVES, int WMW, int NS, int TK>
+template <int MODE, int BM, int BN, int WAVES, int WMW, int NS, int TK, bool EPI = false>
 __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
     const BwOperands ops, const int32_t* __restrict__ off, int E, int M, int N, int K) {
     using S = BwShape<BM, BN, WAVES, WMW, NS, TK>;
@@ -317,6 +336,73 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
         }
 
         // lane (g4, c16) of block (i, j): row i*16 + c16, columns j*16 + 4 g4 .. + 3
+        if constexpr (EPI) {
+            // GeGLU backward of this tile's elements; each wave's 64 columns
+            // (N % 64 == 0: all valid or all past N) give one partial of dgate
+            static_assert(MODE == 0 && NJ * 16 == 64, "epilogue: NT, 64 columns per wave");
+            const int cw = n0 + wn * 64;
+            const int np = N / 64;
+            const bool cols_ok = cw < N;
+            // G, U of row block i + 1 are loaded before row block i is
+            // computed and stored: one load latency per tile, not one per
+            // row block (the loads are issued ahead of the stores in program
+            // order, which the compiler keeps since the arrays are the same)
+            // (the 320-row tile has no registers to spare for the second set:
+            // there each row block loads its own)
+            constexpr bool AHEAD = BM != 320;
+            constexpr int NSET = AHEAD ? 2 : 1;
+            u32x2 gv[NSET][NJ], uv[NSET][NJ];
+            float gts[NSET];
+            auto fetch = [&](int i, int b) {
+                const int r = (wm * MI + i) * 16 + c16;
+                if (r < rows && cols_ok) {
+                    const long long rowg = row0 + r;
+                    gts[b] = ops.row_gate[rowg];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const long long o = rowg * N + cw + j * 16 + g4 * 4;
+                        gv[b][j] = *(const u32x2*)(ops.G + o);
+                        uv[b][j] = *(const u32x2*)(ops.U + o);
+                    }
+                }
+            };
+            if constexpr (AHEAD) fetch(0, 0);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int b = AHEAD ? i & 1 : 0;
+                if constexpr (AHEAD)
+                    if (i + 1 < MI) fetch(i + 1, (i + 1) & 1);
+                const int r = (wm * MI + i) * 16 + c16;
+                float dot = 0.f;
+                if (r < rows && cols_ok) {
+                    const long long rowg = row0 + r;
+                    const float gt = AHEAD ? gts[b] : ops.row_gate[rowg];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const long long o = rowg * N + cw + j * 16 + g4 * 4;
+                        const u32x2 gq = AHEAD ? gv[b][j] : *(const u32x2*)(ops.G + o);
+                        const u32x2 uq = AHEAD ? uv[b][j] : *(const u32x2*)(ops.U + o);
+                        float dg[4], du[4], gh[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t gw = gq[q >> 1], uw = uq[q >> 1];
+                            const float g = bf16_bits_to_f32((q & 1) ? gw >> 16 : gw & 0xffffu);
+                            const float u = bf16_bits_to_f32((q & 1) ? uw >> 16 : uw & 0xffffu);
+                            float term;
+                            geglu_bwd_elem(g, u, acc[i][j][q], gt, dg[q], du[q], gh[q], term);
+                            dot += term;
+                        }
+                        *(u32x2*)(ops.G + o) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+                        *(u32x2*)(ops.U + o) = u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+                        *(u32x2*)(ops.gH + o) = u32x2{pack_bf16x2(gh[0], gh[1]), pack_bf16x2(gh[2], gh[3])};
+                    }
+                }
+                // the four lanes of a row (g4 = 0..3), then lane g4 = 0 writes
+                dot += __shfl_xor(dot, 16);
+                dot += __shfl_xor(dot, 32);
+                if (g4 == 0 && r < rows && cols_ok) ops.dot[(row0 + r) * (long long)np + cw / 64] = dot;
+            }
+        } else {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int r = (wm * MI + i) * 16 + c16;
@@ -329,6 +415,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
                 if (col >= N) continue;
                 *(f32x4*)(crow + col) = acc[i][j];
             }
+        }
         }
         // every wave is done reading this tile's stages before the next tile's
         // loads refill them
@@ -344,13 +431,13 @@ unsigned grid_of(long long tiles, int cap) {
     return (unsigned)std::max<long long>(8, g / 8 * 8);
 }
 
-template <int BM, int BN, int WAVES, int WMW, int NS, int TK>
+template <int BM, int BN, int WAVES, int WMW, int NS, int TK, bool EPI = false>
 hipError_t launch_nt(const BwOperands& ops, const int32_t* off, int E, int N, int K,
                      long long max_rows, int cap, hipStream_t s) {
     const long long tiles = ((max_rows + BM - 1) / BM + E) * ((N + BN - 1) / BN) *
                             (ops.fuse ? 1 : ops.nsrc) * ops.ksplit;
-    hipLaunchKernelGGL((gemm_bw_kernel<0, BM, BN, WAVES, WMW, NS, TK>), dim3(grid_of(tiles, cap)),
-                       dim3(64 * WAVES), 0, s, ops, off, E, 0, N, K);
+    hipLaunchKernelGGL((gemm_bw_kernel<0, BM, BN, WAVES, WMW, NS, TK, EPI>),
+                       dim3(grid_of(tiles, cap)), dim3(64 * WAVES), 0, s, ops, off, E, 0, N, K);
     return hipGetLastError();
 }
 
@@ -404,6 +491,20 @@ hipError_t launch_bw_nt(const uint16_t* A0, const uint16_t* W0, const uint16_t* 
         return launch_nt<320, 256, 8, 2, BW_NT_NS, BW_NT_TK>(ops, off, E, N, K, max_rows, cus / 2,
                                                              s);
     return launch_nt<256, 256, 8, 2, BW_NT_NS, BW_NT_TK>(ops, off, E, N, K, max_rows, cus / 2, s);
+}
+
+hipError_t launch_bw_nt_geglu(const uint16_t* A, const uint16_t* W, uint16_t* G, uint16_t* U,
+                              uint16_t* gH, const float* row_gate, float* dot,
+                              const int32_t* off, int E, int N, int K, long long max_rows,
+                              int cus, hipStream_t s) {
+    if (max_rows == 0) return hipSuccess;
+    if (N % 64 != 0 || N < 64 || K % BW_NT_TK != 0) return hipErrorInvalidValue;
+    BwOperands ops{{A, nullptr}, {W, nullptr}, nullptr, 0, 1, 1, 0, G, U, gH, row_gate, dot};
+    if (bw_nt_bm(max_rows, E) == 320)
+        return launch_nt<320, 256, 8, 2, BW_NT_NS, BW_NT_TK, true>(ops, off, E, N, K, max_rows,
+                                                                   cus / 2, s);
+    return launch_nt<256, 256, 8, 2, BW_NT_NS, BW_NT_TK, true>(ops, off, E, N, K, max_rows,
+                                                               cus / 2, s);
 }
 
 hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off,

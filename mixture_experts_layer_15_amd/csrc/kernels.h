@@ -166,14 +166,25 @@ hipError_t launch_bw_nt(const uint16_t* A0, const uint16_t* W0, const uint16_t* 
 // TN: C[e][M][N] = sum over the rows r of expert e of A[r][m] B[r][n]: the
 // weight gradients, a ragged reduction length per expert; experts with no
 // rows get zeros.
+// dh_raw = A W^T (one K slice) with the GeGLU backward in the epilogue: G, U
+// (bf16 [rows][N]) become dG, dU in place, gH = gate h, and
+// dot[row][N / 64] the partial sums of h . dh_raw over 64-column groups.
+// N % 64 == 0.
+hipError_t launch_bw_nt_geglu(const uint16_t* A, const uint16_t* W, uint16_t* G, uint16_t* U,
+                              uint16_t* gH, const float* row_gate, float* dot,
+                              const int32_t* off, int E, int N, int K, long long max_rows,
+                              int cus, hipStream_t s);
 hipError_t launch_bw_tn(const uint16_t* A, const uint16_t* B, float* C, const int32_t* off,
                         int E, int M, int N, int cus, hipStream_t s);
 
 // Backward elementwise and router kernels (backward.hip).
-hipError_t launch_geglu_bwd(uint16_t* G, uint16_t* U, const float* dHr, uint16_t* gH,
-                            float* dgate_row, const int32_t* offset, const int32_t* token_of_row,
-                            const int32_t* row_of, const float* gate, int E, int k, int F,
-                            long long max_rows, hipStream_t s);
+// The gate of each kept row (row_gate[r] = gate of the assignment that owns
+// row r), and dgate_row[r] = sum of its np partials in order.
+hipError_t launch_row_gate(const int32_t* offset, const int32_t* token_of_row,
+                           const int32_t* row_of, const float* gate, int E, int k,
+                           long long max_rows, float* row_gate, hipStream_t s);
+hipError_t launch_dgate_sum(const float* dot, int np, const int32_t* offset, int E,
+                            long long max_rows, float* dgate_row, hipStream_t s);
 hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
                              const int32_t* row_of, const float* dgate_row, long long T, int E,
                              int k, float tau, int renorm, float* dl, float* dgate,

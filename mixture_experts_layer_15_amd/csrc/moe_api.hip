@@ -620,7 +620,7 @@ namespace {
 // the recomputed pre-activations and the gradients of every product.
 struct BwdLayout {
     size_t logits, idx, gate, count, offset, row_of, token_of_row, dsp, x_perm, dy_perm, G, U,
-        gH, dHr, dXp, dgrow, dl, dwr, total;
+        gH, rgate, dot, dXp, dgrow, dl, dwr, total;
     int dx_parts;   // parts of dx_perm (K slices; each sums the gate and up products)
 };
 
@@ -644,7 +644,8 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.G = take(R * F * 2);
     L.U = take(R * F * 2);
     L.gH = take(R * F * 2);
-    L.dHr = take(R * F * 4);
+    L.rgate = take(R * 4);
+    L.dot = take(R * (F / 64) * 4);
     L.dx_parts = moe::bw_nt_ksplit((long long)R, c->E, c->d, c->d_ff, 1, gemm_grid_cap());
     L.dXp = take((size_t)L.dx_parts * R * d * 4);
     L.dgrow = take(R * 4);
@@ -724,7 +725,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     uint16_t* G = (uint16_t*)(w + L.G);
     uint16_t* U = (uint16_t*)(w + L.U);
     uint16_t* gH = (uint16_t*)(w + L.gH);
-    float* dHr = (float*)(w + L.dHr);
+    float* rgate = (float*)(w + L.rgate);
+    float* dot = (float*)(w + L.dot);
     float* dXp = (float*)(w + L.dXp);
     float* dgrow = (float*)(w + L.dgrow);
     float* dl = (float*)(w + L.dl);
@@ -746,11 +748,14 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     BWD(moe::launch_mfma_gate_up_pre(x_perm, nullptr, offset, (const uint16_t*)w_gate,
                                      (const uint16_t*)w_up, G, U, Ei, di, Fi, Rl, cus, s),
         "moe_backward/gate_up");
-    // dHr = dy W_down^T per kept row, then the GeGLU backward and dgate
-    BWD(moe::launch_bw_nt(dy_perm, (const uint16_t*)w_down, nullptr, nullptr, dHr, 0, 1, offset,
-                          Ei, Fi, di, Rl, cus, s), "moe_backward/dh");
-    BWD(moe::launch_geglu_bwd(G, U, dHr, gH, dgrow, offset, tor, row_of, gate, Ei, ki, Fi, Rl, s),
-        "moe_backward/geglu");
+    // dh_raw = dy W_down^T per kept row with the GeGLU backward in its
+    // epilogue (G, U -> dg, du in place, gate h, partial dgate sums), then
+    // dgate per row
+    BWD(moe::launch_row_gate(offset, tor, row_of, gate, Ei, ki, Rl, rgate, s),
+        "moe_backward/row_gate");
+    BWD(moe::launch_bw_nt_geglu(dy_perm, (const uint16_t*)w_down, G, U, gH, rgate, dot, offset,
+                                Ei, Fi, di, Rl, cus, s), "moe_backward/dh_geglu");
+    BWD(moe::launch_dgate_sum(dot, Fi / 64, offset, Ei, Rl, dgrow, s), "moe_backward/dgate");
     // G, U now hold dg, du
     // dx_perm in parts, one per K slice, each dg W_gate^T + du W_up^T over that
     // slice in one accumulator; summed by launch_dx

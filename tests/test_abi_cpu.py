@@ -261,10 +261,12 @@ def test_backward_validation_on_host(L):
     n = ctypes.c_size_t(0)
     assert L.moe_backward_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0
     R, T, d, E, F, k = moe.max_rows(cfg), cfg.T, cfg.d, cfg.E, cfg.d_ff, cfg.k
-    # the recomputed pre-activations, dg/du in place, gate * h, dh (fp32), x and
-    # dy in expert order, the expert input gradients (fp32, gate and up parts,
-    # up to four K slices each), the routing maps and the logit gradients
-    base = R * F * (3 * 2 + 4) + 2 * R * d * 2 + T * E * 4 * 2 + T * k * 4 * 4
+    # the recomputed pre-activations, dg/du in place, gate * h, the per-row gate
+    # and dgate partials (one per 64 columns; dh itself is never stored), x and
+    # dy in expert order, the expert input gradients (fp32, up to four K
+    # slices), the routing maps and the logit gradients
+    base = R * F * 3 * 2 + R * 4 + R * (F // 64) * 4 + 2 * R * d * 2 + T * E * 4 * 2 + \
+        T * k * 4 * 4
     assert n.value >= base + 2 * R * d * 4
     assert n.value < base + 8 * R * d * 4 + (64 << 20)
     f32 = moe.cconfig(configs.get("tiny"))
