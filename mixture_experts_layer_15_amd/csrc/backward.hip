@@ -469,16 +469,27 @@ hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp, int 
     return hipGetLastError();
 }
 
-// Few experts: dwr_narrow_kernel (2048 columns per workgroup), else
-// dwr_part_kernel (256 columns x 64 experts).
-static bool dwr_narrow(int E) { return E <= 16; }
+// Column tiles and token splits: about two workgroups per CU, splits of at
+// least 64 tokens.
+static long long dwr_splits_for(long long T, long long tiles) {
+    long long ns = (512 + tiles - 1) / tiles;
+    ns = std::min<long long>(ns, std::max<long long>(1, (T + 63) / 64));
+    return std::max<long long>(1, std::min<long long>(ns, 4096));
+}
+
+// Few experts and enough tokens to fill the chip with 2048-column
+// workgroups: dwr_narrow_kernel (long-sequence layer 1046 -> 262 us), else
+// dwr_part_kernel, 256 columns x 64 experts (the ZAYA1-like layer, whose
+// 4,096 tokens would make only 64 narrow workgroups: 50 us against 86).
+static bool dwr_narrow(long long T, int d, int E) {
+    const long long tiles = (d + 2047) / 2048;
+    return E <= 16 && tiles * dwr_splits_for(T, tiles) >= 256;
+}
 
 int dwr_splits(long long T, int d, int E) {
-    const long long tiles = dwr_narrow(E) ? (long long)((d + 2047) / 2048)
-                                          : (long long)((d + 255) / 256) * ((E + 63) / 64);
-    long long ns = (512 + tiles - 1) / tiles;   // about two workgroups per CU
-    ns = std::min<long long>(ns, std::max<long long>(1, (T + 63) / 64));
-    return (int)std::max<long long>(1, std::min<long long>(ns, 4096));
+    const long long tiles = dwr_narrow(T, d, E) ? (long long)((d + 2047) / 2048)
+                                                : (long long)((d + 255) / 256) * ((E + 63) / 64);
+    return (int)dwr_splits_for(T, tiles);
 }
 
 size_t dwr_workspace_bytes(long long T, int d, int E) {
@@ -493,10 +504,11 @@ hipError_t launch_dwr(const uint16_t* x, const float* dl, float* dwr, float* dbi
     const long long split = T == 0 ? 1 : ((T + ns - 1) / ns + 15) / 16 * 16;
     float* part = (float*)ws;
     float* bpart = part + (size_t)ns * d * E;
-    if (dwr_narrow(E) && E <= 8)
+    const bool narrow = dwr_narrow(T, d, E);
+    if (narrow && E <= 8)
         hipLaunchKernelGGL(dwr_narrow_kernel<8>, dim3((d + 2047) / 2048, 1, ns), dim3(256), 0, s,
                            x, dl, part, bpart, T, d, E, split);
-    else if (dwr_narrow(E))
+    else if (narrow)
         hipLaunchKernelGGL(dwr_narrow_kernel<16>, dim3((d + 2047) / 2048, 1, ns), dim3(256), 0,
                            s, x, dl, part, bpart, T, d, E, split);
     else

@@ -68,6 +68,11 @@ CASES = {
     # the widest routing: 256 experts, 8 choices per token, ragged token count
     "bw_e256_k8": BASE.scaled(T=130, d=64, E=256, k=8, d_ff=64, temperature=0.5,
                               renormalize=True, cap_num=3, cap_den=2),
+    # few experts and enough tokens for the router weight gradient's narrow
+    # kernel (each thread 8 columns and every expert); d under one 2048-column tile
+    "bw_narrow_e8": BASE.scaled(T=16384, d=64, E=8, k=2, d_ff=64, temperature=0.7,
+                                renormalize=True, cap_num=5, cap_den=4),
+    "bw_narrow_e12": BASE.scaled(T=16500, d=128, E=12, k=3, d_ff=64, temperature=0.9),
     # dynamic expert count (2-4 per token, the fewest whose softmax mass
     # reaches 0.6), gates renormalised over those taken, capacity 5/4 of the
     # realised load
