@@ -366,8 +366,9 @@ moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
 /* Backward of steps 1-7 for an upstream gradient dy = dL/dy (training, the
  * step that follows the forward on every page: the TorchTitan 1K-GPU article
  * trains this layer, section 2; "AMD MI300X平台上的MoE模型训练实践" trains it
- * too, section 4).  bf16 layers in the compact layout only
- * (MOE_ERR_UNSUPPORTED otherwise).  The forward's routing and expert
+ * too, section 4).  bf16 layers only (MOE_ERR_UNSUPPORTED otherwise), in
+ * either layout (the padded layout's empty rows are zero in every product,
+ * so the gradients equal the compact layout's).  The forward's routing and expert
  * pre-activations are recomputed from the inputs, as the activation
  * recomputation of that training page's section 4.1 does (same kernels, same
  * values as moe_forward);

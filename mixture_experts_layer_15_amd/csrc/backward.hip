@@ -33,7 +33,8 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// row_gate[r] = the gate of the assignment (t, j) that row r < n_kept holds.
+// row_gate[r] = the gate of the assignment (t, j) that row r < offset[E]
+// holds, 0 for an empty row of the padded layout.
 __global__ __launch_bounds__(256) void row_gate_kernel(const int32_t* __restrict__ offset,
                                                        const int32_t* __restrict__ token_of_row,
                                                        const int32_t* __restrict__ row_of,
@@ -41,9 +42,9 @@ __global__ __launch_bounds__(256) void row_gate_kernel(const int32_t* __restrict
                                                        int k, float* __restrict__ row_gate) {
     const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
     if (r >= offset[E]) return;
-    const long long t = token_of_row[r];
+    const long long t = token_of_row[r];   // -1: an empty row of the padded layout
     float gt = 0.f;
-    for (int j = 0; j < k; ++j)
+    for (int j = 0; j < k && t >= 0; ++j)
         if (row_of[t * k + j] == r) gt = gate[t * k + j];
     row_gate[r] = gt;
 }

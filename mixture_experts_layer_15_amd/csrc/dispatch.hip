@@ -560,6 +560,16 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
     return hipGetLastError();
 }
 
+hipError_t launch_zero_empty_rows(const int32_t* count, long long C, int E, int32_t* token_of_row,
+                                  void* buf, int row_bytes, hipStream_t s) {
+    const long long padded_rows = (long long)E * C;
+    if (padded_rows == 0) return hipSuccess;
+    if (row_bytes % 16 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((padded_rows + 3) / 4)), dim3(256), 0, s,
+                       count, C, E, token_of_row, (u32x4*)buf, row_bytes / 16);
+    return hipGetLastError();
+}
+
 hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, void* x_perm, long long T,
                                int row_bytes, int k, hipStream_t s) {
     if (T == 0) return hipSuccess;

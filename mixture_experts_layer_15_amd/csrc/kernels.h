@@ -62,6 +62,10 @@ hipError_t launch_dispatch(const DispatchPlan& p, int dtype, const int32_t* idx,
                            bool scatter = true);
 
 // x_perm[row_of[t][j]] = x[t] for every kept (t, j) (rows of row_bytes bytes).
+// Padded layout: zero the rows of buf [E * C][row_bytes] that hold no token
+// (and mark them -1 in token_of_row, as the dispatch does).
+hipError_t launch_zero_empty_rows(const int32_t* count, long long C, int E, int32_t* token_of_row,
+                                  void* buf, int row_bytes, hipStream_t s);
 hipError_t launch_scatter_rows(const void* x, const int32_t* row_of, void* x_perm, long long T,
                                int row_bytes, int k, hipStream_t s);
 

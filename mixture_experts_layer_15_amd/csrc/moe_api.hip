@@ -637,7 +637,7 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.count = take(E * 4);
     L.offset = take((E + 1) * 4);
     L.row_of = take(T * k * 4);
-    L.token_of_row = take(T * k * 4);
+    L.token_of_row = take((size_t)tor_len(c) * 4);   // the padded layout: E * C rows
     L.dsp = take(moe::dispatch_workspace_bytes(p));
     L.x_perm = take(R * d * 2);
     L.dy_perm = take(R * d * 2);
@@ -658,8 +658,6 @@ BwdLayout bwd_layout(const moe_config* c) {
 moe_status check_bwd(const moe_config* cfg) {
     CHECK(check_cfg(cfg));
     if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
-    if (cfg->layout != MOE_LAYOUT_COMPACT)
-        return fail(MOE_ERR_UNSUPPORTED, "the backward runs on the compact layout only");
     return MOE_OK;
 }
 
@@ -745,6 +743,9 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                              w + L.dsp, di, s, true), "moe_backward/dispatch");
     BWD(moe::launch_scatter_rows(dy, row_of, dy_perm, cfg->T, di * 2, ki, s),
         "moe_backward/scatter_dy");
+    if (cfg->layout == MOE_LAYOUT_PADDED)   // empty rows of dy in expert order are zero, as x's
+        BWD(moe::launch_zero_empty_rows(count, p.C, Ei, tor, dy_perm, di * 2, s),
+            "moe_backward/pad_dy");
     BWD(moe::launch_mfma_gate_up_pre(x_perm, nullptr, offset, (const uint16_t*)w_gate,
                                      (const uint16_t*)w_up, G, U, Ei, di, Fi, Rl, cus, s),
         "moe_backward/gate_up");

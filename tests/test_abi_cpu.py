@@ -315,9 +315,15 @@ def test_padded_layout_validation_and_sizes(L):
         pad = cfg.scaled(layout=1)
         assert moe.max_rows(pad) == cfg.E * C >= moe.max_rows(cfg)
         assert moe.workspace_bytes(pad) > moe.workspace_bytes(cfg)
-        # the backward runs on the compact layout only
-        assert L.moe_backward_workspace_size(ctypes.byref(moe.cconfig(pad)), ctypes.byref(n)) == \
-            moe.MOE_ERR_UNSUPPORTED
+        # the backward runs on it too, its workspace sized for the E * C rows
+        nc = ctypes.c_size_t(0)
+        assert L.moe_backward_workspace_size(ctypes.byref(moe.cconfig(pad)), ctypes.byref(n)) == 0
+        assert L.moe_backward_workspace_size(ctypes.byref(moe.cconfig(cfg)), ctypes.byref(nc)) == 0
+        assert n.value >= nc.value
+        # token_of_row holds one entry per row of the padded layout (E * C of
+        # them, more than the T * k assignment slots here)
+        assert cfg.E * C > cfg.T * cfg.k
+        assert n.value - nc.value >= (cfg.E * C - cfg.T * cfg.k) * 4
     # token_of_row must cover max(T * k, rows): too small a buffer is not checked
     # on the host (it is a device pointer), but the binding sizes it that way
     cfg = configs.get("skewed").scaled(layout=1)

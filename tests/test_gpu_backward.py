@@ -143,6 +143,22 @@ def test_backward_small(name):
         assert torch.equal(g[n], g2[n]), f"{n} differs between two calls"
 
 
+@pytest.mark.parametrize("name", ["bw_renorm_drops", "bw_k3_choice", "bw_zipf_bias"])
+def test_backward_padded_layout_equals_compact(name):
+    # the padded layout's empty rows are zero in every product: every gradient
+    # is the compact layout's, bit for bit, and so within the oracle's bar
+    cfg = CASES[name].scaled(name=name + "_padded", layout=1)
+    dev, _ = gpu_inputs(cfg, seed=3)
+    dy = synthetic.make_dy(cfg, seed=3, device="cuda")
+    args = (dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"], dy)
+    say(f"[{cfg.name}] moe_backward, padded and compact layouts")
+    gp = moe.backward(cfg, *args)
+    gc = moe.backward(cfg.scaled(layout=0), *args)
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(gp[n], gc[n]), n
+
+
 def test_backward_optional_outputs_left_out():
     # dgate and dbias may be NULL; the other gradients are the same bits
     cfg = CASES["bw_renorm_drops"].scaled(name="bw_optional")
