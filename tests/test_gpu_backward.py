@@ -68,6 +68,11 @@ CASES = {
     # the widest routing: 256 experts, 8 choices per token, ragged token count
     "bw_e256_k8": BASE.scaled(T=130, d=64, E=256, k=8, d_ff=64, temperature=0.5,
                               renormalize=True, cap_num=3, cap_den=2),
+    # the validation limits: d = 16384 (K of dh and of the router products, M of the
+    # gate/up weight gradients) and d_ff = 65536 (1024 dgate partials per row)
+    "bw_max_d": BASE.scaled(T=300, d=16384, E=4, k=2, d_ff=64, temperature=0.8,
+                            renormalize=True),
+    "bw_max_dff": BASE.scaled(T=200, d=64, E=2, k=1, d_ff=65536),
     # few experts and enough tokens for the router weight gradient's narrow
     # kernel (each thread 8 columns and every expert); d under one 2048-column tile
     "bw_narrow_e8": BASE.scaled(T=16384, d=64, E=8, k=2, d_ff=64, temperature=0.7,
