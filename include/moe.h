@@ -366,9 +366,9 @@ moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
 /* Backward of steps 1-7 for an upstream gradient dy = dL/dy (training, the
  * step that follows the forward on every page: the TorchTitan 1K-GPU article
  * trains this layer, section 2; "AMD MI300X平台上的MoE模型训练实践" trains it
- * too, section 4).  bf16 layers only (MOE_ERR_UNSUPPORTED otherwise), in
- * either layout (the padded layout's empty rows are zero in every product,
- * so the gradients equal the compact layout's).  The forward's routing and expert
+ * too, section 4).  Both dtypes and either layout (the padded layout's
+ * empty rows are zero in every product, so the gradients equal the compact
+ * layout's).  The forward's routing and expert
  * pre-activations are recomputed from the inputs, as the activation
  * recomputation of that training page's section 4.1 does (same kernels, same
  * values as moe_forward);
@@ -385,18 +385,19 @@ moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
  *   raw: dp_j = dgate_j; dlogit = p (dp - p . dp) / temperature
  *   dw_router = x^T dlogit, dbias = sum_t dlogit,
  *   dx_t = sum_j (dg W_gate[e]^T + du W_up[e]^T) + dlogit_t W_router^T
- *   x, dy       [T, d]          bf16 in      dx [T, d] bf16 out
- *   w_router    [d, E]          bf16 in      dw_router [d, E] fp32 out
+ *   x, dy       [T, d]          dtype in     dx [T, d] dtype out
+ *   w_router    [d, E]          dtype in     dw_router [d, E] fp32 out
  *   bias        [E]             fp32 in, may be NULL (zero bias)
  *   dbias       [E]             fp32 out, may be NULL (not written)
- *   w_gate, w_up [E, d, d_ff]   bf16 in      dw_gate, dw_up [E, d, d_ff] fp32 out
- *   w_down      [E, d_ff, d]    bf16 in      dw_down [E, d_ff, d] fp32 out
+ *   w_gate, w_up [E, d, d_ff]   dtype in     dw_gate, dw_up [E, d, d_ff] fp32 out
+ *   w_down      [E, d_ff, d]    dtype in     dw_down [E, d_ff, d] fp32 out
  *   dgate       [T, k]          fp32 out, may be NULL (not written)
  * Gradients overwrite their outputs (no accumulation); an expert with no kept
- * rows gets zero weight gradients.  Products accumulate in fp32; the expert
- * pre-activations and the per-row gradients fed to the next product are
- * rounded to bf16; the sums over tokens and experts run in a fixed order
- * (the results are deterministic). */
+ * rows gets zero weight gradients.  Products accumulate in fp32; in bf16
+ * layers the expert pre-activations and the per-row gradients fed to the
+ * next product are rounded to bf16 (fp32 layers keep them in fp32); the sums
+ * over tokens and experts run in a fixed order (the results are
+ * deterministic). */
 moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
                         const float* bias, const void* w_gate, const void* w_up,
                         const void* w_down, const void* dy, void* dx, float* dw_router,

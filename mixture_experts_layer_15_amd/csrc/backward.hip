@@ -272,12 +272,30 @@ __global__ __launch_bounds__(256, 3) void dx_kernel(
     }
 }
 
+// Eight consecutive elements of x (bf16 or fp32; 16-byte aligned) as fp32.
+template <typename XT>
+__device__ __forceinline__ void load8(const XT* p, float v[8]) {
+    if constexpr (sizeof(XT) == 2) {
+        const u32x4 raw = *(const u32x4*)p;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = Elem<uint16_t>::to_f32(raw, u);
+    } else {
+        const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[u] = a[u];
+            v[4 + u] = b[u];
+        }
+    }
+}
+
 // Partial router weight gradients over one split of the tokens:
 // part[s][i][e] = sum_{t in split s} x[t][i] dl[t][e]; the first column tile
 // also writes bpart[s][e] = sum_t dl[t][e].  Tile 256 (i) x 64 (e), 8 x 8 per
 // thread, t in chunks of 16 through LDS.
+template <typename XT>
 __global__ __launch_bounds__(256, 2) void dwr_part_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ dl, float* __restrict__ part,
+    const XT* __restrict__ x, const float* __restrict__ dl, float* __restrict__ part,
     float* __restrict__ bpart, long long T, int d, int E, long long split) {
     __shared__ __attribute__((aligned(16))) float s_x[16][256];
     __shared__ __attribute__((aligned(16))) float s_l[16][64];
@@ -293,11 +311,7 @@ __global__ __launch_bounds__(256, 2) void dwr_part_kernel(
             const int q = tid + 256 * r, kk = q >> 5, c8 = (q & 31) * 8;
             const long long t = tc + kk;
             float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (t < tb && i0 + c8 < d) {
-                const u32x4 raw = *(const u32x4*)(x + t * d + i0 + c8);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = Elem<uint16_t>::to_f32(raw, u);
-            }
+            if (t < tb && i0 + c8 < d) load8(x + t * d + i0 + c8, v);
             *(f32x4*)&s_x[kk][c8] = f32x4{v[0], v[1], v[2], v[3]};
             *(f32x4*)&s_x[kk][c8 + 4] = f32x4{v[4], v[5], v[6], v[7]};
         }
@@ -351,9 +365,9 @@ __global__ __launch_bounds__(256, 2) void dwr_part_kernel(
 // uniform across the workgroup.  Tokens of the split ascending, four at a
 // time so that four x loads are in flight.  The 64-expert tile of
 // dwr_part_kernel would spend 64 / E of its multiply-adds on padding here.
-template <int TE>
+template <int TE, typename XT>
 __global__ __launch_bounds__(256) void dwr_narrow_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ dl, float* __restrict__ part,
+    const XT* __restrict__ x, const float* __restrict__ dl, float* __restrict__ part,
     float* __restrict__ bpart, long long T, int d, int E, long long split) {
     const int tid = threadIdx.x;
     const int i0 = blockIdx.x * 2048 + tid * 8;
@@ -363,11 +377,16 @@ __global__ __launch_bounds__(256) void dwr_narrow_kernel(
     float acc[8][TE] = {};
     float bacc[TE] = {};
     for (long long t0 = ta; t0 < tb; t0 += 4) {
-        u32x4 raw[4];
+        float xv[4][8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const long long t = t0 + q;
-            raw[q] = (active && t < tb) ? *(const u32x4*)(x + t * d + i0) : u32x4{0u, 0u, 0u, 0u};
+            if (active && t < tb) {
+                load8(x + t * d + i0, xv[q]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) xv[q][u] = 0.f;
+            }
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(256) void dwr_narrow_kernel(
             for (int e = 0; e < TE; ++e) b[e] = e < E ? dl[t * E + e] : 0.f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const float a = Elem<uint16_t>::to_f32(raw[q], u);
+                const float a = xv[q][u];
 #pragma unroll
                 for (int e = 0; e < TE; ++e) acc[u][e] = fmaf(a, b[e], acc[u][e]);
             }
@@ -498,24 +517,34 @@ size_t dwr_workspace_bytes(long long T, int d, int E) {
     return (size_t)ns * ((size_t)d * E + E) * sizeof(float);
 }
 
-hipError_t launch_dwr(const uint16_t* x, const float* dl, float* dwr, float* dbias, long long T,
-                      int d, int E, void* ws, hipStream_t s) {
+namespace {
+template <typename XT>
+hipError_t dwr_parts(const XT* x, const float* dl, float* part, float* bpart, long long T, int d,
+                     int E, int ns, long long split, hipStream_t s) {
+    const bool narrow = dwr_narrow(T, d, E);
+    if (narrow && E <= 8)
+        hipLaunchKernelGGL((dwr_narrow_kernel<8, XT>), dim3((d + 2047) / 2048, 1, ns), dim3(256), 0,
+                           s, x, dl, part, bpart, T, d, E, split);
+    else if (narrow)
+        hipLaunchKernelGGL((dwr_narrow_kernel<16, XT>), dim3((d + 2047) / 2048, 1, ns), dim3(256),
+                           0, s, x, dl, part, bpart, T, d, E, split);
+    else
+        hipLaunchKernelGGL(dwr_part_kernel<XT>, dim3((d + 255) / 256, (E + 63) / 64, ns),
+                           dim3(256), 0, s, x, dl, part, bpart, T, d, E, split);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_dwr(int dtype, const void* x, const float* dl, float* dwr, float* dbias,
+                      long long T, int d, int E, void* ws, hipStream_t s) {
     if (d % 64 != 0) return hipErrorInvalidValue;
     const int ns = dwr_splits(T, d, E);
     const long long split = T == 0 ? 1 : ((T + ns - 1) / ns + 15) / 16 * 16;
     float* part = (float*)ws;
     float* bpart = part + (size_t)ns * d * E;
-    const bool narrow = dwr_narrow(T, d, E);
-    if (narrow && E <= 8)
-        hipLaunchKernelGGL(dwr_narrow_kernel<8>, dim3((d + 2047) / 2048, 1, ns), dim3(256), 0, s,
-                           x, dl, part, bpart, T, d, E, split);
-    else if (narrow)
-        hipLaunchKernelGGL(dwr_narrow_kernel<16>, dim3((d + 2047) / 2048, 1, ns), dim3(256), 0,
-                           s, x, dl, part, bpart, T, d, E, split);
-    else
-        hipLaunchKernelGGL(dwr_part_kernel, dim3((d + 255) / 256, (E + 63) / 64, ns), dim3(256),
-                           0, s, x, dl, part, bpart, T, d, E, split);
-    hipError_t e = hipGetLastError();
+    hipError_t e = dtype == 1
+        ? dwr_parts((const uint16_t*)x, dl, part, bpart, T, d, E, ns, split, s)
+        : dwr_parts((const float*)x, dl, part, bpart, T, d, E, ns, split, s);
     if (e != hipSuccess) return e;
     const long long n = (long long)d * E + E;
     hipLaunchKernelGGL(dwr_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,

@@ -12,10 +12,13 @@ namespace {
 
 constexpr int FBM = 64, FBN = 64, FBK = 16;
 
+// GATEUP with C2 != nullptr: the two products unfused, g into C and u into C2
+// (the backward's recompute).
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     const float* __restrict__ A, const float* __restrict__ B0, const float* __restrict__ B1,
-    float* __restrict__ C, const int32_t* __restrict__ off, int E, int K, int N) {
+    float* __restrict__ C, const int32_t* __restrict__ off, int E, int K, int N,
+    float* __restrict__ C2) {
     __shared__ float As[FBK][FBM + 4];
     __shared__ float Bg[FBK][FBN + 4];
     __shared__ float Bu[FBK][FBN + 4];
@@ -68,7 +71,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
             for (int j = 0; j < 4; ++j) {
                 const int col = n0 + tc * 4 + j;
                 if (col >= N) continue;
-                C[(long long)(row0 + rt) * N + col] = GATEUP ? gelu_erf(g[i][j]) * u[i][j] : g[i][j];
+                const long long o = (long long)(row0 + rt) * N + col;
+                if (GATEUP && C2 != nullptr) {
+                    C[o] = g[i][j];
+                    C2[o] = u[i][j];
+                } else {
+                    C[o] = GATEUP ? gelu_erf(g[i][j]) * u[i][j] : g[i][j];
+                }
             }
         }
     }
@@ -96,8 +105,19 @@ hipError_t launch_gate_up(int dtype, const void* x_perm, const int32_t* off, con
         const long long mt = (max_rows + FBM - 1) / FBM + E;
         hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3(grid_for(mt * ((d_ff + FBN - 1) / FBN), grid_cap)),
                            dim3(256), 0, s, (const float*)x_perm, (const float*)w_gate,
-                           (const float*)w_up, (float*)h, off, E, d, d_ff);
+                           (const float*)w_up, (float*)h, off, E, d, d_ff, (float*)nullptr);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_up_pre_f32(const float* x_perm, const int32_t* off, const float* w_gate,
+                                  const float* w_up, float* g, float* u, int E, int d, int d_ff,
+                                  long long max_rows, int grid_cap, hipStream_t s) {
+    if (max_rows == 0) return hipSuccess;
+    const long long mt = (max_rows + FBM - 1) / FBM + E;
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>,
+                       dim3(grid_for(mt * ((d_ff + FBN - 1) / FBN), grid_cap)), dim3(256), 0, s,
+                       x_perm, w_gate, w_up, g, off, E, d, d_ff, u);
     return hipGetLastError();
 }
 
@@ -114,7 +134,7 @@ hipError_t launch_down(int dtype, const void* h, const int32_t* off, const void*
         const long long mt = (max_rows + FBM - 1) / FBM + E;
         hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3(grid_for(mt * ((d + FBN - 1) / FBN), grid_cap)),
                            dim3(256), 0, s, (const float*)h, (const float*)w_down,
-                           (const float*)nullptr, (float*)y_perm, off, E, d_ff, d);
+                           (const float*)nullptr, (float*)y_perm, off, E, d_ff, d, (float*)nullptr);
     }
     return hipGetLastError();
 }

@@ -199,8 +199,26 @@ hipError_t launch_dx(const float* dl, const uint16_t* wr, const float* dXp, int 
                      long long part_stride, const int32_t* row_of, uint16_t* dx, long long T,
                      int d, int E, int k, hipStream_t s);
 size_t dwr_workspace_bytes(long long T, int d, int E);
-hipError_t launch_dwr(const uint16_t* x, const float* dl, float* dwr, float* dbias, long long T,
-                      int d, int E, void* ws, hipStream_t s);
+hipError_t launch_dwr(int dtype, const void* x, const float* dl, float* dwr, float* dbias,
+                      long long T, int d, int E, void* ws, hipStream_t s);
+// fp32 layers' backward products (backward_f32.hip): NT with an optional
+// second source, NT dh_raw with the GeGLU backward in its epilogue (G, U, gH
+// fp32; dot as for bf16), TN weight gradients, dx; and the recompute of g, u
+// (gemm.hip).
+hipError_t launch_bw_nt_f32(const float* A, const float* W, const float* A2, const float* W2,
+                            float* C, const int32_t* off, int E, int N, int K, long long max_rows,
+                            int cus, hipStream_t s);
+hipError_t launch_bw_nt_geglu_f32(const float* A, const float* W, float* G, float* U, float* gH,
+                                  const float* row_gate, float* dot, const int32_t* off, int E,
+                                  int N, int K, long long max_rows, int cus, hipStream_t s);
+hipError_t launch_bw_tn_f32(const float* A, const float* B, float* C, const int32_t* off, int E,
+                            int M, int N, int cus, hipStream_t s);
+hipError_t launch_dx_f32(const float* dl, const float* wr, const float* dXp,
+                         const int32_t* row_of, float* dx, long long T, int d, int E, int k,
+                         hipStream_t s);
+hipError_t launch_gate_up_pre_f32(const float* x_perm, const int32_t* off, const float* w_gate,
+                                  const float* w_up, float* g, float* u, int E, int d, int d_ff,
+                                  long long max_rows, int grid_cap, hipStream_t s);
 hipError_t launch_zero_f32(float* p, long long n, hipStream_t s);
 
 }  // namespace moe

@@ -639,14 +639,17 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.row_of = take(T * k * 4);
     L.token_of_row = take((size_t)tor_len(c) * 4);   // the padded layout: E * C rows
     L.dsp = take(moe::dispatch_workspace_bytes(p));
-    L.x_perm = take(R * d * 2);
-    L.dy_perm = take(R * d * 2);
-    L.G = take(R * F * 2);
-    L.U = take(R * F * 2);
-    L.gH = take(R * F * 2);
+    const size_t es = (size_t)esize(c);
+    L.x_perm = take(R * d * es);
+    L.dy_perm = take(R * d * es);
+    L.G = take(R * F * es);
+    L.U = take(R * F * es);
+    L.gH = take(R * F * es);
     L.rgate = take(R * 4);
     L.dot = take(R * (F / 64) * 4);
-    L.dx_parts = moe::bw_nt_ksplit((long long)R, c->E, c->d, c->d_ff, 1, gemm_grid_cap());
+    L.dx_parts = c->dtype == MOE_BF16
+                     ? moe::bw_nt_ksplit((long long)R, c->E, c->d, c->d_ff, 1, gemm_grid_cap())
+                     : 1;
     L.dXp = take((size_t)L.dx_parts * R * d * 4);
     L.dgrow = take(R * 4);
     L.dl = take(T * E * 4);
@@ -657,7 +660,6 @@ BwdLayout bwd_layout(const moe_config* c) {
 
 moe_status check_bwd(const moe_config* cfg) {
     CHECK(check_cfg(cfg));
-    if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
     return MOE_OK;
 }
 
@@ -720,15 +722,15 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     int32_t* offset = (int32_t*)(w + L.offset);
     int32_t* row_of = (int32_t*)(w + L.row_of);
     int32_t* tor = (int32_t*)(w + L.token_of_row);
-    uint16_t* G = (uint16_t*)(w + L.G);
-    uint16_t* U = (uint16_t*)(w + L.U);
-    uint16_t* gH = (uint16_t*)(w + L.gH);
+    void* G = w + L.G;
+    void* U = w + L.U;
+    void* gH = w + L.gH;
     float* rgate = (float*)(w + L.rgate);
     float* dot = (float*)(w + L.dot);
     float* dXp = (float*)(w + L.dXp);
     float* dgrow = (float*)(w + L.dgrow);
     float* dl = (float*)(w + L.dl);
-    const uint16_t* xb = (const uint16_t*)x;
+    const bool bf = cfg->dtype == MOE_BF16;
     const int Ei = cfg->E, di = cfg->d, Fi = cfg->d_ff, ki = cfg->k;
     const long long Rl = max_rows(cfg);
     const int cus = gemm_grid_cap();
@@ -737,41 +739,74 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     BWD(moe::launch_route(cfg->dtype, x, w_router, bias, logits, idx, gate, cfg->T, di, Ei,
                           topk_params(cfg), s), "moe_backward/route");
     const moe::DispatchPlan p = dispatch_plan(cfg);
-    uint16_t* x_perm = (uint16_t*)(w + L.x_perm);
-    uint16_t* dy_perm = (uint16_t*)(w + L.dy_perm);
+    void* x_perm = w + L.x_perm;
+    void* dy_perm = w + L.dy_perm;
     BWD(moe::launch_dispatch(p, cfg->dtype, idx, x, x_perm, count, offset, row_of, tor,
                              w + L.dsp, di, s, true), "moe_backward/dispatch");
-    BWD(moe::launch_scatter_rows(dy, row_of, dy_perm, cfg->T, di * 2, ki, s),
+    BWD(moe::launch_scatter_rows(dy, row_of, dy_perm, cfg->T, (int)(di * es), ki, s),
         "moe_backward/scatter_dy");
     if (cfg->layout == MOE_LAYOUT_PADDED)   // empty rows of dy in expert order are zero, as x's
-        BWD(moe::launch_zero_empty_rows(count, p.C, Ei, tor, dy_perm, di * 2, s),
+        BWD(moe::launch_zero_empty_rows(count, p.C, Ei, tor, dy_perm, (int)(di * es), s),
             "moe_backward/pad_dy");
-    BWD(moe::launch_mfma_gate_up_pre(x_perm, nullptr, offset, (const uint16_t*)w_gate,
-                                     (const uint16_t*)w_up, G, U, Ei, di, Fi, Rl, cus, s),
-        "moe_backward/gate_up");
+    if (bf)
+        BWD(moe::launch_mfma_gate_up_pre((const uint16_t*)x_perm, nullptr, offset,
+                                         (const uint16_t*)w_gate, (const uint16_t*)w_up,
+                                         (uint16_t*)G, (uint16_t*)U, Ei, di, Fi, Rl, cus, s),
+            "moe_backward/gate_up");
+    else
+        BWD(moe::launch_gate_up_pre_f32((const float*)x_perm, offset, (const float*)w_gate,
+                                        (const float*)w_up, (float*)G, (float*)U, Ei, di, Fi, Rl,
+                                        cus, s), "moe_backward/gate_up");
     // dh_raw = dy W_down^T per kept row with the GeGLU backward in its
     // epilogue (G, U -> dg, du in place, gate h, partial dgate sums), then
     // dgate per row
     BWD(moe::launch_row_gate(offset, tor, row_of, gate, Ei, ki, Rl, rgate, s),
         "moe_backward/row_gate");
-    BWD(moe::launch_bw_nt_geglu(dy_perm, (const uint16_t*)w_down, G, U, gH, rgate, dot, offset,
-                                Ei, Fi, di, Rl, cus, s), "moe_backward/dh_geglu");
+    if (bf)
+        BWD(moe::launch_bw_nt_geglu((const uint16_t*)dy_perm, (const uint16_t*)w_down,
+                                    (uint16_t*)G, (uint16_t*)U, (uint16_t*)gH, rgate, dot, offset,
+                                    Ei, Fi, di, Rl, cus, s), "moe_backward/dh_geglu");
+    else
+        BWD(moe::launch_bw_nt_geglu_f32((const float*)dy_perm, (const float*)w_down, (float*)G,
+                                        (float*)U, (float*)gH, rgate, dot, offset, Ei, Fi, di, Rl,
+                                        cus, s), "moe_backward/dh_geglu");
     BWD(moe::launch_dgate_sum(dot, Fi / 64, offset, Ei, Rl, dgrow, s), "moe_backward/dgate");
     // G, U now hold dg, du
     // dx_perm in parts, one per K slice, each dg W_gate^T + du W_up^T over that
     // slice in one accumulator; summed by launch_dx
     const long long part = Rl * (long long)di;
-    BWD(moe::launch_bw_nt(G, (const uint16_t*)w_gate, U, (const uint16_t*)w_up, dXp, part,
-                          L.dx_parts, offset, Ei, di, Fi, Rl, cus, s), "moe_backward/dx_perm");
-    BWD(moe::launch_bw_tn(x_perm, G, dw_gate, offset, Ei, di, Fi, cus, s), "moe_backward/dw_gate");
-    BWD(moe::launch_bw_tn(x_perm, U, dw_up, offset, Ei, di, Fi, cus, s), "moe_backward/dw_up");
-    BWD(moe::launch_bw_tn(gH, dy_perm, dw_down, offset, Ei, Fi, di, cus, s), "moe_backward/dw_down");
+    if (bf) {
+        BWD(moe::launch_bw_nt((const uint16_t*)G, (const uint16_t*)w_gate, (const uint16_t*)U,
+                              (const uint16_t*)w_up, dXp, part, L.dx_parts, offset, Ei, di, Fi, Rl,
+                              cus, s), "moe_backward/dx_perm");
+        BWD(moe::launch_bw_tn((const uint16_t*)x_perm, (const uint16_t*)G, dw_gate, offset, Ei,
+                              di, Fi, cus, s), "moe_backward/dw_gate");
+        BWD(moe::launch_bw_tn((const uint16_t*)x_perm, (const uint16_t*)U, dw_up, offset, Ei, di,
+                              Fi, cus, s), "moe_backward/dw_up");
+        BWD(moe::launch_bw_tn((const uint16_t*)gH, (const uint16_t*)dy_perm, dw_down, offset, Ei,
+                              Fi, di, cus, s), "moe_backward/dw_down");
+    } else {
+        BWD(moe::launch_bw_nt_f32((const float*)G, (const float*)w_gate, (const float*)U,
+                                  (const float*)w_up, dXp, offset, Ei, di, Fi, Rl, cus, s),
+            "moe_backward/dx_perm");
+        BWD(moe::launch_bw_tn_f32((const float*)x_perm, (const float*)G, dw_gate, offset, Ei, di,
+                                  Fi, cus, s), "moe_backward/dw_gate");
+        BWD(moe::launch_bw_tn_f32((const float*)x_perm, (const float*)U, dw_up, offset, Ei, di,
+                                  Fi, cus, s), "moe_backward/dw_up");
+        BWD(moe::launch_bw_tn_f32((const float*)gH, (const float*)dy_perm, dw_down, offset, Ei,
+                                  Fi, di, cus, s), "moe_backward/dw_down");
+    }
     // router: dlogit, then dx and the router's weight and bias gradients
     BWD(moe::launch_router_bwd(logits, idx, gate, row_of, dgrow, cfg->T, Ei, ki, cfg->temperature,
                                cfg->renormalize, dl, dgate, s), "moe_backward/router");
-    BWD(moe::launch_dx(dl, (const uint16_t*)w_router, dXp, L.dx_parts, part, row_of,
-                       (uint16_t*)dx, cfg->T, di, Ei, ki, s), "moe_backward/dx");
-    BWD(moe::launch_dwr(xb, dl, dw_router, dbias, cfg->T, di, Ei, w + L.dwr, s), "moe_backward/dwr");
+    if (bf)
+        BWD(moe::launch_dx(dl, (const uint16_t*)w_router, dXp, L.dx_parts, part, row_of,
+                           (uint16_t*)dx, cfg->T, di, Ei, ki, s), "moe_backward/dx");
+    else
+        BWD(moe::launch_dx_f32(dl, (const float*)w_router, dXp, row_of, (float*)dx, cfg->T, di,
+                               Ei, ki, s), "moe_backward/dx");
+    BWD(moe::launch_dwr(cfg->dtype, x, dl, dw_router, dbias, cfg->T, di, Ei, w + L.dwr, s),
+        "moe_backward/dwr");
 #undef BWD
     return MOE_OK;
 }

@@ -269,9 +269,13 @@ def test_backward_validation_on_host(L):
         T * k * 4 * 4
     assert n.value >= base + 2 * R * d * 4
     assert n.value < base + 8 * R * d * 4 + (64 << 20)
-    f32 = moe.cconfig(configs.get("tiny"))
-    assert L.moe_backward_workspace_size(ctypes.byref(f32), ctypes.byref(n)) == \
-        moe.MOE_ERR_UNSUPPORTED
+    # fp32 layers too: their rows and pre-activations take 4 bytes per element
+    t32 = configs.get("tiny")
+    f32 = moe.cconfig(t32)
+    n32 = ctypes.c_size_t(0)
+    assert L.moe_backward_workspace_size(ctypes.byref(f32), ctypes.byref(n32)) == 0
+    R32 = moe.max_rows(t32)
+    assert n32.value >= R32 * t32.d_ff * 3 * 4 + 2 * R32 * t32.d * 4 + R32 * t32.d * 4
     assert L.moe_backward_workspace_size(ctypes.byref(c), None) == moe.MOE_ERR_INVALID_ARG
     ok = ctypes.c_void_p(1 << 20)
     odd = ctypes.c_void_p((1 << 20) + 4)
@@ -291,8 +295,6 @@ def test_backward_validation_on_host(L):
     assert b"aligned" in L.moe_last_error()
     assert call(nbytes=n.value - 1) == moe.MOE_ERR_WORKSPACE
     assert call(ws=None) == moe.MOE_ERR_WORKSPACE
-    c32 = moe.cconfig(configs.get("tiny"))
-    assert L.moe_backward(ctypes.byref(c32), *([ok] * 15), big, None) == moe.MOE_ERR_UNSUPPORTED
     bad = moe.cconfig(cfg)
     bad.k = 0
     assert L.moe_backward(ctypes.byref(bad), *([ok] * 15), big, None) == moe.MOE_ERR_INVALID_ARG

@@ -34,6 +34,8 @@ from parity_util import (MaxRel, check_route, dynamic_margin, gpu_inputs, oracle
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+# fp32 layers: every product and intermediate in fp32, the layer's fp32 bar
+TOL_F32 = 1e-5
 GRADS = ("dx", "dw_router", "dbias", "dw_gate", "dw_up", "dw_down", "dgate")
 
 
@@ -90,6 +92,18 @@ CASES = {
                                      drop_policy=1),
 }
 
+F32 = configs.get("tiny")   # fp32, top-1, no capacity limit
+CASES.update({
+    # fp32 layers (plain fp32 FMA products)
+    "f32_tiny": F32,
+    "f32_renorm_drops": F32.scaled(T=300, d=128, E=6, k=2, d_ff=192, temperature=0.7,
+                                   renormalize=True, cap_num=5, cap_den=4),
+    "f32_dyn": F32.scaled(T=400, d=64, E=8, k=4, k_min=2, route_threshold=0.6, d_ff=128,
+                          temperature=0.5, renormalize=True, cap_num=5, cap_den=4),
+    "f32_padded_choice": F32.scaled(T=250, d=64, E=5, k=3, d_ff=64, temperature=0.9,
+                                    cap_num=3, cap_den=4, drop_policy=1, layout=1),
+})
+
 
 def _dyn(cfg):
     return getattr(cfg, "route_threshold", 0.0) > 0
@@ -128,10 +142,11 @@ def test_backward_small(name):
     ob = orc.backward(host["x"], host["w_router"], host["bias"], host["w_gate"], host["w_up"],
                       host["w_down"], dy_h.double().numpy(), logits_in=lg.double().numpy(),
                       **_oracle_kw(cfg))
+    tol = TOL if cfg.dtype == "bf16" else TOL_F32
     for n in GRADS:
         err = rel_err(to_np(g[n]), ob[n])
         say(f"[{name}] {n} err {err:.3g} (max |oracle| {np.abs(ob[n]).max():.3g})")
-        assert err <= TOL, f"{n}: {err}"
+        assert err <= tol, f"{n}: {err}"
     if name == "bw_one_expert":   # p = 1 exactly: no router gradient
         assert (g["dw_router"] == 0).all() and (g["dbias"] == 0).all()
     if name == "bw_all_dropped":
