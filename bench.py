@@ -21,7 +21,11 @@ bf16 GEMM on two expert shapes as a reference) run outside every timed
 region, and the core clock is sampled from sysfs while the headline's
 timed loop runs.  The fp64 oracle is timed on the host's cores on a bounded
 token sample of each layer (`cpu_baseline`), and ranks its own fp64 logits
-to count the tokens whose routing differs from the GPU's fp32 logits.
+to count the tokens whose routing differs from the GPU's fp32 logits.  Each
+layer also times moe_backward (`backward`) and, outside the timed regions, its
+variants (`variants`: the padded-capacity layout and the choice-order drop
+priority where a capacity limit applies, the MLP router at r = 256, m = 1024,
+one PID controller step).
 
 Prints ONE JSON line.
 """
@@ -60,6 +64,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the moe_backward timing (e.g. for counter runs of the forward)")
     ap.add_argument("--no-probes", action="store_true", help="skip the peak probes")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the timing of the layout, drop-priority and router variants")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the headline layer's oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -458,6 +464,51 @@ def measure(cfg, args, headline: bool, clock=None):
         bwd_ms = a.elapsed_time(b) / K
         del out, bw, dy
 
+    # variants of the layer on the same inputs (outside every timed region
+    # above): the padded-capacity layout and the choice-order drop priority
+    # (layers with a capacity limit and a fixed expert count), the MLP router at
+    # the ZAYA1 page's widths (r = 256, m = 1024) on this layer's tokens, and
+    # one step of its PID load-balance controller
+    variants = None
+    if not args.no_variants:
+        variants = {}
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def timed(fn, n=10):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(n):
+                fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / n
+
+        if cfg.cap_den > 0 and cfg.route_threshold == 0:
+            yv = torch.empty_like(y)
+            for key, vcfg in (("padded_layout_ms_per_step", cfg.scaled(layout=1)),
+                              ("choice_order_ms_per_step", cfg.scaled(drop_policy=1))):
+                fv = moe.Forward(vcfg)
+                variants[key] = round(timed(lambda: fv(xs[0], wr, bias, wg, wu, wd, yv)), 4)
+                del fv
+            del yv
+        if cfg.dtype == "bf16":
+            g = torch.Generator(device="cuda").manual_seed(7)
+            rnd = lambda *shape, sc: (torch.randn(*shape, generator=g, device="cuda") * sc).to(
+                torch.bfloat16)
+            r_, m_ = 256, 1024
+            router = dict(w_down=rnd(cfg.d, r_, sc=cfg.d ** -0.5), w1=rnd(r_, m_, sc=r_ ** -0.5),
+                          w2=rnd(m_, m_, sc=m_ ** -0.5), w3=rnd(m_, cfg.E, sc=m_ ** -0.5))
+            prev = rnd(cfg.T, r_, sc=1.0)
+            variants["mlp_router_ms"] = round(
+                timed(lambda: moe.route_mlp(cfg, xs[0], prev, router, 0.5, 1e-6)), 4)
+            del router, prev
+        st_pid = torch.zeros((2, cfg.E), dtype=torch.float64, device="cuda")
+        variants["pid_update_us_per_call"] = round(
+            1e3 * timed(lambda: moe.pid_update(cfg, count, st_pid, 0.2, 0.02, 0.0), n=100), 2)
+        torch.cuda.synchronize()
+
     # algorithmic work of the first batch's routing
     step(xs[0])
     torch.cuda.synchronize()
@@ -511,6 +562,7 @@ def measure(cfg, args, headline: bool, clock=None):
                         "max_deviation": round(float(ls[4]), 4), "cv": round(float(ls[5]), 4),
                         "dropped": int(ls[6]), "empty_experts": int(ls[7])},
         "roofline": roofline(cfg, a, stage_mean["gate_up"], peak, traffic, tkernel),
+        "variants": variants,
         "backward": None if bwd_ms is None else {
             "ms_per_step": round(bwd_ms, 4),
             "tokens_per_s": round(cfg.T / (bwd_ms * 1e-3), 1),
