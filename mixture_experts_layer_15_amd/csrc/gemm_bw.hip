@@ -47,6 +47,14 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
+// x, hidden from the optimizer: lane constants derived from it inside the
+// epilogue are computed there instead of being hoisted out of the tile loop
+// and kept live through the K-loop.
+__device__ __forceinline__ int hidden(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 template <int BM, int BN, int WAVES, int WMW, int NS, int TK>
 struct BwShape {
     static constexpr int THREADS = 64 * WAVES;
@@ -403,19 +411,51 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
                 if (g4 == 0 && r < rows && cols_ok) ops.dot[(row0 + r) * (long long)np + cw / 64] = dot;
             }
         } else {
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const int r = (wm * MI + i) * 16 + c16;
-            if (MODE == 0 ? r >= rows : m0 + r >= M) continue;
-            float* crow = MODE == 0 ? ops.C + part * ops.c_stride + (long long)(row0 + r) * N
-                                    : ops.C + ((long long)e * M + m0 + r) * N;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int col = n0 + (wn * NJ + j) * 16 + g4 * 4;
-                if (col >= N) continue;
-                *(f32x4*)(crow + col) = acc[i][j];
+            // Each 16-row block goes through this wave's 4 KB slice of an idle
+            // stage buffer (the one the last K-step but one used: no wave
+            // reads it any more and no load fills it again in this tile), so
+            // that every store writes whole row pieces, 4 rows x 256 bytes,
+            // instead of the MFMA layout's 16 rows x 64 bytes: per CU, stores
+            // of 128 bytes or more per row move about three times the bytes
+            // per clock.  Chunk c (16 bytes) of row r sits in slot c ^ r.
+            static_assert(NJ == 4, "64 columns (16 chunks of 16 bytes) per wave row");
+            const int fb = (nk + NS - 2) % NS;
+            char* const fa = fb == 0 ? sa0 : fb == 1 ? sa1 : fb == 2 ? sa2 : sa3;
+            char* const fbb = fb == 0 ? sb0 : fb == 1 ? sb1 : fb == 2 ? sb2 : sb3;
+            char* stg;
+            if constexpr (WAVES * 4096 <= S::A_STAGE) {
+                stg = fa + w * 4096;
+            } else {
+                static_assert(WAVES / 2 * 4096 <= S::A_STAGE && WAVES / 2 * 4096 <= S::B_STAGE,
+                              "staging room");
+                stg = w < WAVES / 2 ? fa + w * 4096 : fbb + (w - WAVES / 2) * 4096;
             }
-        }
+            const int colw = n0 + wn * 64;   // the wave's first column
+            const int ln = hidden(lane);
+            const int h16 = ln & 15, hg4 = ln >> 4;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                // lane (g4, c16) holds row c16, columns 16 j + 4 g4 .. + 3: chunk 4 j + g4
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    *(f32x4*)(stg + h16 * 256 + (((j * 4 + hg4) ^ h16) << 4)) = acc[i][j];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int rr = q * 4 + hg4, ch = h16;
+                    const f32x4 v = *(const f32x4*)(stg + rr * 256 + ((ch ^ rr) << 4));
+                    const int r = (wm * MI + i) * 16 + rr;
+                    const int col = colw + ch * 4;
+                    if ((MODE == 0 ? r < rows : m0 + r < M) && col < N) {
+                        float* crow = MODE == 0
+                                          ? ops.C + part * ops.c_stride + (long long)(row0 + r) * N
+                                          : ops.C + ((long long)e * M + m0 + r) * N;
+                        *(f32x4*)(crow + col) = v;
+                    }
+                }
+                // this block's reads are done before the next block's writes
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
         }
         // every wave is done reading this tile's stages before the next tile's
         // loads refill them
