@@ -24,8 +24,9 @@
 // ds_read_b64_tr_b16 on the weight tile kept in its [K][N] layout (each
 // 16-lane group reads a 4 x 16 block; lane n receives column n).
 // Rows past the expert's last row are clamped on load and their MFMAs are
-// skipped per 16-row subtile.  The epilogue stages the tile through LDS and
-// writes whole 16-byte row pieces.
+// skipped per 16-row subtile.  The epilogue stores 8-byte pieces straight
+// from the accumulators, except the 256-row down GEMM's, which goes through
+// LDS and stores whole 128-byte row pieces.
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -394,6 +395,57 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         // token t = tor[r], and y[t] = gate[t] * O[r], with O rounded to bf16
         // first and the product rounded like the combine rounds it, so the
         // result is bit-identical to writing O and combining.
+        // Plain products of 64 columns per wave on 256-row tiles (the
+        // long-sequence down GEMM writing O) go through LDS instead: each
+        // 16-row block into this wave's 2 KB slice of the A stage buffer the
+        // last K-step but one used (idle: nothing reads or fills it again in
+        // this tile), then out in whole 128-byte row pieces, 8 rows per store,
+        // against 16 rows x 8 bytes per store from the MFMA layout, which
+        // moves about a quarter of the bytes per clock per CU (long-sequence
+        // down 5.00 -> 4.80 ms).  Not taken elsewhere: on the 320-row tiles,
+        // where the weights stream, it measured no faster, and for the GeGLU
+        // output (32 columns per wave, staged per row half behind a barrier)
+        // neither.  16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7).
+        if constexpr (!GATEUP && S::BM == 256 && S::OUTW == 64 &&
+                      S::WAVES * 2048 <= S::A_BYTES) {
+            if (Y == nullptr && P == nullptr && bias == nullptr && act == 0 && (N & 7) == 0) {
+                const int fb = (nk + NA - 2) % NA;
+                char* const stg = (fb == 0 ? sa0 : fb == 1 ? sa1 : fb == 2 ? sa2 : sa3) + w * 2048;
+                const int hl16 = opaque(lane);
+                const int h16 = hl16 & 15, hg4 = hl16 >> 4;
+                const int colw = n0 + wn * 64;
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    if (i >= nvm) continue;   // uniform: an empty block of this wave
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        bf16x4 v;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = (__bf16)acc[i][jj][q];
+                        // columns 16 jj + 4 g4 .. + 3: chunk 2 jj + g4 / 2, half g4 & 1
+                        const int slot = (jj * 2 + (hg4 >> 1)) ^ ((h16 >> 1) & 7);
+                        *(u32x2*)(stg + h16 * 128 + slot * 16 + (hg4 & 1) * 8) =
+                            __builtin_bit_cast(u32x2, v);
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int rr = q * 8 + (hl16 >> 3), ch = hl16 & 7;
+                        const u32x4 v =
+                            *(const u32x4*)(stg + rr * 128 + ((ch ^ ((rr >> 1) & 7)) << 4));
+                        const int r = wm * MI * 16 + i * 16 + rr;
+                        if (r < rows && colw + ch * 8 < N)
+                            *(u32x4*)(C + (long long)(row0 + r) * N + colw + ch * 8) = v;
+                    }
+                    // this block's reads are done before the next block's writes
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                continue;
+            }
+        }
         float bv[S::OUTW / 16][4];
 #pragma unroll
         for (int jj = 0; jj < S::OUTW / 16; ++jj)
