@@ -346,12 +346,38 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
         // lane (g4, c16) of block (i, j): row i*16 + c16, columns j*16 + 4 g4 .. + 3
         if constexpr (EPI) {
             // GeGLU backward of this tile's elements; each wave's 64 columns
-            // (N % 64 == 0: all valid or all past N) give one partial of dgate
+            // (N % 64 == 0: all valid or all past N) give one partial of dgate.
+            // g, u come in and dg, du, gate h go out in whole 128-byte row
+            // pieces (8 rows per instruction) through this wave's 6 KB of an
+            // idle stage buffer, switched to and from the MFMA layout there
+            // (16 rows x 8 bytes per instruction straight from the MFMA layout
+            // move about a quarter of the bytes per clock per CU).  Chunk c of
+            // row r of a 16-row block sits in slot c ^ ((r >> 1) & 7).
             static_assert(MODE == 0 && NJ * 16 == 64, "epilogue: NT, 64 columns per wave");
+            static_assert(WAVES / 2 * 6144 <= S::A_STAGE && WAVES / 2 * 6144 <= S::B_STAGE,
+                          "staging room");
             const int cw = n0 + wn * 64;
             const int np = N / 64;
             const bool cols_ok = cw < N;
-            // G, U of row block i + 1 are loaded before row block i is
+            const int fb = (nk + NS - 2) % NS;
+            char* const fa = fb == 0 ? sa0 : fb == 1 ? sa1 : fb == 2 ? sa2 : sa3;
+            char* const fbb = fb == 0 ? sb0 : fb == 1 ? sb1 : fb == 2 ? sb2 : sb3;
+            char* const sG = w < WAVES / 2 ? fa + w * 6144 : fbb + (w - WAVES / 2) * 6144;
+            char* const sU = sG + 2048;
+            char* const sH = sG + 4096;
+            const int ln = hidden(lane);
+            const int h16 = ln & 15, hg4 = ln >> 4, l8 = ln >> 3, c8 = ln & 7;
+            // row-contiguous piece q of a block: row 8 q + l8, chunk c8
+            auto rc = [&](int q) {
+                const int rr = q * 8 + l8;
+                return rr * 128 + ((c8 ^ ((rr >> 1) & 7)) << 4);
+            };
+            // MFMA-layout piece jj: row c16, columns 16 jj + 4 g4 .. + 3
+            auto ml = [&](int jj) {
+                return h16 * 128 + (((jj * 2 + (hg4 >> 1)) ^ ((h16 >> 1) & 7)) << 4) +
+                       (hg4 & 1) * 8;
+            };
+            // g, u of row block i + 1 are loaded before row block i is
             // computed and stored: one load latency per tile, not one per
             // row block (the loads are issued ahead of the stores in program
             // order, which the compiler keeps since the arrays are the same)
@@ -359,18 +385,15 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
             // there each row block loads its own)
             constexpr bool AHEAD = BM != 320;
             constexpr int NSET = AHEAD ? 2 : 1;
-            u32x2 gv[NSET][NJ], uv[NSET][NJ];
-            float gts[NSET];
+            u32x4 gq[NSET][2], uq[NSET][2];
             auto fetch = [&](int i, int b) {
-                const int r = (wm * MI + i) * 16 + c16;
-                if (r < rows && cols_ok) {
-                    const long long rowg = row0 + r;
-                    gts[b] = ops.row_gate[rowg];
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const long long o = rowg * N + cw + j * 16 + g4 * 4;
-                        gv[b][j] = *(const u32x2*)(ops.G + o);
-                        uv[b][j] = *(const u32x2*)(ops.U + o);
+                for (int q = 0; q < 2; ++q) {
+                    const int r = (wm * MI + i) * 16 + q * 8 + l8;
+                    if (r < rows && cols_ok) {
+                        const long long o = (long long)(row0 + r) * N + cw + c8 * 8;
+                        gq[b][q] = *(const u32x4*)(ops.G + o);
+                        uq[b][q] = *(const u32x4*)(ops.U + o);
                     }
                 }
             };
@@ -378,37 +401,55 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const int b = AHEAD ? i & 1 : 0;
+                if constexpr (!AHEAD) fetch(i, 0);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    *(u32x4*)(sG + rc(q)) = gq[b][q];
+                    *(u32x4*)(sU + rc(q)) = uq[b][q];
+                }
                 if constexpr (AHEAD)
                     if (i + 1 < MI) fetch(i + 1, (i + 1) & 1);
-                const int r = (wm * MI + i) * 16 + c16;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                const int r = (wm * MI + i) * 16 + h16;
+                const bool row_ok = r < rows && cols_ok;
+                const float gt = row_ok ? ops.row_gate[row0 + r] : 0.f;
                 float dot = 0.f;
-                if (r < rows && cols_ok) {
-                    const long long rowg = row0 + r;
-                    const float gt = AHEAD ? gts[b] : ops.row_gate[rowg];
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const long long o = rowg * N + cw + j * 16 + g4 * 4;
-                        const u32x2 gq = AHEAD ? gv[b][j] : *(const u32x2*)(ops.G + o);
-                        const u32x2 uq = AHEAD ? uv[b][j] : *(const u32x2*)(ops.U + o);
-                        float dg[4], du[4], gh[4];
+                for (int j = 0; j < NJ; ++j) {
+                    const u32x2 gw = *(const u32x2*)(sG + ml(j));
+                    const u32x2 uw = *(const u32x2*)(sU + ml(j));
+                    float dg[4], du[4], gh[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const uint32_t gw = gq[q >> 1], uw = uq[q >> 1];
-                            const float g = bf16_bits_to_f32((q & 1) ? gw >> 16 : gw & 0xffffu);
-                            const float u = bf16_bits_to_f32((q & 1) ? uw >> 16 : uw & 0xffffu);
-                            float term;
-                            geglu_bwd_elem(g, u, acc[i][j][q], gt, dg[q], du[q], gh[q], term);
-                            dot += term;
-                        }
-                        *(u32x2*)(ops.G + o) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-                        *(u32x2*)(ops.U + o) = u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-                        *(u32x2*)(ops.gH + o) = u32x2{pack_bf16x2(gh[0], gh[1]), pack_bf16x2(gh[2], gh[3])};
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t g2 = gw[q >> 1], u2 = uw[q >> 1];
+                        const float g = bf16_bits_to_f32((q & 1) ? g2 >> 16 : g2 & 0xffffu);
+                        const float u = bf16_bits_to_f32((q & 1) ? u2 >> 16 : u2 & 0xffffu);
+                        float term;
+                        geglu_bwd_elem(g, u, acc[i][j][q], gt, dg[q], du[q], gh[q], term);
+                        dot += term;
+                    }
+                    *(u32x2*)(sG + ml(j)) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+                    *(u32x2*)(sU + ml(j)) = u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+                    *(u32x2*)(sH + ml(j)) = u32x2{pack_bf16x2(gh[0], gh[1]), pack_bf16x2(gh[2], gh[3])};
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int rq = (wm * MI + i) * 16 + q * 8 + l8;
+                    if (rq < rows && cols_ok) {
+                        const long long o = (long long)(row0 + rq) * N + cw + c8 * 8;
+                        *(u32x4*)(ops.G + o) = *(const u32x4*)(sG + rc(q));
+                        *(u32x4*)(ops.U + o) = *(const u32x4*)(sU + rc(q));
+                        *(u32x4*)(ops.gH + o) = *(const u32x4*)(sH + rc(q));
                     }
                 }
                 // the four lanes of a row (g4 = 0..3), then lane g4 = 0 writes
+                if (!row_ok) dot = 0.f;
                 dot += __shfl_xor(dot, 16);
                 dot += __shfl_xor(dot, 32);
-                if (g4 == 0 && r < rows && cols_ok) ops.dot[(row0 + r) * (long long)np + cw / 64] = dot;
+                if (hg4 == 0 && row_ok) ops.dot[(row0 + r) * (long long)np + cw / 64] = dot;
+                // this block's LDS reads are done before the next block's writes
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
         } else {
             // Each 16-row block goes through this wave's 4 KB slice of an idle
