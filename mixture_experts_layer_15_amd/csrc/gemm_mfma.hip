@@ -227,7 +227,19 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w / S::WN, wn = w % S::WN;
-    const bool a_loader = w < 4;            // waves 0-3 fill A stages, 4-7 fill B stages
+    // Who loads what.  On 256-row tiles (the long-sequence layer) every wave
+    // loads an eighth of each stage of both operands, its weight pieces
+    // first (BAL): the weight slices miss in L2 more often than the
+    // activation rows, and with waves 4-7 loading all of them the activation
+    // loaders waited at each stage's barrier for a quarter of their time
+    // (balanced: gate/up 9.61-9.69 -> 9.33-9.34 ms, down 4.81-4.85 -> 4.67-4.70
+    // ms, alternated on one GPU, bit-identical).  Otherwise waves 0-3 fill
+    // the A stages and 4-7 the B stages (the 320-row stages do not split
+    // into eighths of whole 1 KB wave-loads).
+    constexpr bool BAL = NA == NB && S::BM == 256 && S::A_BYTES % 8192 == 0 &&
+                         S::B_BYTES % 8192 == 0;
+    constexpr int AL = S::A_BYTES / 8192, BL = S::B_BYTES / 8192;   // wave-loads per wave (BAL)
+    const bool a_loader = w < 4;
     const int lw = w & 3;                   // index among the loaders of its operand
     const int c16 = lane & 15, g4 = lane >> 4;
     const int G = gridDim.x;
@@ -279,23 +291,29 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         const i32x4 rs_a = buffer_rsrc(a_rows ? A : A + (long long)row0 * K);
         const i32x4 rs_b0 = buffer_rsrc(B0 + wofs);
         const i32x4 rs_b1 = buffer_rsrc((GATEUP ? B1 : B0) + wofs);
-        constexpr int NL = S::A_LOADS > S::B_LOADS ? S::A_LOADS : S::B_LOADS;
+        // this lane's offsets: (BAL) l_off[0 .. AL) for its A wave-loads and
+        // l_off[AL .. AL + BL) for its B wave-loads, else those of its operand
+        constexpr int NL = BAL ? AL + BL
+                               : (S::A_LOADS > S::B_LOADS ? S::A_LOADS : S::B_LOADS);
         uint32_t l_off[NL];
         const int ln = opaque(lane);
 #pragma unroll
         for (int q = 0; q < NL; ++q) {
-            if (a_loader) {
-                const int r = (lw * S::A_LOADS + q) * S::A_RPK + ln / S::ACH;
+            const bool is_a = BAL ? q < AL : a_loader;
+            if (is_a) {
+                const int wl = BAL ? w * AL + q : lw * S::A_LOADS + q;   // wave-load in the stage
+                const int r = wl * S::A_RPK + ln / S::ACH;
                 const int c = (ln % S::ACH) ^ fa<BKT>(r);
                 const int rr = min(r, rows - 1);
                 const int src = a_rows ? a_rows[row0 + rr] : rr;
-                l_off[q] = (q < S::A_LOADS) ? ((uint32_t)src * (uint32_t)K + c * 8) * 2u : 0u;
+                l_off[q] = (BAL || q < S::A_LOADS) ? ((uint32_t)src * (uint32_t)K + c * 8) * 2u
+                                                   : 0u;
             } else {
-                const int gl = lw * S::B_LOADS + q;                 // wave-load index in the stage
+                const int gl = BAL ? w * BL + (q - AL) : lw * S::B_LOADS + q;
                 const int r = (gl % S::SUB_LOADS) * S::RPK + ln / S::CPR;
                 const int c = (ln % S::CPR) ^ (hb<S::CPR>(r) << 1);
                 const int col = min(n0 + c * 8, N - 8) - n0;
-                l_off[q] = (q < S::B_LOADS) ? (r * N + col) * 2 : 0;
+                l_off[q] = (BAL || q < S::B_LOADS) ? (r * N + col) * 2 : 0;
             }
         }
 
@@ -303,11 +321,11 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         // address lb
         auto load_a = [&](int kt, uint32_t lb, int q) {
             load_to_lds(rs_a, l_off[q], (uint32_t)((kb + kt) * BKT * 2),
-                        lb + (lw * S::A_LOADS + q) * 1024);
+                        lb + ((BAL ? w * AL : lw * S::A_LOADS) + q) * 1024);
         };
         auto load_b = [&](int kt, uint32_t lb, int q) {
-            const int gl = lw * S::B_LOADS + q;
-            load_to_lds((GATEUP && gl >= S::SUB_LOADS) ? rs_b1 : rs_b0, l_off[q],
+            const int gl = BAL ? w * BL + q : lw * S::B_LOADS + q;
+            load_to_lds((GATEUP && gl >= S::SUB_LOADS) ? rs_b1 : rs_b0, l_off[BAL ? AL + q : q],
                         (uint32_t)(kb + kt) * (uint32_t)(BKT * 2) * (uint32_t)N,
                         lb + gl * 1024);
         };
@@ -322,7 +340,18 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
         char* abuf[4] = {sa0, sa1, sa2, sa3};
         char* bbuf[8] = {sb0, sb1, sb2, sb3, sb4, sb5, sb6, sb7};
         // prologue: A stages 0 .. NA-2, B stages 0 .. NB-2
-        if (a_loader) {
+        if constexpr (BAL) {
+#pragma unroll
+            for (int kt = 0; kt + 1 < NA; ++kt)
+                if (kt < nk) {
+                    const uint32_t lbb = lds_base(bbuf[kt]);
+#pragma unroll
+                    for (int q = 0; q < BL; ++q) load_b(kt, lbb, q);
+                    const uint32_t lba = lds_base(abuf[kt]);
+#pragma unroll
+                    for (int q = 0; q < AL; ++q) load_a(kt, lba, q);
+                }
+        } else if (a_loader) {
 #pragma unroll
             for (int kt = 0; kt + 1 < NA; ++kt)
                 if (kt < nk) {
@@ -342,11 +371,11 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
 
         // step k: wait for A and B stage k, run the MFMAs on stage k and,
         // spread among them, refill the buffers read at step k-1 with A stage
-        // k+NA-1 (A loaders) or B stage k+NB-1 (B loaders)
+        // k+NA-1 (A loaders) or B stage k+NB-1 (B loaders), or both (BAL)
         auto k_loop = [&](auto full_tag, auto role_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
             constexpr bool ROLE_A = decltype(role_tag)::value;
-            constexpr int LOADS = ROLE_A ? S::A_LOADS : S::B_LOADS;
+            constexpr int LOADS = BAL ? AL + BL : ROLE_A ? S::A_LOADS : S::B_LOADS;
             constexpr int NS = ROLE_A ? NA : NB;
             // slots per wave-load: spread over the whole stage with three or
             // more stages (two still in flight behind it), over its first
@@ -366,9 +395,15 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
                     const bool refill = k + NS - 1 < nk;
                     const uint32_t lb = lds_base(ROLE_A ? abuf[(s + NA - 1) % NA]
                                                         : bbuf[(s + NB - 1) % NB]);
+                    const uint32_t lb2 = BAL ? lds_base(abuf[(s + NA - 1) % NA]) : 0u;
+                    const uint32_t lb3 = BAL ? lds_base(bbuf[(s + NB - 1) % NB]) : 0u;
                     auto iss = [&](int slot) {
                         if (slot % STRIDE == 0 && slot / STRIDE < LOADS && refill) {
-                            if constexpr (ROLE_A) load_a(k + NA - 1, lb, slot / STRIDE);
+                            if constexpr (BAL) {
+                                const int q = slot / STRIDE;   // B (weights) first
+                                if (q < BL) load_b(k + NB - 1, lb3, q);
+                                else load_a(k + NA - 1, lb2, q - BL);
+                            } else if constexpr (ROLE_A) load_a(k + NA - 1, lb, slot / STRIDE);
                             else load_b(k + NB - 1, lb, slot / STRIDE);
                         }
                     };
@@ -377,7 +412,10 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
                 }
             }
         };
-        if (a_loader) {
+        if (BAL) {
+            if (nvm == MI) k_loop(std::true_type{}, std::true_type{});
+            else k_loop(std::false_type{}, std::true_type{});
+        } else if (a_loader) {
             if (nvm == MI) k_loop(std::true_type{}, std::true_type{});
             else k_loop(std::false_type{}, std::true_type{});
         } else {
