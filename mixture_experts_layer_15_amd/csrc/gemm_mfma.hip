@@ -233,9 +233,12 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(
     // activation rows, and with waves 4-7 loading all of them the activation
     // loaders waited at each stage's barrier for a quarter of their time
     // (balanced: gate/up 9.61-9.69 -> 9.33-9.34 ms, down 4.81-4.85 -> 4.67-4.70
-    // ms, alternated on one GPU, bit-identical).  Otherwise waves 0-3 fill
-    // the A stages and 4-7 the B stages (the 320-row stages do not split
-    // into eighths of whole 1 KB wave-loads).
+    // ms, alternated on one GPU, bit-identical; activation pieces first
+    // 9.41 against 9.13 ms, loads spread over the whole stage 10.5 ms).
+    // Otherwise waves 0-3 fill the A stages and 4-7 the B stages: on the
+    // 640-row tiles, where the weights stream from HBM, the balanced loads
+    // measured 8-10% slower, and the 320-row stages do not split into
+    // eighths of whole 1 KB wave-loads.
     constexpr bool BAL = NA == NB && S::BM == 256 && S::A_BYTES % 8192 == 0 &&
                          S::B_BYTES % 8192 == 0;
     constexpr int AL = S::A_BYTES / 8192, BL = S::B_BYTES / 8192;   // wave-loads per wave (BAL)
