@@ -255,14 +255,29 @@ __global__ __launch_bounds__(64 * WAVES, 2) void gemm_bw_kernel(
                                  left * (uint32_t)N * 2u - (uint32_t)n0 * 2u);
                 so = 0u;
             }
+            // NT on 256-row tiles (long-sequence layer): the weight pieces
+            // first, as they miss in L2 more often than the activation rows
+            // (alone on one GPU: dh_raw-shaped product 5.22-5.27 -> 5.02-5.03
+            // ms, dx_perm-shaped 9.48-9.51 -> 9.35-9.40 ms; on the wide
+            // layer's 320-row tiles -1.6% and +1%, so there A first)
+            constexpr bool WFIRST = MODE == 0 && BM == 256;
+            constexpr int FIRST = WFIRST ? S::B_WL : S::A_WL;
 #pragma unroll
-            for (int q = 0; q < S::A_WL; ++q)
-                if (only_q < 0 || only_q == q)
-                    load_to_lds(ra, l_off[q], so, la + (w * S::A_WL + q) * 1024);
+            for (int q = 0; q < FIRST; ++q)
+                if (only_q < 0 || only_q == q) {
+                    if constexpr (WFIRST)
+                        load_to_lds(rb, l_off[S::A_WL + q], so, lb + (w * S::B_WL + q) * 1024);
+                    else
+                        load_to_lds(ra, l_off[q], so, la + (w * S::A_WL + q) * 1024);
+                }
 #pragma unroll
-            for (int q = 0; q < S::B_WL; ++q)
-                if (only_q < 0 || only_q == S::A_WL + q)
-                    load_to_lds(rb, l_off[S::A_WL + q], so, lb + (w * S::B_WL + q) * 1024);
+            for (int q = 0; q < (WFIRST ? S::A_WL : S::B_WL); ++q)
+                if (only_q < 0 || only_q == FIRST + q) {
+                    if constexpr (WFIRST)
+                        load_to_lds(ra, l_off[q], so, la + (w * S::A_WL + q) * 1024);
+                    else
+                        load_to_lds(rb, l_off[S::A_WL + q], so, lb + (w * S::B_WL + q) * 1024);
+                }
         };
 
         // per-lane fragment read offsets (lane constants)
