@@ -582,13 +582,16 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
 }  // namespace
 
 // Tile shape policy.  Rows per expert are only known on the device; the host
-// knows their mean (max_rows / E, exact when nothing is dropped).  Up to 2048
+// knows their mean (max_rows / E, exact when nothing is dropped).  Up to 512
 // rows per expert on average the GEMMs take 320-row tiles: one M-tile covers a
 // ZAYA1-like or wide-layer expert (about 256 rows: weight-streaming bound, so
-// each weight tile is streamed once), and the skewed layer's capacity-bound
-// experts of 1280 rows take four instead of five 256-row tiles (1.21 -> 1.17
-// ms per step).  Above that, 256 x 256 tiles (long-sequence layer, about 16k
-// rows per expert: 16.5 against 17.4 ms per step on 320-row tiles).
+// each weight tile is streamed once).  Above that, 256 x 256 tiles, whose
+// waves load both operands (long-sequence layer, about 16k rows per expert:
+// 16.5 against 17.4 ms per step on 320-row tiles before that; the skewed
+// layer, 631 rows on average with its capacity-bound experts at 1280: 2.103
+// -> 2.033 ms per step against 320-row tiles, which it took while the 256-row
+// waves still split the operands; 1024 uniform rows: gate/up 2.41 -> 2.09 ms,
+// down 1.15 -> 0.91 ms; 631 uniform rows: equal).
 //   gate/up: 320 x 256, 32-deep K-steps in rings of four stages per operand
 //     (three in flight while one is multiplied): 321 against 334 us with
 //     64-deep steps in two stages on the ZAYA1-like layer, the same on the
@@ -601,7 +604,7 @@ hipError_t launch_shape(const uint16_t* A, const uint16_t* B0, const uint16_t* B
 //     stages measured 2% slower on this tile).  Its waves are arranged 4 (M) x 2 (N): 80 x 64 per wave
 //     instead of 160 x 32 reads 27% fewer fragment bytes from LDS per stage
 //     (measured 4% faster).
-static bool tiles320(long long max_rows, int E) { return max_rows <= 2048LL * E; }
+static bool tiles320(long long max_rows, int E) { return max_rows <= 512LL * E; }
 
 // Between 320 and 640 rows per expert on average (the wide layer with 2-4
 // experts per token: about 350 rows, up to 512 by its mean bound), 320-row
