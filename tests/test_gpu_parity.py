@@ -146,12 +146,16 @@ SMALL = [
     # k = E: every expert chosen, renormalised gates = the softmax over all experts
     ("k_eq_E", configs.get("tiny").scaled(T=500, d=128, E=4, k=4, d_ff=128, temperature=0.5,
                                           renormalize=True, dtype="bf16")),
-    # 320-row tiles over experts of very different sizes: 15 to 4054 rows
-    # (top-2), 1 to 1868 rows (top-1)
-    ("skew_320", configs.get("tiny").scaled(T=4096, d=128, E=6, k=2, d_ff=192, temperature=0.5,
+    # experts of very different sizes: 15 to 4054 rows on 256-row tiles (top-2,
+    # 1365 rows per expert on average), 1 to 1868 rows on 640-row tiles (top-1,
+    # 410 on average), and on 320-row tiles (top-1, 256 on average) with the
+    # hot experts over several M-tiles
+    ("skew_256", configs.get("tiny").scaled(T=4096, d=128, E=6, k=2, d_ff=192, temperature=0.5,
                                             renormalize=True, dtype="bf16", zipf_bias=2.5)),
-    ("skew_320_top1", configs.get("tiny").scaled(T=2048, d=128, E=5, k=1, d_ff=192,
+    ("skew_640_top1", configs.get("tiny").scaled(T=2048, d=128, E=5, k=1, d_ff=192,
                                                  temperature=0.5, dtype="bf16", zipf_bias=3.0)),
+    ("skew_320", configs.get("tiny").scaled(T=1536, d=128, E=6, k=1, d_ff=192, temperature=0.5,
+                                            dtype="bf16", zipf_bias=2.5)),
     # 320-640 rows per expert on average: 640-row tiles, with skew so that the
     # hot experts take two or more of them and the cold ones a few rows
     ("skew_640", configs.get("tiny").scaled(T=2000, d=192, E=8, k=2, d_ff=320, temperature=0.5,
@@ -170,7 +174,7 @@ SMALL = [
     # K slices (d = 320: a ragged second N-tile)
     ("split_down", configs.get("tiny").scaled(T=3000, d=320, E=6, k=1, d_ff=384,
                                               temperature=0.7, dtype="bf16")),
-    # more than 2048 rows per expert on average: 256-row tiles, and the experts
+    # more than 512 rows per expert on average: 256-row tiles, and the experts
     # under 64 rows in their own launch of 128-row tiles (7 and 2 rows here)
     ("few_rows_split", configs.get("tiny").scaled(T=12288, d=128, E=5, k=1, d_ff=192,
                                                   temperature=0.5, dtype="bf16", zipf_bias=3.0)),
